@@ -1,0 +1,43 @@
+"""Brute-force decode attention in 50-digit decimal arithmetic.
+
+TEST INFRASTRUCTURE ONLY. A second implementation of the definition (page
+"MoA-Structured Decode Attention", §2: Step I scores s = scale * (K q),
+Step II softmax with the max subtracted, Step III out = a V; §6: query head h
+reads KV head h // (h_q // h_kv)), written independently of ``oracle.c`` in
+pure-Python loops over ``decimal.Decimal``. It is meant for tiny inputs only
+(a few rows, a few dimensions) and pins the fp64 oracle there: with 50
+significant digits its own rounding is far below fp64's.
+"""
+from __future__ import annotations
+
+from decimal import Decimal, localcontext
+
+
+def attend_one(q, K, V, scale) -> list[Decimal]:
+    """One head: q length d_k, K n x d_k, V n x d_v (nested lists of numbers)."""
+    with localcontext() as ctx:
+        ctx.prec = 50
+        sc = Decimal(float(scale))
+        qd = [Decimal(float(x)) for x in q]
+        s = [sc * sum(qd[j] * Decimal(float(row[j])) for j in range(len(qd))) for row in K]
+        m = max(s)
+        e = [(x - m).exp() for x in s]
+        Z = sum(e)
+        a = [x / Z for x in e]
+        d_v = len(V[0])
+        return [sum(a[l] * Decimal(float(V[l][d])) for l in range(len(V))) for d in range(d_v)]
+
+
+def decode(q, k_cache, v_cache, lens, scale):
+    """Batched GQA decode: q [B][h_q][d_k], caches [B][h_kv][cap][d], lens [B]."""
+    out = []
+    for b in range(len(q)):
+        h_q, h_kv = len(q[b]), len(k_cache[b])
+        g = h_q // h_kv
+        n = int(lens[b])
+        rows = []
+        for h in range(h_q):
+            kvh = h // g
+            rows.append(attend_one(q[b][h], k_cache[b][kvh][:n], v_cache[b][kvh][:n], scale))
+        out.append(rows)
+    return out

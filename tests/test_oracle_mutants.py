@@ -1,0 +1,81 @@
+"""The oracle's pins are strong enough to catch plausible mistakes.
+
+Each case plants one mistake in a private copy of ``oracle/oracle.c`` (a
+dropped term, a wrong sign, index or group map, a transposed operand, a
+doubled scale, a wrong dequantisation scale, a decoder off by one, a missing
+length update), builds it with gcc in a temporary directory, routes the
+oracle wrapper to it and runs the pin tests of ``test_oracle.py``. At least
+one pin must fail for every mutant; the unmutated copy must pass them all.
+Everything runs on the CPU.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "group_map_modulo": ("const int kvh = h / g;", "const int kvh = h % h_kv;"),
+    "transposed_K": ("acc += q[j] * K[(size_t)l * d_k + j];", "acc += q[j] * K[(size_t)j * n + l];"),
+    "scale_twice": ("s[l] = scale * acc;", "s[l] = scale * scale * acc;"),
+    "exp_sign": ("e[l] = exp(s[l] - m);\n        Z +=", "e[l] = exp(m - s[l]);\n        Z +="),
+    "dropped_first_row_in_step3": ("for (int l = 0; l < n; ++l) acc += a[l] * V",
+                                   "for (int l = 1; l < n; ++l) acc += a[l] * V"),
+    "v_uses_k_scale": ("load_elem(v_cache, kv_dtype, idx) * vs;", "load_elem(v_cache, kv_dtype, idx) * ks;"),
+    "fp8_bias_8": ("v = ldexp(1.0 + mant / 8.0, expo - 7);", "v = ldexp(1.0 + mant / 8.0, expo - 8);"),
+    "append_no_len_update": ("lens[b] += 1;", "lens[b] += 0;"),
+    "append_wrong_row": ("(slot * cap + (size_t)lens[b]) * d_k * eb", "(slot * cap + (size_t)lens[b] / 2) * d_k * eb"),
+    # a rewrite that changes nothing: the control that must pass every pin
+    "control_noop": ("(slot * cap + (size_t)lens[b]) * d_k * eb", "(slot * cap + (size_t)lens[b] + 0) * d_k * eb"),
+}
+CONTROL = "control_noop"
+
+PINS = [
+    ("worked_example", lambda gd: pins.test_worked_example_printed_values(gd)),
+    ("closed_form", lambda gd: pins.test_worked_example_closed_form(gd)),
+    ("brute_f32", lambda gd: [pins.test_oracle_vs_decimal_brute_force(s, "f32") for s in range(6)]),
+    ("brute_fp8", lambda gd: [pins.test_oracle_vs_decimal_brute_force(s, "fp8") for s in range(3)]),
+    ("sdpa_gqa", lambda gd: pins.test_oracle_vs_torch_sdpa_fp64("gqa4", 8, 2, 128, "bf16")),
+    ("special_cases", lambda gd: pins.test_special_cases_reduce_to_rows_or_mean()),
+    ("fp8_codes", lambda gd: pins.test_fp8_e4m3fn_decoder_all_codes()),
+    ("append_layout", lambda gd: pins.test_append_layout_gamma_offsets(gd)),
+    ("append_bits", lambda gd: pins.test_append_is_bit_exact_and_touches_only_its_rows()),
+]
+
+
+def _build(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / f"lib{name}.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", str(path), "-o", str(so), "-lm"])
+    return str(so)
+
+
+def _failing_pins(so, golden_dir):
+    failed = []
+    with oracle.using_library(so):
+        for pname, fn in PINS:
+            try:
+                fn(golden_dir)
+            except (AssertionError, ValueError):
+                failed.append(pname)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(k for k in MUTANTS if k != CONTROL))
+def test_planted_mistake_is_caught(name, tmp_path, golden_dir):
+    old, new = MUTANTS[name]
+    so = _build(tmp_path, name, old, new)
+    assert _failing_pins(so, golden_dir), f"mutant {name} passed every pin"
+
+
+def test_unmutated_copy_passes_all_pins(tmp_path, golden_dir):
+    old, new = MUTANTS[CONTROL]
+    so = _build(tmp_path, CONTROL, old, new)
+    assert _failing_pins(so, golden_dir) == []
