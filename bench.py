@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X: µs per decode step and achieved HBM GB/s.
+
+A step is one pass of the whole hot path over the workload's batch: for a workload
+that appends (the grouped-query one does), the lengths are reset to their pre-append
+values and one K/V row per (sequence, KV head) is appended; then the split-KV
+attention kernel and the log-sum-exp combine run. Inputs are seeded synthetic
+tensors (workloads.py) already resident in HBM when timing starts; R rotating
+copies of the cache (R * cache bytes >= 2 GiB) keep the 256 MB Infinity Cache from
+serving one step's reads out of the previous step's.
+
+Prints ONE JSON line:
+  value       = KV-cache bytes per step / wall-clock time per step   (GB/s, 1e9 B/s)
+  ms_per_step = wall-clock per step over the timed region, bracketed by synchronisation
+  roofline    = the split-KV attention kernel, timed with HIP events on the stream it
+                runs on: algorithmic bytes per launch (the KV rows of every sequence plus
+                q) / mean launch duration, against the 8 TB/s HBM3E peak; `traffic` is
+                the HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, read
+                from the profiles/ summary when it was taken on the current kernel source
+  cpu_baseline= the fp64 CPU oracle on the same inputs, full step, host cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "achieved HBM GB/s (KV bytes/step ÷ time, % of peak) + µs/decode step"
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_kv_split_amd", "csrc", "decode_attn.hip")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="gqa8_bf16",
+                   help="single_head_f32 | mha_bf16 | gqa8_bf16 | mqa_bf16 | gqa8_fp8")
+    p.add_argument("--const-len", type=int, default=0,
+                   help="override: every sequence this long (the 8K/16K/32K sweep)")
+    p.add_argument("--chunk-rows", type=int, default=0, help="rows per split (0 = library choice)")
+    p.add_argument("--rotations", type=int, default=0, help="cache copies to rotate (0 = auto)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle timing budget")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 1 GiB device copy (FETCH_SIZE / WRITE_SIZE scale factor)")
+    return p.parse_args()
+
+
+def source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per split-kernel launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"split_kv_attn__{workload}__pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        m = re.match(r"^\s*([a-z_0-9]+)\s*:\s*(\S+)\s*$", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("source_sha256") != source_sha() or "hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is a design note, not built", file=sys.stderr)
+        return 2
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    import decode_attention_kv_split_amd as da
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    if args.const_len:
+        w = w.resized(lens=("const", args.const_len), cap=max(w.cap, args.const_len))
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    c = workloads.generate(w, poison=False)
+    t_gen = time.perf_counter() - t_gen
+    lens_final = c["lens_final"]
+    max_len = int(lens_final.max())
+    esz = workloads.ELEM_BYTES[w.kv_dtype]
+    kv_bytes = int(lens_final.to(torch.int64).sum()) * w.h_kv * 2 * w.d * esz
+    q_bytes = w.B * w.h_q * w.d * workloads.ELEM_BYTES[w.q_dtype]
+    cache_bytes = 2 * c["k_cache"].numel() * esz
+    R = args.rotations or max(2, min(8, math.ceil((2 << 30) / max(kv_bytes, 1))))
+
+    desc = da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, workloads.TORCH_DTYPE[w.q_dtype],
+                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, args.chunk_rows)
+    plan = da.da_plan(desc, max_len)
+    q = c["q"].to(dev)
+    scales = c["kv_scales"].to(dev) if c["kv_scales"] is not None else None
+    lens_init = c["lens_init"].to(dev)
+    k_new = c["k_new"][0].contiguous().to(dev) if w.steps else None
+    v_new = c["v_new"][0].contiguous().to(dev) if w.steps else None
+    slots = []
+    k0, v0 = c["k_cache"].to(dev), c["v_cache"].to(dev)
+    del c
+    for r in range(R):
+        kc = k0 if r == 0 else k0.clone()
+        vc = v0 if r == 0 else v0.clone()
+        slots.append((kc, vc, (lens_init if not w.steps else lens_init.clone())))
+    if w.steps == 0:
+        slots = [(kc, vc, lens_init) for kc, vc, _ in slots]
+    ws = da.Workspace(desc, max_len, device=dev)
+    out = torch.empty(w.B, w.h_q, w.d, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        kc, vc, lens = slots[i % R]
+        if w.steps:
+            lens.copy_(lens_init)
+            da.kv_append(desc, kc, vc, lens, k_new, v_new, ws)
+        if ev is not None:
+            ev[0].record(stream)
+        da.decode_attn_partial(desc, q, kc, vc, lens, max_len, scales, ws)
+        if ev is not None:
+            ev[1].record(stream)
+        da.decode_attn_combine(desc, lens, max_len, out, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    assert da.da_read_device_error(ws) == 0, "device error flagged during warm-up"
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    gpu_ms = start.elapsed_time(end) / args.steps
+    split_ms = [a.elapsed_time(b) for a, b in evs]
+    split_ms_mean = sum(split_ms) / len(split_ms)
+    split_sorted = sorted(split_ms)
+    algo_bytes = kv_bytes + q_bytes
+    achieved = algo_bytes / (split_ms_mean * 1e-3) / 1e9
+    value = kv_bytes / (wall_ms * 1e-3) / 1e9
+    traffic = profiled_traffic(args.workload) if not args.const_len and not args.chunk_rows else None
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "us_per_step": round(wall_ms * 1e3, 2),
+        "gpu_event_us_per_step": round(gpu_ms * 1e3, 2),
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.B, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
+            "cap": w.cap, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype,
+            "lens": (f"const {max_len}" if w.lens[0] == "const"
+                     else f"uniform[{w.lens[1]},{w.lens[2]}] seed {w.seed}"),
+            "sum_lens": int(lens_final.sum()), "max_len": max_len,
+            "appends_per_step": int(w.steps > 0), "kv_bytes_per_step": kv_bytes,
+            "rotations": R, "cache_bytes_per_copy": cache_bytes, **plan,
+        },
+        "roofline": {
+            "kernel": "split_kv_attn_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": algo_bytes,
+            "launch_us_mean": round(split_ms_mean * 1e3, 2),
+            "launch_us_p10": round(split_sorted[len(split_sorted) // 10] * 1e3, 2),
+            "launch_us_p90": round(split_sorted[(9 * len(split_sorted)) // 10] * 1e3, 2),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, kv_bytes)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(w, budget_s: float, kv_bytes_full: int) -> dict:
+    """The fp64 oracle, unchanged, on the host cores: whole sequences of the same workload
+    (the first k sequences, k chosen to fit the time budget), caches after the append."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    nthreads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    c = workloads.generate(w, poison=False)
+    kc = oracle._np(c["k_cache"]).copy() if w.steps else oracle._np(c["k_cache"])
+    vc = oracle._np(c["v_cache"]).copy() if w.steps else oracle._np(c["v_cache"])
+    lens = c["lens_init"].numpy().copy()
+    for t in range(w.steps):
+        oracle.kv_append(kc, vc, lens, oracle._np(c["k_new"][t]).copy(), oracle._np(c["v_new"][t]).copy())
+    esz = workloads.ELEM_BYTES[w.kv_dtype]
+    # time one sequence first, then grow the sample to about the budget
+    order = list(range(w.B))
+    per_seq = []
+
+    def run(bs):
+        sl = slice(bs[0], bs[-1] + 1)
+        sc = None if c["kv_scales"] is None else c["kv_scales"][sl].contiguous()
+        t = time.perf_counter()
+        oracle.decode_f64(c["q"][sl].contiguous(), np.ascontiguousarray(kc[sl]),
+                          np.ascontiguousarray(vc[sl]), lens[sl], w.scale, kv_scales=sc,
+                          nthreads=nthreads)
+        return time.perf_counter() - t
+
+    t_one = run([0])
+    est_per_row = t_one / max(int(lens[0]), 1)
+    k = 1
+    while k < w.B and est_per_row * float(lens[:k + 1].sum()) <= budget_s:
+        k += 1
+    elapsed = run(order[:k])
+    rows = int(lens[:k].sum())
+    sample_bytes = rows * w.h_kv * 2 * w.d * esz
+    gbs = sample_bytes / elapsed / 1e9
+    full_step_s = elapsed * (kv_bytes_full / sample_bytes)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"first {k} of {w.B} sequences ({rows} rows x {w.h_kv} KV heads, all "
+                      f"{w.h_q} query heads), fp64, {elapsed:.2f} s",
+            "us_per_full_step_est": round(full_step_s * 1e6, 1),
+            "cpu": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    sys.exit(main())

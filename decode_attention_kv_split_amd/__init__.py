@@ -1,0 +1,212 @@
+"""Split-KV decode attention for MI355X (gfx950): thin Python binding.
+
+Every function here has the name of the C entry point it wraps (declared in
+``include/decode_attn.h``) and does argument marshalling only: it checks the
+torch tensors' dtypes, shapes, devices and contiguity, passes their device
+pointers and torch's current HIP stream to ``libdecode_attn.so`` through
+ctypes, and raises ``DecodeAttnError`` on a non-zero status. All arithmetic
+runs in the library's HIP kernels; torch only provides device memory and the
+stream. There is no fallback: if the library is not built, importing the
+binding's functions fails.
+
+Layouts (the same as the C ABI):
+  q [B, h_q, d] ; k_cache, v_cache [B, h_kv, cap, d] ; lens [B] int32 ;
+  k_new, v_new [B, h_kv, d] ; kv_scales [B, h_kv, 2] fp32 (fp8 only) ;
+  out [B, h_q, d] fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+from ._lib import DA_BF16, DA_F32, DA_FP8_E4M3FN, lib, library_path  # noqa: F401
+
+__all__ = [
+    "Desc", "DecodeAttnError", "Workspace", "da_workspace_size", "da_plan", "da_workspace_init",
+    "kv_append", "decode_attn_run", "decode_attn_partial", "decode_attn_combine",
+    "da_read_device_error", "da_status_string", "da_last_error", "library_path",
+    "DA_F32", "DA_BF16", "DA_FP8_E4M3FN", "DEV_ERR_APPEND_FULL", "DEV_ERR_LEN_RANGE",
+]
+
+DEV_ERR_APPEND_FULL = 1
+DEV_ERR_LEN_RANGE = 2
+
+_TORCH_CODE = {torch.float32: DA_F32, torch.bfloat16: DA_BF16, torch.float8_e4m3fn: DA_FP8_E4M3FN}
+
+
+class DecodeAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {da_status_string(status)} ({status}): {da_last_error()}")
+
+
+class _CDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("cap", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("chunk_rows", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Desc:
+    """Problem descriptor (mirrors ``da_desc``). dtypes are torch dtypes."""
+    batch: int
+    h_q: int
+    h_kv: int
+    d: int
+    cap: int
+    q_dtype: torch.dtype
+    kv_dtype: torch.dtype
+    scale: float | None = None  # default 1/sqrt(d)
+    chunk_rows: int = 0         # 0: the library's choice
+
+    def c(self) -> _CDesc:
+        scale = 1.0 / math.sqrt(self.d) if self.scale is None else self.scale
+        return _CDesc(self.batch, self.h_q, self.h_kv, self.d, self.d, self.cap,
+                      _TORCH_CODE.get(self.q_dtype, -1), _TORCH_CODE.get(self.kv_dtype, -1),
+                      float(scale), self.chunk_rows)
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise DecodeAttnError(status, where)
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, shape, dtype, device=None) -> ctypes.c_void_p:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def da_status_string(status: int) -> str:
+    return lib().da_status_string(int(status)).decode()
+
+
+def da_last_error() -> str:
+    return lib().da_last_error().decode()
+
+
+def da_workspace_size(desc: Desc, max_len: int) -> int:
+    n = ctypes.c_size_t()
+    cd = desc.c()
+    _check(lib().da_workspace_size(ctypes.byref(cd), int(max_len), ctypes.byref(n)), "da_workspace_size")
+    return n.value
+
+
+def da_plan(desc: Desc, max_len: int) -> dict:
+    c, s, g = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    cd = desc.c()
+    _check(lib().da_plan(ctypes.byref(cd), int(max_len), ctypes.byref(c), ctypes.byref(s), ctypes.byref(g)),
+           "da_plan")
+    return {"chunk_rows": c.value, "n_splits": s.value, "heads_per_block": g.value}
+
+
+def da_workspace_init(ws: torch.Tensor) -> None:
+    if ws.device.type != "cuda" or ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    _check(lib().da_workspace_init(ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(ws)),
+           "da_workspace_init")
+
+
+class Workspace:
+    """A device workspace sized for (desc, max_len), with its error word cleared."""
+
+    def __init__(self, desc: Desc, max_len: int, device="cuda"):
+        self.nbytes = da_workspace_size(desc, max_len)
+        self.tensor = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        da_workspace_init(self.tensor)
+
+    def ptr(self) -> ctypes.c_void_p:
+        return ctypes.c_void_p(self.tensor.data_ptr())
+
+
+def _ws(ws) -> tuple[ctypes.c_void_p, int, torch.Tensor]:
+    t = ws.tensor if isinstance(ws, Workspace) else ws
+    if t.device.type != "cuda" or t.dtype != torch.uint8 or not t.is_contiguous():
+        raise ValueError("workspace must be a Workspace or a contiguous uint8 GPU tensor")
+    return ctypes.c_void_p(t.data_ptr()), t.numel(), t
+
+
+def _cache_shapes(desc: Desc):
+    return (desc.batch, desc.h_kv, desc.cap, desc.d)
+
+
+def kv_append(desc: Desc, k_cache, v_cache, lens, k_new, v_new, workspace=None) -> None:
+    """Append one K row and one V row per (sequence, KV head) at row lens[b]; lens += 1."""
+    dev = k_cache.device
+    kc = _dev(k_cache, "k_cache", _cache_shapes(desc), desc.kv_dtype, dev)
+    vc = _dev(v_cache, "v_cache", _cache_shapes(desc), desc.kv_dtype, dev)
+    ln = _dev(lens, "lens", (desc.batch,), torch.int32, dev)
+    kn = _dev(k_new, "k_new", (desc.batch, desc.h_kv, desc.d), desc.kv_dtype, dev)
+    vn = _dev(v_new, "v_new", (desc.batch, desc.h_kv, desc.d), desc.kv_dtype, dev)
+    wp = _ws(workspace)[0] if workspace is not None else ctypes.c_void_p(None)
+    cd = desc.c()
+    _check(lib().kv_append(ctypes.byref(cd), kc, vc, ln, kn, vn, wp, _stream(k_cache)), "kv_append")
+
+
+def _attn_args(desc: Desc, q, k_cache, v_cache, lens, kv_scales):
+    dev = q.device
+    qp = _dev(q, "q", (desc.batch, desc.h_q, desc.d), desc.q_dtype, dev)
+    kc = _dev(k_cache, "k_cache", _cache_shapes(desc), desc.kv_dtype, dev)
+    vc = _dev(v_cache, "v_cache", _cache_shapes(desc), desc.kv_dtype, dev)
+    ln = _dev(lens, "lens", (desc.batch,), torch.int32, dev)
+    if desc.kv_dtype == torch.float8_e4m3fn:
+        sc = _dev(kv_scales, "kv_scales", (desc.batch, desc.h_kv, 2), torch.float32, dev)
+    else:
+        sc = ctypes.c_void_p(None)
+    return qp, kc, vc, ln, sc
+
+
+def decode_attn_run(desc: Desc, q, k_cache, v_cache, lens, max_len: int, kv_scales, out, workspace) -> None:
+    """out[b, h] = softmax(scale * K[b, h/g, :lens[b]] q[b, h]) V[b, h/g, :lens[b]]."""
+    qp, kc, vc, ln, sc = _attn_args(desc, q, k_cache, v_cache, lens, kv_scales)
+    op = _dev(out, "out", (desc.batch, desc.h_q, desc.d), torch.float32, q.device)
+    wp, wn, _ = _ws(workspace)
+    cd = desc.c()
+    _check(lib().decode_attn_run(ctypes.byref(cd), qp, kc, vc, ln, int(max_len), sc, op, wp, wn, _stream(q)),
+           "decode_attn_run")
+
+
+def decode_attn_partial(desc: Desc, q, k_cache, v_cache, lens, max_len: int, kv_scales, workspace) -> None:
+    """First stage: per-split (max, sum, unnormalised output) into the workspace."""
+    qp, kc, vc, ln, sc = _attn_args(desc, q, k_cache, v_cache, lens, kv_scales)
+    wp, wn, _ = _ws(workspace)
+    cd = desc.c()
+    _check(lib().decode_attn_partial(ctypes.byref(cd), qp, kc, vc, ln, int(max_len), sc, wp, wn, _stream(q)),
+           "decode_attn_partial")
+
+
+def decode_attn_combine(desc: Desc, lens, max_len: int, out, workspace) -> None:
+    """Second stage: merge the splits by log-sum-exp weights into out."""
+    ln = _dev(lens, "lens", (desc.batch,), torch.int32)
+    op = _dev(out, "out", (desc.batch, desc.h_q, desc.d), torch.float32, lens.device)
+    wp, wn, _ = _ws(workspace)
+    cd = desc.c()
+    _check(lib().decode_attn_combine(ctypes.byref(cd), ln, int(max_len), op, wp, wn, _stream(out)),
+           "decode_attn_combine")
+
+
+def da_read_device_error(workspace) -> int:
+    """Synchronises the current stream and returns the workspace's sticky error bits."""
+    wp, _, t = _ws(workspace)
+    code = ctypes.c_int32()
+    _check(lib().da_read_device_error(wp, _stream(t), ctypes.byref(code)), "da_read_device_error")
+    return code.value

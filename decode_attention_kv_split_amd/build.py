@@ -1,0 +1,45 @@
+"""Build the gfx950 HIP library in-tree: libdecode_attn.so next to this file.
+
+One translation unit (csrc/decode_attn.hip) holds the kernels and the C ABI
+declared in include/decode_attn.h. Flags:
+  --offload-arch=gfx950                 MI355X (CDNA4) only
+  -fno-gpu-flush-denormals-to-zero      fp32 subnormals kept (the fp8 decoder relies on them)
+  -target-feature -packed-fp32-ops      no packed fp32 VALU instructions are generated
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "decode_attn.hip")
+HEADER = os.path.join(ROOT, "include", "decode_attn.h")
+LIB = os.path.join(PKG, "libdecode_attn.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
+         "-fno-gpu-flush-denormals-to-zero",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include")]
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile the HIP library (always recompiles) and return its path."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass warns that it does not know the packed-fp32 feature: harmless
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{msg}")
+    if verbose and msg.strip():
+        print(msg, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True))

@@ -1,0 +1,153 @@
+/*
+ * decode_attn.h -- C ABI of the MI355X (gfx950) split-KV decode-attention library.
+ *
+ * The operation (page "MoA-Structured Decode Attention", §2 Decode DNF, eqs. (1)-(3)):
+ * for every sequence b and query head h, with n = lens[b] cached rows,
+ *     s[l]   = scale * sum_j q[b,h,j] * K[b,kvh,l,j]            (Step I, K read row by row)
+ *     a      = softmax(s)  (max subtracted, exponentials normalised)   (Step II)
+ *     out[d] = sum_l a[l] * V[b,kvh,l,d]                          (Step III)
+ * where kvh = h / (h_q / h_kv) selects the query head's KV group (same page, §6 GQA/MQA:
+ * the group is selected, never broadcast-copied), and one row per step is appended to the
+ * cache at its row-major offset (same page, §5 KV-cache accumulation).
+ *
+ * Layouts (all row-major, contiguous; the same page's §4 gamma offsets lifted to rank 4):
+ *   q        [batch, h_q, d_k]          element type desc->q_dtype
+ *   k_cache  [batch, h_kv, cap, d_k]    element type desc->kv_dtype;
+ *                                       element (b,kvh,l,j) at ((b*h_kv+kvh)*cap+l)*d_k+j
+ *   v_cache  [batch, h_kv, cap, d_v]    element type desc->kv_dtype
+ *   lens     [batch] int32              rows currently in each sequence (device memory)
+ *   kv_scales[batch, h_kv, 2] fp32      (K scale, V scale) per slot; fp8 caches only
+ *   out      [batch, h_q, d_v] fp32
+ * For an fp8 cache the value of an element is decode_e4m3fn(code) * its slot's scale.
+ *
+ * Memory and threads: the caller owns every buffer (all pointers are device pointers unless
+ * stated otherwise). The library never allocates or frees device memory and keeps no
+ * pointers between calls. Every launch is asynchronous on the caller's stream (a
+ * hipStream_t passed as void*; NULL means the default stream); nothing on the run path
+ * synchronises the host. Calls are thread-safe.
+ *
+ * Errors: every function returns DA_OK (0) or a negative DA_ERR_* code, checked on the host
+ * before anything is launched; on failure nothing is launched. da_last_error() gives a
+ * per-thread message for the latest failure. Conditions only the device can see (a lens
+ * value out of range) cannot be returned without a synchronisation: the kernel then skips
+ * the affected work, writes zeros where it would have written results, and ORs a
+ * DA_DEV_ERR_* bit into the workspace's sticky error word, which da_read_device_error reads.
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Host-side status codes. */
+#define DA_OK 0
+#define DA_ERR_INVALID_ARG (-1) /* null or misaligned pointer, bad shape, h_q % h_kv != 0,
+                                   max_len outside [1, cap], non-finite scale */
+#define DA_ERR_UNSUPPORTED (-2) /* head size or dtype combination not built */
+#define DA_ERR_WORKSPACE (-3)   /* workspace smaller than da_workspace_size() */
+#define DA_ERR_LAUNCH (-4)      /* the HIP runtime refused a launch (see da_last_error) */
+
+/* Device-side error bits, ORed into the workspace's error word. */
+#define DA_DEV_ERR_APPEND_FULL 1 /* kv_append: lens[b] outside [0, cap); row b not written,
+                                    lens[b] unchanged */
+#define DA_DEV_ERR_LEN_RANGE 2   /* decode: lens[b] outside [1, max_len]; out[b] zeroed */
+
+typedef enum { DA_F32 = 0, DA_BF16 = 1, DA_FP8_E4M3FN = 2 } da_dtype;
+
+/*
+ * Problem descriptor. Supported: d_k == d_v in {64, 128}; (q_dtype, kv_dtype) in
+ * {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN)}; any h_q that is a multiple of h_kv.
+ * scale is the factor of Step I (1/sqrt(d_k) in the page's setting), applied once.
+ * chunk_rows is the number of cache rows each split covers (a multiple of 256), or 0 to
+ * let the library choose from the shape and max_len.
+ */
+typedef struct {
+    int32_t batch;
+    int32_t h_q;
+    int32_t h_kv;
+    int32_t d_k;
+    int32_t d_v;
+    int32_t cap;
+    int32_t q_dtype;  /* da_dtype */
+    int32_t kv_dtype; /* da_dtype */
+    float scale;
+    int32_t chunk_rows;
+} da_desc;
+
+/*
+ * Bytes of device workspace decode_attn_run / kv_append need for this descriptor when no
+ * sequence is longer than max_len (1 <= max_len <= cap). The workspace holds the sticky
+ * error word and the per-split partial results (running max, sum of exponentials and
+ * unnormalised output of each split; see decode_attn_partial). *bytes is written on the host.
+ */
+int da_workspace_size(const da_desc *desc, int32_t max_len, size_t *bytes);
+
+/*
+ * Chosen work partition for (desc, max_len), all outputs host int32 (any may be NULL):
+ * rows per split, splits per sequence at max_len, query heads each workgroup serves.
+ */
+int da_plan(const da_desc *desc, int32_t max_len, int32_t *chunk_rows, int32_t *n_splits,
+            int32_t *heads_per_block);
+
+/* Clears the workspace's error word (a kernel, not a memset). Call once after allocating. */
+int da_workspace_init(void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * KV-cache accumulation (page "MoA-Structured Decode Attention", §5): for every sequence b
+ * and KV head kvh, copies row k_new[b,kvh,:] (shape [batch, h_kv, d_k], kv_dtype) into row
+ * lens[b] of k_cache and v_new[b,kvh,:] into row lens[b] of v_cache, then sets
+ * lens[b] += 1. Bit copies: every other byte of the caches is unchanged. fp8 rows must
+ * already be quantised with their slot's scale. A sequence with lens[b] outside [0, cap) is
+ * skipped and raises DA_DEV_ERR_APPEND_FULL in the workspace (which may be NULL when the
+ * caller does not want the error word; the row is still skipped).
+ */
+int kv_append(const da_desc *desc, void *k_cache, void *v_cache, int32_t *lens,
+              const void *k_new, const void *v_new, void *workspace, void *stream);
+
+/*
+ * Decode attention for every (b, h) over rows [0, lens[b]) (page "MoA-Structured Decode
+ * Attention", §2 Steps I-III, §6 group selection). max_len is a host-side upper bound on
+ * every lens[b] (1 <= max_len <= cap) that sizes the work partition. kv_scales is required
+ * for an fp8 cache and ignored otherwise. out is fp32 [batch, h_q, d_v]. Equivalent to
+ * decode_attn_partial followed by decode_attn_combine.
+ */
+int decode_attn_run(const da_desc *desc, const void *q, const void *k_cache,
+                    const void *v_cache, const int32_t *lens, int32_t max_len,
+                    const float *kv_scales, float *out, void *workspace, size_t ws_bytes,
+                    void *stream);
+
+/*
+ * First stage of decode_attn_run: each (sequence, KV head, split of chunk_rows rows) reads
+ * its K and V rows once for all query heads of the group and writes, per query head, the
+ * split's running max (base-2 exponent domain), its sum of exponentials and its
+ * unnormalised output row to the workspace.
+ */
+int decode_attn_partial(const da_desc *desc, const void *q, const void *k_cache,
+                        const void *v_cache, const int32_t *lens, int32_t max_len,
+                        const float *kv_scales, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Second stage: merges the splits of every (b, h) by their log-sum-exp weights into out
+ * (an exact rewriting of Step II's normalisation over the whole row range).
+ */
+int decode_attn_combine(const da_desc *desc, const int32_t *lens, int32_t max_len, float *out,
+                        void *workspace, size_t ws_bytes, void *stream);
+
+/* Waits for the stream, then copies the error word into *code (host). For tests and tools. */
+int da_read_device_error(const void *workspace, void *stream, int32_t *code);
+
+/* Static text for a DA_* status code. */
+const char *da_status_string(int status);
+
+/* Message of the latest failure on the calling thread ("" if none). */
+const char *da_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H */

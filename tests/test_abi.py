@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point the
+header declares, and rejects invalid arguments on the host before launching anything.
+
+Every call here fails validation (or only does host arithmetic), so no kernel is
+launched and no device is touched; fake device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import decode_attention_kv_split_amd as da
+from decode_attention_kv_split_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "decode_attn.h")
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced on the host
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.library_path()):
+        from decode_attention_kv_split_amd import build
+        build.build_library()
+    return _lib.load()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} is declared in the header but not exported"
+
+
+def _desc(**kw):
+    base = dict(batch=2, h_q=8, h_kv=2, d_k=128, d_v=128, cap=1024, q_dtype=1, kv_dtype=1,
+                scale=0.088, chunk_rows=0)
+    base.update(kw)
+    return da._CDesc(**base)
+
+
+def _ws_size(lib, desc, max_len):
+    n = ctypes.c_size_t(0)
+    rc = lib.da_workspace_size(ctypes.byref(desc), max_len, ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw,max_len,code", [
+    (dict(h_q=6, h_kv=4), 100, -1),           # h_q not a multiple of h_kv
+    (dict(batch=0), 100, -1),
+    (dict(), 0, -1),                           # max_len < 1
+    (dict(), 2000, -1),                        # max_len > cap
+    (dict(d_k=96, d_v=96), 100, -2),           # head size not built
+    (dict(d_k=128, d_v=64), 100, -2),          # d_k != d_v
+    (dict(q_dtype=0, kv_dtype=1), 100, -2),    # dtype pair not built
+    (dict(kv_dtype=7), 100, -1),               # unknown dtype code
+    (dict(chunk_rows=100), 100, -1),           # chunk not a multiple of 256
+    (dict(scale=float("nan")), 100, -1),
+])
+def test_invalid_descriptors_are_rejected(lib, kw, max_len, code):
+    rc, _ = _ws_size(lib, _desc(**kw), max_len)
+    assert rc == code
+    assert lib.da_last_error()  # a message was recorded
+
+
+def test_workspace_size_and_plan(lib):
+    d = _desc(batch=16, h_q=32, h_kv=8, cap=32768)
+    rc, n = _ws_size(lib, d, 32768)
+    assert rc == 0
+    c, s, g = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    assert lib.da_plan(ctypes.byref(d), 32768, ctypes.byref(c), ctypes.byref(s), ctypes.byref(g)) == 0
+    assert c.value % 256 == 0 and s.value == -(-32768 // c.value) and g.value == 4
+    rows = 16 * 32 * s.value
+    assert n >= 256 + rows * 2 * 4 + rows * 128 * 4
+    d2 = _desc(batch=16, h_q=32, h_kv=8, cap=32768, chunk_rows=512)
+    assert lib.da_plan(ctypes.byref(d2), 1000, ctypes.byref(c), ctypes.byref(s), None) == 0
+    assert (c.value, s.value) == (512, 2)
+
+
+def test_null_and_misaligned_pointers_fail_before_launch(lib):
+    d = _desc()
+    assert lib.kv_append(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert lib.kv_append(ctypes.byref(d), ctypes.c_void_p(0x10002), FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert lib.decode_attn_run(ctypes.byref(d), None, FAKE, FAKE, FAKE, 100, None, FAKE, FAKE, 1 << 30, None) == -1
+    assert lib.decode_attn_run(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 100, None, None, FAKE, 1 << 30, None) == -1
+    fp8 = _desc(kv_dtype=2)
+    assert lib.decode_attn_partial(ctypes.byref(fp8), FAKE, FAKE, FAKE, FAKE, 100, None, FAKE, 1 << 30, None) == -1
+    assert lib.da_read_device_error(None, None, None) == -1
+    assert lib.da_workspace_init(None, 1024, None) == -1
+    assert lib.da_workspace_init(FAKE, 16, None) == -3
+
+
+def test_small_workspace_is_rejected(lib):
+    d = _desc()
+    rc, n = _ws_size(lib, d, 1000)
+    assert rc == 0
+    assert lib.decode_attn_run(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1000, None, FAKE, FAKE, n - 1, None) == -3
+    assert lib.decode_attn_combine(ctypes.byref(d), FAKE, 1000, FAKE, FAKE, n - 1, None) == -3
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.da_status_string(code)
+    assert lib.da_status_string(0) == b"ok"
+    assert lib.da_status_string(-3) == b"workspace too small"
+
+
+def test_python_binding_marshalling_errors():
+    """The binding refuses CPU tensors and wrong shapes before calling the library."""
+    desc = da.Desc(1, 4, 2, 64, 128, torch.bfloat16, torch.bfloat16)
+    q = torch.zeros(1, 4, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        da.decode_attn_run(desc, q, kc, kc, torch.ones(1, dtype=torch.int32), 1, None,
+                           torch.zeros(1, 4, 64), torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(da.DecodeAttnError):
+        da.da_workspace_size(da.Desc(1, 3, 2, 64, 128, torch.bfloat16, torch.bfloat16), 10)

@@ -1,0 +1,222 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the GPU.
+
+Small cases span several row tiles, several splits and ragged tails; the
+full-size workloads run in the launch configuration the benchmark times and
+are compared on sampled sequences. Caches are NaN-poisoned past each
+sequence's length, so a read out of range shows up as a non-finite output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_kv_split_amd as da
+import oracle
+import workloads
+from tests.gpu_case import check_close, desc_of, log, oracle_out, run_gpu, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def W(**kw):
+    base = dict(name="case", B=3, h_q=8, h_kv=2, d=128, cap=1500, q_dtype="bf16", kv_dtype="bf16",
+                lens=("uniform", 1, 1500), steps=0, seed=11, scale=workloads._inv_sqrt(128))
+    base.update(kw)
+    if base["kv_dtype"] == "f32":
+        base["q_dtype"] = "f32"
+    base["scale"] = workloads._inv_sqrt(base["d"])
+    return workloads.Workload(**base)
+
+
+# ------------------------------------------------------------------ the single-head workload
+def test_single_head_f32_sixteen_append_then_attend_steps():
+    """n 1008 -> 1024, fp32, 1e-5 relative per step; cache bit-exact afterwards (I4, I5)."""
+    w = workloads.WORKLOADS["single_head_f32"]
+    c = workloads.generate(w)
+    log(f"case single_head_f32 B={w.B} d={w.d}")
+    desc = desc_of(w)
+    g = to_gpu(c)
+    lens = g["lens_init"].clone()
+    ws = da.Workspace(desc, w.cap)
+    kc = oracle._np(c["k_cache"]).copy()
+    vc = oracle._np(c["v_cache"]).copy()
+    ln = c["lens_init"].numpy().copy()
+    out = torch.empty(1, 1, w.d, device="cuda")
+    for t in range(w.steps):
+        da.kv_append(desc, g["k_cache"], g["v_cache"], lens, g["k_new"][t].contiguous(),
+                     g["v_new"][t].contiguous(), ws)
+        oracle.kv_append(kc, vc, ln, c["k_new"][t].numpy().copy(), c["v_new"][t].numpy().copy())
+        da.decode_attn_run(desc, g["q"], g["k_cache"], g["v_cache"], lens, w.cap, None, out, ws)
+        ref = oracle.decode_f64(c["q"], kc, vc, ln, w.scale)
+        check_close(out, ref, "f32", f"step {t}")
+    assert int(lens.item()) == 1024 and da.da_read_device_error(ws) == 0
+    assert np.array_equal(g["k_cache"].cpu().numpy().view(np.uint32), kc.view(np.uint32))
+    assert np.array_equal(g["v_cache"].cpu().numpy().view(np.uint32), vc.view(np.uint32))
+
+
+# ------------------------------------------------------------------ small parity grid
+CASES = [
+    # kv, d, h_q, h_kv, lens, chunk
+    ("f32", 64, 1, 1, ("uniform", 1, 1500), 256),
+    ("f32", 128, 4, 2, ("uniform", 1, 1500), 0),
+    ("f32", 64, 6, 3, ("uniform", 200, 1500), 512),
+    ("bf16", 128, 8, 8, ("uniform", 1, 1500), 256),
+    ("bf16", 128, 8, 2, ("uniform", 1, 1500), 0),
+    ("bf16", 128, 32, 8, ("uniform", 1, 1500), 512),
+    ("bf16", 64, 16, 2, ("uniform", 1, 1500), 256),
+    ("bf16", 128, 32, 1, ("uniform", 700, 1500), 256),
+    ("bf16", 128, 6, 2, ("uniform", 1, 1500), 256),
+    ("bf16", 128, 5, 5, ("uniform", 1, 1500), 0),
+    ("fp8", 128, 16, 2, ("uniform", 1, 1500), 256),
+    ("fp8", 128, 8, 8, ("uniform", 1, 1500), 0),
+    ("fp8", 64, 8, 1, ("uniform", 1, 1500), 512),
+]
+
+
+@pytest.mark.parametrize("kv,d,h_q,h_kv,lens,chunk", CASES)
+def test_parity_small(kv, d, h_q, h_kv, lens, chunk):
+    w = W(kv_dtype=kv, d=d, h_q=h_q, h_kv=h_kv, lens=lens, seed=100 + CASES.index((kv, d, h_q, h_kv, lens, chunk)))
+    c = workloads.generate(w)
+    log(f"case {kv} d={d} h_q={h_q} h_kv={h_kv} chunk={chunk} lens={c['lens_final'].tolist()}")
+    out, _, _, err = run_gpu(w, c, chunk_rows=chunk)
+    assert err == 0
+    check_close(out, oracle_out(w, c), kv)
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+def test_parity_tile_and_split_boundaries(kv):
+    """Lengths at 1, tile edges and split edges (+-1); f32/bf16 append their last row first."""
+    edges = [1, 2, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1023]
+    steps = 0 if kv == "fp8" else 1
+    w = W(kv_dtype=kv, B=len(edges), h_q=4, h_kv=2, d=128, cap=1024, steps=steps,
+          lens=("const", 1024), seed=5)
+    c = workloads.generate(w)
+    # cut sequence b to length L: drawn row L-1 becomes the appended row, rows >= L-steps poisoned
+    for b, L in enumerate(edges):
+        n0 = L - steps
+        if steps:
+            c["k_new"][0, b] = c["k_cache"][b, :, L - 1]
+            c["v_new"][0, b] = c["v_cache"][b, :, L - 1]
+        c["k_cache"][b, :, n0:] = workloads._poisoned(c["k_cache"][b, :, n0:].shape, kv)
+        c["v_cache"][b, :, n0:] = workloads._poisoned(c["v_cache"][b, :, n0:].shape, kv)
+    c["lens_final"] = torch.tensor(edges, dtype=torch.int32)
+    c["lens_init"] = c["lens_final"] - steps
+    log(f"case boundaries {kv} lens={edges}")
+    out, _, _, err = run_gpu(w, c, chunk_rows=256, max_len=1024)
+    assert err == 0
+    check_close(out, oracle_out(w, c), kv)
+
+
+def test_single_row_returns_that_value_row_exactly():
+    """I1: with one row the softmax weight is 1 and out equals the V row (bf16 widened)."""
+    w = W(B=4, h_q=8, h_kv=2, cap=300, lens=("const", 1))
+    c = workloads.generate(w)
+    out, _, _, err = run_gpu(w, c, max_len=1)
+    assert err == 0
+    expect = c["v_cache"][:, :, 0].float().repeat_interleave(w.g, dim=1)
+    assert torch.equal(out.cpu(), expect)
+
+
+def test_fp8_decoding_of_every_finite_code():
+    """The in-register e4m3fn decode: with one row per sequence out = decode(code) * v_scale,
+    checked for all 254 finite codes against the oracle's decoder (v_scale = 1, exact)."""
+    codes = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    codes += [0] * (256 - len(codes))
+    w = W(B=2, h_q=1, h_kv=1, d=128, cap=64, kv_dtype="fp8", lens=("const", 1))
+    c = workloads.generate(w)
+    v = torch.tensor(codes, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).reshape(2, 128)
+    c["v_cache"][:, 0, 0] = v
+    c["kv_scales"][:] = 1.0
+    out, _, _, err = run_gpu(w, c, max_len=1)
+    assert err == 0
+    expect = np.array([oracle.e4m3fn_to_f64(x) for x in codes]).reshape(2, 1, 128)
+    assert np.array_equal(out.cpu().double().numpy(), expect)
+
+
+def test_gqa_equals_mha_on_broadcast_cache():
+    """I3 on the GPU: the grouped kernel equals the one-head-per-group kernel on a
+    repeat_interleave'd cache, within the bf16 tolerance."""
+    w = W(B=3, h_q=16, h_kv=4, cap=1200, lens=("uniform", 1, 1200), seed=31)
+    c = workloads.generate(w)
+    out_gqa, _, _, _ = run_gpu(w, c)
+    wm = W(B=3, h_q=16, h_kv=16, cap=1200, lens=("uniform", 1, 1200), seed=31)
+    cm = dict(c)
+    cm["k_cache"] = c["k_cache"].repeat_interleave(w.g, dim=1).contiguous()
+    cm["v_cache"] = c["v_cache"].repeat_interleave(w.g, dim=1).contiguous()
+    out_mha, _, _, _ = run_gpu(wm, cm)
+    assert (out_gqa - out_mha).abs().max().item() <= 2e-3
+    check_close(out_gqa, oracle_out(w, c), "bf16")
+
+
+def test_runs_are_bitwise_deterministic():
+    w = W(B=4, h_q=32, h_kv=8, cap=3000, lens=("uniform", 1, 3000), seed=41)
+    c = workloads.generate(w)
+    a, _, _, _ = run_gpu(w, c, chunk_rows=256)
+    b, _, _, _ = run_gpu(w, c, chunk_rows=256)
+    assert torch.equal(a, b)
+
+
+def test_append_is_bit_exact_over_the_whole_buffer():
+    w = W(B=5, h_q=8, h_kv=4, d=128, cap=40, lens=("uniform", 3, 40), steps=3, seed=9)
+    c = workloads.generate(w)
+    desc = desc_of(w)
+    g = to_gpu(c)
+    lens = g["lens_init"].clone()
+    ws = da.Workspace(desc, w.cap)
+    kc = oracle._np(c["k_cache"]).copy()
+    vc = oracle._np(c["v_cache"]).copy()
+    ln = c["lens_init"].numpy().copy()
+    for t in range(w.steps):
+        da.kv_append(desc, g["k_cache"], g["v_cache"], lens, g["k_new"][t].contiguous(),
+                     g["v_new"][t].contiguous(), ws)
+        oracle.kv_append(kc, vc, ln, oracle._np(c["k_new"][t]).copy(), oracle._np(c["v_new"][t]).copy())
+    assert np.array_equal(oracle._np(g["k_cache"].cpu()), kc)
+    assert np.array_equal(oracle._np(g["v_cache"].cpu()), vc)
+    assert np.array_equal(lens.cpu().numpy(), ln) and da.da_read_device_error(ws) == 0
+
+
+def test_device_errors_are_flagged_and_work_skipped():
+    """A full sequence is not appended to; an out-of-range length gives zeros; both set bits."""
+    w = W(B=2, h_q=4, h_kv=2, d=128, cap=16, lens=("const", 16), steps=0, seed=2)
+    c = workloads.generate(w)
+    desc = desc_of(w)
+    g = to_gpu(c)
+    ws = da.Workspace(desc, 16)
+    lens = torch.tensor([16, 5], dtype=torch.int32, device="cuda")
+    before = g["k_cache"].clone()
+    row = torch.zeros(2, 2, 128, dtype=torch.bfloat16, device="cuda")
+    da.kv_append(desc, g["k_cache"], g["v_cache"], lens, row, row, ws)
+    assert da.da_read_device_error(ws) == da.DEV_ERR_APPEND_FULL
+    assert lens.tolist() == [16, 6]
+    assert torch.equal(g["k_cache"][0], before[0])
+    ws2 = da.Workspace(desc, 8)
+    out = torch.full((2, 4, 128), 7.0, device="cuda")
+    da.decode_attn_run(desc, g["q"], g["k_cache"], g["v_cache"], lens, 8, None, out, ws2)
+    assert da.da_read_device_error(ws2) == da.DEV_ERR_LEN_RANGE
+    assert torch.equal(out[0].cpu(), torch.zeros(4, 128))   # lens 16 > max_len 8
+    # expected cache built on the CPU: sequence 1 received the zero row at row 5
+    c["k_cache"][1, :, 5] = 0
+    c["v_cache"][1, :, 5] = 0
+    ref = oracle_out(w, c, lens=torch.tensor([16, 6], dtype=torch.int32))
+    check_close(out[1:], ref[1:], "bf16")
+
+
+# ------------------------------------------------------------------ full-size workloads
+FULL = ["mha_bf16", "gqa8_bf16", "mqa_bf16", "gqa8_fp8"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload_sampled(name):
+    """The workloads at their real sizes in the default launch plan; the oracle checks
+    every head of three sampled sequences (first, last and the longest)."""
+    w = workloads.WORKLOADS[name]
+    log(f"case full {name}: generating")
+    c = workloads.generate(w)
+    log(f"case full {name}: running GPU, plan {da.da_plan(desc_of(w), int(c['lens_final'].max()))}")
+    out, _, _, err = run_gpu(w, c)
+    assert err == 0
+    out = out.cpu()
+    assert torch.isfinite(out).all()
+    samples = sorted({0, w.B - 1, int(c["lens_final"].argmax())})
+    for b in samples:
+        log(f"case full {name}: oracle b={b} L={int(c['lens_final'][b])}")
+        check_close(out[b:b + 1], oracle_out(w, c, batch_index=b), w.kv_dtype, f"{name} b={b}")
