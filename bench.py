@@ -3,8 +3,8 @@
 
 A step is one pass of the whole hot path over the workload's batch: for a workload
 that appends (the grouped-query one does), the lengths are reset to their pre-append
-values and one K/V row per (sequence, KV head) is appended; then the split-KV
-attention kernel and the log-sum-exp combine run. Inputs are seeded synthetic
+values and one K/V row per (sequence, KV head) is appended; then decode_attn_run runs
+the split-KV attention kernel and the log-sum-exp combine. Inputs are seeded synthetic
 tensors (workloads.py) already resident in HBM when timing starts; R rotating
 copies of the cache (R * cache bytes >= 2 GiB) keep the 256 MB Infinity Cache from
 serving one step's reads out of the previous step's.
@@ -12,9 +12,12 @@ serving one step's reads out of the previous step's.
 Prints ONE JSON line:
   value       = KV-cache bytes per step / wall-clock time per step   (GB/s, 1e9 B/s)
   ms_per_step = wall-clock per step over the timed region, bracketed by synchronisation
-  roofline    = the split-KV attention kernel, timed with HIP events on the stream it
-                runs on: algorithmic bytes per launch (the KV rows of every sequence plus
-                q) / mean launch duration, against the 8 TB/s HBM3E peak; `traffic` is
+  roofline    = the split-KV attention kernel, timed with HIP events around it on the
+                stream it runs on (the timed steps call decode_attn_run in its two-stage
+                form, decode_attn_partial then decode_attn_combine, with the events around
+                the first):
+                algorithmic bytes per launch (the KV rows of every sequence plus q) / mean
+                launch duration, against the 8 TB/s HBM3E peak; `traffic` is
                 the HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, read
                 from the profiles/ summary when it was taken on the current kernel source
   cpu_baseline= the fp64 CPU oracle on the same inputs, full step, host cores
@@ -145,12 +148,13 @@ def main() -> int:
         if w.steps:
             lens.copy_(lens_init)
             da.kv_append(desc, kc, vc, lens, k_new, v_new, ws)
-        if ev is not None:
+        if ev is None:
+            da.decode_attn_run(desc, q, kc, vc, lens, max_len, scales, out, ws)
+        else:
             ev[0].record(stream)
-        da.decode_attn_partial(desc, q, kc, vc, lens, max_len, scales, ws)
-        if ev is not None:
+            da.decode_attn_partial(desc, q, kc, vc, lens, max_len, scales, ws)
             ev[1].record(stream)
-        da.decode_attn_combine(desc, lens, max_len, out, ws)
+            da.decode_attn_combine(desc, lens, max_len, out, ws)
 
     for i in range(args.warmup):
         step(i)

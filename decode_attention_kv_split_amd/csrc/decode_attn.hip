@@ -29,6 +29,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 
 #include "decode_attn.h"
 
@@ -81,6 +82,33 @@ __device__ __forceinline__ void widen(const typename Kv<KV>::Vec &v, float *f) {
     }
 }
 
+// ------------------------------------------------------------------ buffer loads
+// Raw buffer loads: a 128-bit resource holds the base address and the number of valid
+// bytes; a lane whose offset is at or past that count reads zeros without touching
+// memory. Word 3 = 0x00020000 is the gfx9-family (incl. gfx950) default format.
+// KV rows are streamed exactly once, so they are loaded with the non-temporal hint (cache
+// policy bit 1, "nt"), which keeps them from displacing other lines; measured on MI355X it
+// raises the split kernel's sustained read rate by 5-10 %.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kLoadNonTemporal = 2;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+template <typename Vec>
+__device__ __forceinline__ Vec buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (sizeof(Vec) == 16) {
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kLoadNonTemporal);
+        return Vec{x[0], x[1], x[2], x[3]};
+    } else {
+        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kLoadNonTemporal);
+        return Vec{x[0], x[1]};
+    }
+}
+
 // ------------------------------------------------------------------ cross-lane sums
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -101,8 +129,10 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 // ------------------------------------------------------------------ kernels
-__global__ void workspace_init_kernel(int32_t *hdr) {
-    if (threadIdx.x < kHeaderBytes / 4) hdr[threadIdx.x] = 0;
+// Zeroes n words (the whole workspace: error word and partial results).
+__global__ void workspace_init_kernel(int32_t *ws, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        ws[i] = 0;
 }
 
 // One workgroup per sequence: copy the h_kv new K rows and V rows into row lens[b] in
@@ -132,15 +162,25 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     if (threadIdx.x == 0) lens[b] = L + 1;
 }
 
+// Arguments of the split kernel (passed by value as one kernel argument).
+struct SplitArgs {
+    const void *q, *kc, *vc;
+    const int32_t *lens;
+    const float *kv_scales;   // [B, h_kv, 2] for fp8 caches, else unused
+    float *part_ml, *part_o;  // per-split (max, sum) and unnormalised output rows
+    float *out;               // decode_attn_run: output rows of single-split sequences
+    int32_t *err;             // sticky device error word
+    int h_q, h_kv, cap, chunk, n_splits, max_len;
+    float qk_scale;           // scale * log2(e)
+};
+
 // One workgroup = one split of one (sequence, KV head) for GT query heads of its group.
-// Writes part_ml[(b*h_q+h)*n_splits+split] = (max, sum) in the base-2 domain and
-// part_o[...*D + d] = unnormalised output (times the V scale for fp8 caches).
-template <int KV, int D, int GT>
-__global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(
-    const void *__restrict__ q_, const void *__restrict__ kc_, const void *__restrict__ vc_,
-    const int32_t *__restrict__ lens, const float *__restrict__ kv_scales,
-    float *__restrict__ part_ml, float *__restrict__ part_o, int h_q, int h_kv, int cap,
-    int chunk, int n_splits, int max_len, float qk_scale) {
+// Every split writes part_ml[(b*h_q+h)*n_splits+split] = (max, sum) in the base-2 domain and
+// part_o[...*D + d] = its unnormalised output row (times the V scale for fp8 caches);
+// lse_combine_kernel merges them. With DIRECT (decode_attn_run) a sequence that fits one
+// split writes its normalised output straight to out and the combine skips it.
+template <int KV, int D, int GT, bool DIRECT>
+__global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a) {
     using T = Kv<KV>;
     using Vec = typename T::Vec;
     constexpr int EPL = T::kEpl;
@@ -148,7 +188,7 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(
     constexpr int RPL = kWave / LPR;   // rows per wave load
     constexpr int TILE = kUnroll * RPL;  // rows per wave per iteration
     constexpr int STEP = TILE * kWaves;  // rows per workgroup per iteration
-    constexpr int VPR = D / EPL;       // vectors per row
+    const int h_q = a.h_q, h_kv = a.h_kv, chunk = a.chunk;
 
     const int split = blockIdx.x;
     const int g = h_q / h_kv;
@@ -157,22 +197,28 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(
     const int h0 = kvh * g + (blockIdx.y % tiles) * GT;
     const int b = blockIdx.z;
 
-    int L = lens[b];
-    L = L > max_len ? max_len : L;  // a length past max_len is flagged by the combine
+    const int L = a.lens[b];
+    if (L < 1 || L > a.max_len) return;  // flagged and zeroed by the combine
+    const int nsplit_b = (L + chunk - 1) / chunk;  // splits this sequence really has
     const int r0 = split * chunk;
-    if (L < 1 || r0 >= L) return;
+    if (r0 >= L) return;
     const int r1 = min(r0 + chunk, L);
 
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int grp = lane / LPR, sub = lane % LPR;
 
     const size_t slot = (size_t)b * h_kv + kvh;
-    const Vec *kbase = reinterpret_cast<const Vec *>(kc_) + slot * cap * VPR + sub;
-    const Vec *vbase = reinterpret_cast<const Vec *>(vc_) + slot * cap * VPR + sub;
-    float vscale = 1.f, sc = qk_scale;
+    constexpr uint32_t ROWB = D * T::kEsz;  // bytes per cache row
+    // Resources cover rows [0, r1) of this (sequence, KV head): loads of rows past the
+    // split's end return zeros (and are masked out of the softmax below).
+    const size_t slot_bytes = (size_t)a.cap * ROWB;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const char *>(a.kc) + slot * slot_bytes, r1 * ROWB);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const char *>(a.vc) + slot * slot_bytes, r1 * ROWB);
+    const uint32_t lane_off = grp * ROWB + sub * (uint32_t)sizeof(Vec);
+    float vscale = 1.f, sc = a.qk_scale;
     if constexpr (KV == DA_FP8_E4M3FN) {
-        sc *= kv_scales[slot * 2 + 0];
-        vscale = kv_scales[slot * 2 + 1];
+        sc *= a.kv_scales[slot * 2 + 0];
+        vscale = a.kv_scales[slot * 2 + 1];
     }
 
     // This lane's slice of q for the GT heads: fp32 values, or packed bf16 pairs for the
@@ -183,10 +229,10 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(
     for (int h = 0; h < GT; ++h) {
         const size_t qoff = ((size_t)b * h_q + h0 + h) * D + sub * EPL;
         if constexpr (KV == DA_F32) {
-            const float4 x = *reinterpret_cast<const float4 *>(static_cast<const float *>(q_) + qoff);
+            const float4 x = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.q) + qoff);
             qf[h][0] = x.x; qf[h][1] = x.y; qf[h][2] = x.z; qf[h][3] = x.w;
         } else {
-            const uint4 x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(q_) + qoff);
+            const uint4 x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qoff);
             if constexpr (KV == DA_BF16) {
                 qp[h][0] = x.x; qp[h][1] = x.y; qp[h][2] = x.z; qp[h][3] = x.w;
             } else {
@@ -206,28 +252,20 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(
         for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
     }
 
-    for (int base = r0 + wave * TILE; base < r1; base += STEP) {
-        Vec kv[kUnroll], vv[kUnroll];
-        bool valid[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int row = base + u * RPL + grp;
-            valid[u] = row < r1;
-            const size_t rr = valid[u] ? row : r1 - 1;  // rows past the end re-read a valid row
-            kv[u] = kbase[rr * VPR];
-            vv[u] = vbase[rr * VPR];
-        }
-        // Step I: scores of this tile's rows for every head of the group.
+    // Steps I-III on one tile already in registers: scores for the GT heads, an online
+    // softmax update of (m, l, o), then the weighted V rows.
+    auto process = [&](const Vec (&kt)[kUnroll], const Vec (&vt)[kUnroll], int tbase) {
         float s[GT][kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
+            const bool valid = tbase + u * RPL + grp < r1;
             float kf[EPL];
-            if constexpr (KV != DA_BF16) widen<KV>(kv[u], kf);
+            if constexpr (KV != DA_BF16) widen<KV>(kt[u], kf);
 #pragma unroll
             for (int h = 0; h < GT; ++h) {
                 float acc = 0.f;
                 if constexpr (KV == DA_BF16) {
-                    const uint32_t w[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+                    const uint32_t w[4] = {kt[u].x, kt[u].y, kt[u].z, kt[u].w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]),
@@ -238,13 +276,10 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(
                     for (int e = 0; e < EPL; ++e) acc = fmaf(kf[e], qf[h][e], acc);
                 }
                 acc = group_sum<LPR>(acc) * sc;
-                s[h][u] = valid[u] ? acc : -INFINITY;
+                s[h][u] = valid ? acc : -INFINITY;
             }
         }
-        // Steps II and III, online: rescale the running sums to the new max, add the tile.
-        float vf[kUnroll][EPL];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) widen<KV>(vv[u], vf[u]);
+        // s becomes p = 2^(s - m_new); l and o are rescaled to the new running max.
 #pragma unroll
         for (int h = 0; h < GT; ++h) {
             float mx = s[h][0];
@@ -253,19 +288,53 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(
             const float mn = fmaxf(m[h], mx);
             const float corr = __builtin_amdgcn_exp2f(m[h] - mn);
             m[h] = mn;
-            float p[kUnroll], ps = 0.f;
+            float ps = 0.f;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) { p[u] = __builtin_amdgcn_exp2f(s[h][u] - mn); ps += p[u]; }
+            for (int u = 0; u < kUnroll; ++u) { s[h][u] = __builtin_amdgcn_exp2f(s[h][u] - mn); ps += s[h][u]; }
             l[h] = fmaf(l[h], corr, ps);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                float acc = o[h][e] * corr;
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) acc = fmaf(p[u], vf[u][e], acc);
-                o[h][e] = acc;
-            }
+            for (int e = 0; e < EPL; ++e) o[h][e] *= corr;
         }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float vf[EPL];
+            widen<KV>(vt[u], vf);
+#pragma unroll
+            for (int h = 0; h < GT; ++h)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(s[h][u], vf[e], o[h][e]);
+        }
+    };
+
+    // Software pipeline over two register buffers: while one tile is computed the loads of
+    // the next are in flight. The whole byte offset sits in the per-lane offset (the scalar
+    // offset is not range-checked), so rows at or past r1 read as zeros.
+    Vec ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
+    auto load = [&](Vec (&kt)[kUnroll], Vec (&vt)[kUnroll], int tbase) {
+        const uint32_t off = lane_off + tbase * ROWB;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            kt[u] = buffer_load<Vec>(krs, off + u * RPL * ROWB, 0);
+            vt[u] = buffer_load<Vec>(vrs, off + u * RPL * ROWB, 0);
+        }
+    };
+    int base = r0 + wave * TILE;
+    const int ntiles = base < r1 ? (r1 - base + STEP - 1) / STEP : 0;
+    if (ntiles > 0) load(ka, va, base);
+    // Pairs of tiles with no exit in between, so each prefetch is consumed on every path
+    // (a load used on one path only would be sunk to its use by the compiler).
+    // The scheduling barriers keep the instruction scheduler from sinking the prefetch
+    // loads toward their uses.
+    for (int t = 0; t + 1 < ntiles; t += 2) {
+        load(kb, vb, base + STEP);
+        __builtin_amdgcn_sched_barrier(0);
+        process(ka, va, base);
+        load(ka, va, base + 2 * STEP);  // past the end this reads zeros and is not processed
+        __builtin_amdgcn_sched_barrier(0);
+        process(kb, vb, base + STEP);
+        base += 2 * STEP;
     }
+    if (ntiles & 1) process(ka, va, base);
 
     // Merge the row groups of this wave (they saw disjoint rows) by their max.
 #pragma unroll
@@ -299,6 +368,7 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(
         }
     }
     __syncthreads();
+    const bool direct = DIRECT && nsplit_b == 1;
     for (int idx = threadIdx.x; idx < GT * D; idx += kBlock) {
         const int h = idx / D, d = idx % D;
         float M = s_m[0][h];
@@ -311,18 +381,23 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(
             Ls = fmaf(s_l[w][h], f, Ls);
             O = fmaf(s_o[w][h][d], f, O);
         }
-        const size_t pidx = ((size_t)b * h_q + h0 + h) * n_splits + split;
-        part_o[pidx * D + d] = O * vscale;
-        if (d == 0) { part_ml[pidx * 2 + 0] = M; part_ml[pidx * 2 + 1] = Ls; }
+        if (direct) {
+            a.out[((size_t)b * h_q + h0 + h) * D + d] = O * vscale / Ls;
+        } else {
+            const size_t pidx = ((size_t)b * h_q + h0 + h) * a.n_splits + split;
+            a.part_o[pidx * D + d] = O * vscale;
+            if (d == 0) { a.part_ml[pidx * 2 + 0] = M; a.part_ml[pidx * 2 + 1] = Ls; }
+        }
     }
 }
 
 // One workgroup per (sequence, query head): merge its splits by log-sum-exp weights.
+// skip_single: sequences with one split were already written by the split kernel.
 template <int D>
 __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     const int32_t *__restrict__ lens, const float *__restrict__ part_ml,
     const float *__restrict__ part_o, float *__restrict__ out, int32_t *__restrict__ err,
-    int h_q, int chunk, int n_splits, int max_len) {
+    int h_q, int chunk, int n_splits, int max_len, int skip_single) {
     constexpr int SG = kCombineBlock / D;  // split groups working side by side
     const int bh = blockIdx.x;
     const int b = bh / h_q;
@@ -334,6 +409,7 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
         return;
     }
     const int ns = (L + chunk - 1) / chunk;
+    if (skip_single && ns == 1) return;
     const float *ml = part_ml + (size_t)bh * n_splits * 2;
     const float *po = part_o + (size_t)bh * n_splits * D;
 
@@ -407,6 +483,9 @@ int validate(const da_desc *d) {
     return DA_OK;
 }
 
+// Workspace layout: [error word, padded to 256 B][split (max, sum) pairs,
+// B*h_q*n_splits*2 fp32][split output rows, B*h_q*n_splits*d_v fp32], each section starting
+// on a 256-byte boundary.
 struct Plan {
     int chunk, n_splits, gt;
     size_t ml_off, o_off, bytes;
@@ -432,6 +511,7 @@ int make_plan(const da_desc *d, int max_len, Plan *p) {
     p->gt = heads_per_block(d->h_q / d->h_kv);
     p->chunk = d->chunk_rows ? d->chunk_rows : choose_chunk(d, max_len, p->gt);
     p->n_splits = (max_len + p->chunk - 1) / p->chunk;
+
     const size_t rows = (size_t)d->batch * d->h_q * p->n_splits;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     p->ml_off = kHeaderBytes;
@@ -446,34 +526,98 @@ int launch_status(const char *what) {
     return DA_OK;
 }
 
-template <int KV, int D>
-void launch_split_dtype(int gt, dim3 grid, hipStream_t s, const void *q, const void *kc, const void *vc,
-                        const int32_t *lens, const float *scales, float *ml, float *po, int h_q, int h_kv,
-                        int cap, int chunk, int ns, int max_len, float qk) {
+template <int KV, int D, bool DIRECT>
+void launch_split_gt(int gt, dim3 grid, hipStream_t st, const SplitArgs &args) {
     switch (gt) {
-    case 4:
-        hipLaunchKernelGGL((split_kv_attn_kernel<KV, D, 4>), grid, dim3(kBlock), 0, s, q, kc, vc, lens, scales, ml,
-                           po, h_q, h_kv, cap, chunk, ns, max_len, qk);
-        break;
-    case 2:
-        hipLaunchKernelGGL((split_kv_attn_kernel<KV, D, 2>), grid, dim3(kBlock), 0, s, q, kc, vc, lens, scales, ml,
-                           po, h_q, h_kv, cap, chunk, ns, max_len, qk);
-        break;
-    default:
-        hipLaunchKernelGGL((split_kv_attn_kernel<KV, D, 1>), grid, dim3(kBlock), 0, s, q, kc, vc, lens, scales, ml,
-                           po, h_q, h_kv, cap, chunk, ns, max_len, qk);
-        break;
+    case 4: hipLaunchKernelGGL((split_kv_attn_kernel<KV, D, 4, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
+    case 2: hipLaunchKernelGGL((split_kv_attn_kernel<KV, D, 2, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
+    default: hipLaunchKernelGGL((split_kv_attn_kernel<KV, D, 1, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
     }
 }
 
-template <int KV>
-void launch_split_kv(int dk, int gt, dim3 grid, hipStream_t s, const void *q, const void *kc, const void *vc,
-                     const int32_t *lens, const float *scales, float *ml, float *po, int h_q, int h_kv, int cap,
-                     int chunk, int ns, int max_len, float qk) {
-    if (dk == 64)
-        launch_split_dtype<KV, 64>(gt, grid, s, q, kc, vc, lens, scales, ml, po, h_q, h_kv, cap, chunk, ns, max_len, qk);
+template <bool DIRECT>
+void launch_split(int kv, int d, int gt, dim3 grid, hipStream_t st, const SplitArgs &args) {
+    if (kv == DA_F32) {
+        if (d == 64) launch_split_gt<DA_F32, 64, DIRECT>(gt, grid, st, args);
+        else launch_split_gt<DA_F32, 128, DIRECT>(gt, grid, st, args);
+    } else if (kv == DA_BF16) {
+        if (d == 64) launch_split_gt<DA_BF16, 64, DIRECT>(gt, grid, st, args);
+        else launch_split_gt<DA_BF16, 128, DIRECT>(gt, grid, st, args);
+    } else {
+        if (d == 64) launch_split_gt<DA_FP8_E4M3FN, 64, DIRECT>(gt, grid, st, args);
+        else launch_split_gt<DA_FP8_E4M3FN, 128, DIRECT>(gt, grid, st, args);
+    }
+}
+
+// Checks the run arguments and launches the split kernel: with out non-NULL, sequences that
+// fit one split are written to out directly (decode_attn_run); otherwise every split writes
+// its partial result (decode_attn_partial).
+int run_split(const da_desc *desc, const void *q, const void *k_cache, const void *v_cache, const int32_t *lens,
+              int32_t max_len, const float *kv_scales, float *out, void *workspace, size_t ws_bytes,
+              void *stream, const char *who) {
+    Plan p;
+    int rc = make_plan(desc, max_len, &p);
+    if (rc) return rc;
+    if (!q || !k_cache || !v_cache || !lens || !workspace)
+        return fail(DA_ERR_INVALID_ARG, "%s: a buffer pointer is NULL", who);
+    if (desc->kv_dtype == DA_FP8_E4M3FN && !kv_scales)
+        return fail(DA_ERR_INVALID_ARG, "%s: an fp8 cache needs kv_scales", who);
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace) ||
+        (out && !aligned16(out)))
+        return fail(DA_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", who);
+    if (ws_bytes < p.bytes)
+        return fail(DA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", who, ws_bytes, p.bytes);
+    char *ws = static_cast<char *>(workspace);
+    SplitArgs args;
+    args.q = q;
+    args.kc = k_cache;
+    args.vc = v_cache;
+    args.lens = lens;
+    args.kv_scales = kv_scales;
+    args.part_ml = reinterpret_cast<float *>(ws + p.ml_off);
+    args.part_o = reinterpret_cast<float *>(ws + p.o_off);
+    args.out = out;
+    args.err = reinterpret_cast<int32_t *>(ws);
+    args.h_q = desc->h_q;
+    args.h_kv = desc->h_kv;
+    args.cap = desc->cap;
+    args.chunk = p.chunk;
+    args.n_splits = p.n_splits;
+    args.max_len = max_len;
+    args.qk_scale = desc->scale * kLog2e;
+    const int g = desc->h_q / desc->h_kv;
+    const dim3 grid(p.n_splits, desc->h_kv * (g / p.gt), desc->batch);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (out)
+        launch_split<true>(desc->kv_dtype, desc->d_k, p.gt, grid, st, args);
     else
-        launch_split_dtype<KV, 128>(gt, grid, s, q, kc, vc, lens, scales, ml, po, h_q, h_kv, cap, chunk, ns, max_len, qk);
+        launch_split<false>(desc->kv_dtype, desc->d_k, p.gt, grid, st, args);
+    return launch_status("split_kv_attn_kernel");
+}
+
+int run_combine(const da_desc *desc, const int32_t *lens, int32_t max_len, float *out, void *workspace,
+                size_t ws_bytes, void *stream, int skip_single, const char *who) {
+    Plan p;
+    int rc = make_plan(desc, max_len, &p);
+    if (rc) return rc;
+    if (!lens || !out || !workspace) return fail(DA_ERR_INVALID_ARG, "%s: a pointer is NULL", who);
+    if (!aligned16(out) || !aligned16(workspace))
+        return fail(DA_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", who);
+    if (ws_bytes < p.bytes)
+        return fail(DA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", who, ws_bytes, p.bytes);
+    char *ws = static_cast<char *>(workspace);
+    const float *ml = reinterpret_cast<const float *>(ws + p.ml_off);
+    const float *po = reinterpret_cast<const float *>(ws + p.o_off);
+    int32_t *err = reinterpret_cast<int32_t *>(ws);
+    const dim3 grid(desc->batch * desc->h_q);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (desc->d_v == 64)
+        hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineBlock), 0, st, lens, ml, po, out, err,
+                           desc->h_q, p.chunk, p.n_splits, max_len, skip_single);
+    else
+        hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, st, lens, ml, po, out, err,
+                           desc->h_q, p.chunk, p.n_splits, max_len, skip_single);
+    return launch_status("lse_combine_kernel");
 }
 
 }  // namespace
@@ -517,8 +661,10 @@ int da_plan(const da_desc *desc, int32_t max_len, int32_t *chunk_rows, int32_t *
 int da_workspace_init(void *workspace, size_t ws_bytes, void *stream) {
     if (!workspace || !aligned16(workspace)) return fail(DA_ERR_INVALID_ARG, "workspace is NULL or misaligned");
     if (ws_bytes < kHeaderBytes) return fail(DA_ERR_WORKSPACE, "workspace smaller than its %zu-byte header", kHeaderBytes);
-    hipLaunchKernelGGL(workspace_init_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
-                       static_cast<int32_t *>(workspace));
+    const size_t words = ws_bytes / 4;
+    const unsigned blocks = (unsigned)std::min<size_t>((words + 255) / 256, 2048);
+    hipLaunchKernelGGL(workspace_init_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<int32_t *>(workspace), words);
     return launch_status("workspace_init_kernel");
 }
 
@@ -543,72 +689,23 @@ int kv_append(const da_desc *desc, void *k_cache, void *v_cache, int32_t *lens, 
 int decode_attn_partial(const da_desc *desc, const void *q, const void *k_cache, const void *v_cache,
                         const int32_t *lens, int32_t max_len, const float *kv_scales, void *workspace,
                         size_t ws_bytes, void *stream) {
-    Plan p;
-    int rc = make_plan(desc, max_len, &p);
-    if (rc) return rc;
-    if (!q || !k_cache || !v_cache || !lens || !workspace)
-        return fail(DA_ERR_INVALID_ARG, "decode_attn: a buffer pointer is NULL");
-    if (desc->kv_dtype == DA_FP8_E4M3FN && !kv_scales)
-        return fail(DA_ERR_INVALID_ARG, "decode_attn: an fp8 cache needs kv_scales");
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
-        return fail(DA_ERR_INVALID_ARG, "decode_attn: buffers must be 16-byte aligned");
-    if (ws_bytes < p.bytes)
-        return fail(DA_ERR_WORKSPACE, "decode_attn: workspace has %zu bytes, needs %zu", ws_bytes, p.bytes);
-    char *ws = static_cast<char *>(workspace);
-    float *ml = reinterpret_cast<float *>(ws + p.ml_off);
-    float *po = reinterpret_cast<float *>(ws + p.o_off);
-    const int g = desc->h_q / desc->h_kv;
-    const dim3 grid(p.n_splits, desc->h_kv * (g / p.gt), desc->batch);
-    const float qk = desc->scale * kLog2e;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (desc->kv_dtype) {
-    case DA_F32:
-        launch_split_kv<DA_F32>(desc->d_k, p.gt, grid, s, q, k_cache, v_cache, lens, kv_scales, ml, po, desc->h_q,
-                                desc->h_kv, desc->cap, p.chunk, p.n_splits, max_len, qk);
-        break;
-    case DA_BF16:
-        launch_split_kv<DA_BF16>(desc->d_k, p.gt, grid, s, q, k_cache, v_cache, lens, kv_scales, ml, po, desc->h_q,
-                                 desc->h_kv, desc->cap, p.chunk, p.n_splits, max_len, qk);
-        break;
-    default:
-        launch_split_kv<DA_FP8_E4M3FN>(desc->d_k, p.gt, grid, s, q, k_cache, v_cache, lens, kv_scales, ml, po,
-                                       desc->h_q, desc->h_kv, desc->cap, p.chunk, p.n_splits, max_len, qk);
-        break;
-    }
-    return launch_status("split_kv_attn_kernel");
+    return run_split(desc, q, k_cache, v_cache, lens, max_len, kv_scales, nullptr, workspace, ws_bytes, stream,
+                     "decode_attn_partial");
 }
 
 int decode_attn_combine(const da_desc *desc, const int32_t *lens, int32_t max_len, float *out, void *workspace,
                         size_t ws_bytes, void *stream) {
-    Plan p;
-    int rc = make_plan(desc, max_len, &p);
-    if (rc) return rc;
-    if (!lens || !out || !workspace) return fail(DA_ERR_INVALID_ARG, "decode_attn_combine: a pointer is NULL");
-    if (!aligned16(out) || !aligned16(workspace))
-        return fail(DA_ERR_INVALID_ARG, "decode_attn_combine: buffers must be 16-byte aligned");
-    if (ws_bytes < p.bytes)
-        return fail(DA_ERR_WORKSPACE, "decode_attn_combine: workspace has %zu bytes, needs %zu", ws_bytes, p.bytes);
-    char *ws = static_cast<char *>(workspace);
-    const dim3 grid(desc->batch * desc->h_q);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (desc->d_v == 64)
-        hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineBlock), 0, s, lens,
-                           reinterpret_cast<const float *>(ws + p.ml_off), reinterpret_cast<const float *>(ws + p.o_off),
-                           out, reinterpret_cast<int32_t *>(ws), desc->h_q, p.chunk, p.n_splits, max_len);
-    else
-        hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, s, lens,
-                           reinterpret_cast<const float *>(ws + p.ml_off), reinterpret_cast<const float *>(ws + p.o_off),
-                           out, reinterpret_cast<int32_t *>(ws), desc->h_q, p.chunk, p.n_splits, max_len);
-    return launch_status("lse_combine_kernel");
+    return run_combine(desc, lens, max_len, out, workspace, ws_bytes, stream, 0, "decode_attn_combine");
 }
 
 int decode_attn_run(const da_desc *desc, const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *lens, int32_t max_len, const float *kv_scales, float *out, void *workspace,
                     size_t ws_bytes, void *stream) {
     if (!out) return fail(DA_ERR_INVALID_ARG, "decode_attn_run: out is NULL");
-    int rc = decode_attn_partial(desc, q, k_cache, v_cache, lens, max_len, kv_scales, workspace, ws_bytes, stream);
+    const int rc = run_split(desc, q, k_cache, v_cache, lens, max_len, kv_scales, out, workspace, ws_bytes, stream,
+                             "decode_attn_run");
     if (rc) return rc;
-    return decode_attn_combine(desc, lens, max_len, out, workspace, ws_bytes, stream);
+    return run_combine(desc, lens, max_len, out, workspace, ws_bytes, stream, 1, "decode_attn_run");
 }
 
 int da_read_device_error(const void *workspace, void *stream, int32_t *code) {

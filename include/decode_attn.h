@@ -82,7 +82,8 @@ typedef struct {
  * Bytes of device workspace decode_attn_run / kv_append need for this descriptor when no
  * sequence is longer than max_len (1 <= max_len <= cap). The workspace holds the sticky
  * error word and the per-split partial results (running max, sum of exponentials and
- * unnormalised output of each split; see decode_attn_partial). *bytes is written on the host.
+ * unnormalised output of each split; see decode_attn_partial). *bytes is written on the
+ * host. A workspace serves one call at a time: calls that overlap on the same workspace race.
  */
 int da_workspace_size(const da_desc *desc, int32_t max_len, size_t *bytes);
 
@@ -93,7 +94,10 @@ int da_workspace_size(const da_desc *desc, int32_t max_len, size_t *bytes);
 int da_plan(const da_desc *desc, int32_t max_len, int32_t *chunk_rows, int32_t *n_splits,
             int32_t *heads_per_block);
 
-/* Clears the workspace's error word (a kernel, not a memset). Call once after allocating. */
+/*
+ * Zeroes the whole workspace with a kernel (not a memset), clearing its error word. Call
+ * once after allocating it.
+ */
 int da_workspace_init(void *workspace, size_t ws_bytes, void *stream);
 
 /*
@@ -112,8 +116,10 @@ int kv_append(const da_desc *desc, void *k_cache, void *v_cache, int32_t *lens,
  * Decode attention for every (b, h) over rows [0, lens[b]) (page "MoA-Structured Decode
  * Attention", §2 Steps I-III, §6 group selection). max_len is a host-side upper bound on
  * every lens[b] (1 <= max_len <= cap) that sizes the work partition. kv_scales is required
- * for an fp8 cache and ignored otherwise. out is fp32 [batch, h_q, d_v]. Equivalent to
- * decode_attn_partial followed by decode_attn_combine.
+ * for an fp8 cache and ignored otherwise. out is fp32 [batch, h_q, d_v]. Two kernels: the
+ * split kernel (a sequence that fits one split is written to out directly, the others leave
+ * per-split partial results) and the log-sum-exp combine of the multi-split sequences. The
+ * result equals decode_attn_partial followed by decode_attn_combine.
  */
 int decode_attn_run(const da_desc *desc, const void *q, const void *k_cache,
                     const void *v_cache, const int32_t *lens, int32_t max_len,

@@ -147,6 +147,41 @@ def test_gqa_equals_mha_on_broadcast_cache():
     check_close(out_gqa, oracle_out(w, c), "bf16")
 
 
+def test_two_stage_path_matches_fused_run():
+    """decode_attn_partial + decode_attn_combine (the split partials merged by a separate
+    kernel) agree with the fused decode_attn_run and with the oracle."""
+    w = W(B=4, h_q=16, h_kv=4, cap=3000, lens=("uniform", 1, 3000), seed=43)
+    c = workloads.generate(w)
+    desc = desc_of(w, 256)
+    g = to_gpu(c)
+    ml = int(c["lens_final"].max())
+    ws = da.Workspace(desc, ml)
+    fused = torch.empty(w.B, w.h_q, w.d, device="cuda")
+    da.decode_attn_run(desc, g["q"], g["k_cache"], g["v_cache"], g["lens_final"], ml, None, fused, ws)
+    two = torch.empty_like(fused)
+    da.decode_attn_partial(desc, g["q"], g["k_cache"], g["v_cache"], g["lens_final"], ml, None, ws)
+    da.decode_attn_combine(desc, g["lens_final"], ml, two, ws)
+    assert da.da_read_device_error(ws) == 0
+    assert (fused - two).abs().max().item() <= 1e-5
+    check_close(two, oracle_out(w, c), "bf16")
+
+
+def test_workspace_reuse_across_calls():
+    """The fused merge's arrival counters return to zero after every call: one workspace
+    serves a sequence of calls with different lengths (single- and multi-split sequences)."""
+    w = W(B=5, h_q=8, h_kv=2, cap=2000, lens=("const", 2000), seed=47)
+    c = workloads.generate(w)
+    desc = desc_of(w, 256)
+    g = to_gpu(c)
+    ws = da.Workspace(desc, w.cap)
+    out = torch.empty(w.B, w.h_q, w.d, device="cuda")
+    for lens in ([2000, 1, 256, 257, 1999], [5, 2000, 700, 256, 1], [1000, 1000, 1000, 1000, 1000]):
+        lt = torch.tensor(lens, dtype=torch.int32)
+        da.decode_attn_run(desc, g["q"], g["k_cache"], g["v_cache"], lt.cuda(), w.cap, None, out, ws)
+        check_close(out, oracle_out(w, c, lens=lt), "bf16", f"lens {lens}")
+    assert da.da_read_device_error(ws) == 0
+
+
 def test_runs_are_bitwise_deterministic():
     w = W(B=4, h_q=32, h_kv=8, cap=3000, lens=("uniform", 1, 3000), seed=41)
     c = workloads.generate(w)
