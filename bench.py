@@ -50,7 +50,7 @@ def parse_args():
                    help="single_head_f32 | mha_bf16 | gqa8_bf16 | mqa_bf16 | gqa8_fp8")
     p.add_argument("--const-len", type=int, default=0,
                    help="override: every sequence this long (the 8K/16K/32K sweep)")
-    p.add_argument("--chunk-rows", type=int, default=0, help="rows per split (0 = library choice)")
+    p.add_argument("--block-rows", type=int, default=0, help="rows per split (0 = library choice)")
     p.add_argument("--rotations", type=int, default=0, help="cache copies to rotate (0 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle timing budget")
@@ -123,7 +123,7 @@ def main() -> int:
     R = args.rotations or max(2, min(8, math.ceil((2 << 30) / max(kv_bytes, 1))))
 
     desc = da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, workloads.TORCH_DTYPE[w.q_dtype],
-                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, args.chunk_rows)
+                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, args.block_rows)
     plan = da.da_plan(desc, max_len)
     q = c["q"].to(dev)
     scales = c["kv_scales"].to(dev) if c["kv_scales"] is not None else None
@@ -181,7 +181,7 @@ def main() -> int:
     algo_bytes = kv_bytes + q_bytes
     achieved = algo_bytes / (split_ms_mean * 1e-3) / 1e9
     value = kv_bytes / (wall_ms * 1e-3) / 1e9
-    traffic = profiled_traffic(args.workload) if not args.const_len and not args.chunk_rows else None
+    traffic = profiled_traffic(args.workload) if not args.const_len and not args.block_rows else None
 
     result = {
         "metric": METRIC,

@@ -48,7 +48,7 @@ class _CDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("cap", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("chunk_rows", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("block_rows", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -62,13 +62,13 @@ class Desc:
     q_dtype: torch.dtype
     kv_dtype: torch.dtype
     scale: float | None = None  # default 1/sqrt(d)
-    chunk_rows: int = 0         # 0: the library's choice
+    block_rows: int = 0         # rows per workgroup at max_len; 0: one resident wave, equal shares
 
     def c(self) -> _CDesc:
         scale = 1.0 / math.sqrt(self.d) if self.scale is None else self.scale
         return _CDesc(self.batch, self.h_q, self.h_kv, self.d, self.d, self.cap,
                       _TORCH_CODE.get(self.q_dtype, -1), _TORCH_CODE.get(self.kv_dtype, -1),
-                      float(scale), self.chunk_rows)
+                      float(scale), self.block_rows)
 
 
 def _check(status: int, where: str) -> None:
@@ -116,7 +116,7 @@ def da_plan(desc: Desc, max_len: int) -> dict:
     cd = desc.c()
     _check(lib().da_plan(ctypes.byref(cd), int(max_len), ctypes.byref(c), ctypes.byref(s), ctypes.byref(g)),
            "da_plan")
-    return {"chunk_rows": c.value, "n_splits": s.value, "heads_per_block": g.value}
+    return {"rows_per_block": c.value, "n_blocks": s.value, "heads_per_block": g.value}
 
 
 def da_workspace_init(ws: torch.Tensor) -> None:

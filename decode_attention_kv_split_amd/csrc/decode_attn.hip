@@ -30,6 +30,9 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "decode_attn.h"
 
@@ -162,55 +165,96 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     if (threadIdx.x == 0) lens[b] = L + 1;
 }
 
+// ------------------------------------------------------------------ work partition
+// A "unit" is one (sequence b, KV head kvh, head tile t) with its lens[b] cache rows; a
+// sequence whose length is out of range contributes no rows. Units are numbered
+// u = (b * h_kv + kvh) * tiles + t and their rows concatenated: unit u starts at row P_u of
+// T rows in total. Workgroup w of N takes rows [w*T/N, (w+1)*T/N), so every workgroup gets
+// the same number of rows whatever the length mix, and N is chosen so that all of them are
+// resident at once. A workgroup's range cut by unit boundaries gives "segments"; the
+// (w, u) pairs of all segments form a monotone staircase, so k = w + u numbers them
+// uniquely (k < N + units) and indexes their partial results. The workgroups that touch
+// unit u are w in [owner(P_u), owner(P_u + L - 1)], owner(x) = ((x + 1) * N - 1) / T,
+// skipping any with an empty range.
+constexpr int kMaxBatch = 1024;
+
+struct Partition {
+    int batch, h_kv, tiles, max_len, nwg;
+};
+
+__device__ __forceinline__ int64_t unit_rows(int L, int max_len) { return (L >= 1 && L <= max_len) ? L : 0; }
+__device__ __forceinline__ int64_t wg_start(int64_t w, int64_t T, int64_t N) { return w * T / N; }
+__device__ __forceinline__ int64_t wg_owner(int64_t x, int64_t T, int64_t N) { return ((x + 1) * N - 1) / T; }
+
+// Exclusive prefix over sequences of their rows in all units, s_pre[0..batch]; s_pre[batch] = T.
+// Needs batch <= kMaxBatch and blockDim.x == kBlock.
+__device__ void sequence_prefix(const int32_t *__restrict__ lens, const Partition &pt, int64_t *s_pre,
+                                int64_t *s_wave) {
+    const int per = (pt.batch + kBlock - 1) / kBlock;  // <= kMaxBatch / kBlock
+    const int64_t upb = (int64_t)pt.h_kv * pt.tiles;
+    int64_t local[kMaxBatch / kBlock];
+    int64_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxBatch / kBlock; ++i) {
+        const int bb = threadIdx.x * per + i;
+        local[i] = sum;
+        if (i < per && bb < pt.batch) sum += unit_rows(lens[bb], pt.max_len) * upb;
+    }
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    int64_t incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off *= 2) {
+        const int64_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    int64_t wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += s_wave[w];
+    const int64_t excl = wbase + incl - sum;
+#pragma unroll
+    for (int i = 0; i < kMaxBatch / kBlock; ++i) {
+        const int bb = threadIdx.x * per + i;
+        if (i < per && bb < pt.batch) s_pre[bb] = excl + local[i];
+    }
+    if (threadIdx.x == kBlock - 1) s_pre[pt.batch] = excl + sum;
+    __syncthreads();
+}
+
 // Arguments of the split kernel (passed by value as one kernel argument).
 struct SplitArgs {
     const void *q, *kc, *vc;
     const int32_t *lens;
     const float *kv_scales;   // [B, h_kv, 2] for fp8 caches, else unused
-    float *part_ml, *part_o;  // per-split (max, sum) and unnormalised output rows
-    float *out;               // decode_attn_run: output rows of single-split sequences
-    int32_t *err;             // sticky device error word
-    int h_q, h_kv, cap, chunk, n_splits, max_len;
+    float *part_ml, *part_o;  // per segment: [GT][2] (max, sum) and [GT][D] output rows
+    float *out;               // decode_attn_run: output rows of units one workgroup covers
+    int h_q, cap;
+    Partition pt;
     float qk_scale;           // scale * log2(e)
 };
 
-// One workgroup = one split of one (sequence, KV head) for GT query heads of its group.
-// Every split writes part_ml[(b*h_q+h)*n_splits+split] = (max, sum) in the base-2 domain and
-// part_o[...*D + d] = its unnormalised output row (times the V scale for fp8 caches);
-// lse_combine_kernel merges them. With DIRECT (decode_attn_run) a sequence that fits one
-// split writes its normalised output straight to out and the combine skips it.
-template <int KV, int D, int GT, bool DIRECT>
-__global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a) {
+// Steps I-III over rows [r0, r1) of one (sequence b, KV head kvh) for query heads
+// h0 .. h0+GT-1, by the whole workgroup. The result (max, sum of exponentials, unnormalised
+// output; base-2 domain, V scale applied) goes to segment slot k of the partial arrays, or
+// normalised straight to out when `direct` (the segment is the whole unit).
+template <int KV, int D, int GT>
+__device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
+                                               size_t k, bool direct) {
     using T = Kv<KV>;
     using Vec = typename T::Vec;
     constexpr int EPL = T::kEpl;
-    constexpr int LPR = D / EPL;       // lanes per row
-    constexpr int RPL = kWave / LPR;   // rows per wave load
+    constexpr int LPR = D / EPL;         // lanes per row
+    constexpr int RPL = kWave / LPR;     // rows per wave load
     constexpr int TILE = kUnroll * RPL;  // rows per wave per iteration
     constexpr int STEP = TILE * kWaves;  // rows per workgroup per iteration
-    const int h_q = a.h_q, h_kv = a.h_kv, chunk = a.chunk;
-
-    const int split = blockIdx.x;
-    const int g = h_q / h_kv;
-    const int tiles = g / GT;
-    const int kvh = blockIdx.y / tiles;
-    const int h0 = kvh * g + (blockIdx.y % tiles) * GT;
-    const int b = blockIdx.z;
-
-    const int L = a.lens[b];
-    if (L < 1 || L > a.max_len) return;  // flagged and zeroed by the combine
-    const int nsplit_b = (L + chunk - 1) / chunk;  // splits this sequence really has
-    const int r0 = split * chunk;
-    if (r0 >= L) return;
-    const int r1 = min(r0 + chunk, L);
-
+    const int h_q = a.h_q;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int grp = lane / LPR, sub = lane % LPR;
 
-    const size_t slot = (size_t)b * h_kv + kvh;
+    const size_t slot = (size_t)b * a.pt.h_kv + kvh;
     constexpr uint32_t ROWB = D * T::kEsz;  // bytes per cache row
     // Resources cover rows [0, r1) of this (sequence, KV head): loads of rows past the
-    // split's end return zeros (and are masked out of the softmax below).
+    // segment's end return zeros (and are masked out of the softmax below).
     const size_t slot_bytes = (size_t)a.cap * ROWB;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const char *>(a.kc) + slot * slot_bytes, r1 * ROWB);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const char *>(a.vc) + slot * slot_bytes, r1 * ROWB);
@@ -322,9 +366,8 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a
     const int ntiles = base < r1 ? (r1 - base + STEP - 1) / STEP : 0;
     if (ntiles > 0) load(ka, va, base);
     // Pairs of tiles with no exit in between, so each prefetch is consumed on every path
-    // (a load used on one path only would be sunk to its use by the compiler).
-    // The scheduling barriers keep the instruction scheduler from sinking the prefetch
-    // loads toward their uses.
+    // (a load used on one path only would be sunk to its use by the compiler); the
+    // scheduling barriers keep the instruction scheduler from sinking the prefetch loads.
     for (int t = 0; t + 1 < ntiles; t += 2) {
         load(kb, vb, base + STEP);
         __builtin_amdgcn_sched_barrier(0);
@@ -356,7 +399,7 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a
         m[h] = M;
     }
 
-    // Merge the waves in LDS and write this split's partial result.
+    // Merge the waves in LDS and write this segment's result.
     __shared__ float s_m[kWaves][GT], s_l[kWaves][GT];
     __shared__ float s_o[kWaves][GT][D];
     if (grp == 0) {
@@ -368,7 +411,6 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a
         }
     }
     __syncthreads();
-    const bool direct = DIRECT && nsplit_b == 1;
     for (int idx = threadIdx.x; idx < GT * D; idx += kBlock) {
         const int h = idx / D, d = idx % D;
         float M = s_m[0][h];
@@ -384,39 +426,104 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a
         if (direct) {
             a.out[((size_t)b * h_q + h0 + h) * D + d] = O * vscale / Ls;
         } else {
-            const size_t pidx = ((size_t)b * h_q + h0 + h) * a.n_splits + split;
-            a.part_o[pidx * D + d] = O * vscale;
-            if (d == 0) { a.part_ml[pidx * 2 + 0] = M; a.part_ml[pidx * 2 + 1] = Ls; }
+            a.part_o[(k * GT + h) * D + d] = O * vscale;
+            if (d == 0) { a.part_ml[(k * GT + h) * 2 + 0] = M; a.part_ml[(k * GT + h) * 2 + 1] = Ls; }
+        }
+    }
+    __syncthreads();  // the LDS arrays are reused by the next segment
+}
+
+// Workgroup w walks its share of the rows, one segment per unit it crosses.
+// DIRECT (decode_attn_run): a unit covered by a single workgroup is written to out directly
+// and lse_combine_kernel skips it; otherwise every segment leaves a partial result.
+template <int KV, int D, int GT, bool DIRECT>
+__global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a) {
+    __shared__ int64_t s_pre[kMaxBatch + 1];
+    __shared__ int64_t s_wave[kWaves];
+    const Partition &pt = a.pt;
+    sequence_prefix(a.lens, pt, s_pre, s_wave);
+    const int64_t Tot = s_pre[pt.batch], N = pt.nwg, w = blockIdx.x;
+    int64_t pos = wg_start(w, Tot, N);
+    const int64_t end = wg_start(w + 1, Tot, N);
+    if (pos >= end) return;
+    // the sequence holding row `pos`: the last b with s_pre[b] <= pos (it has rows)
+    int lo = 0, hi = pt.batch;  // invariant: s_pre[lo] <= pos < s_pre[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (s_pre[mid] <= pos) lo = mid; else hi = mid;
+    }
+    int b = lo;
+    int L = a.lens[b];
+    int64_t off = pos - s_pre[b];
+    int ul = (int)(off / L);     // unit within the sequence
+    int row = (int)(off % L);
+    const int upb = a.pt.h_kv * pt.tiles, g = a.h_q / a.pt.h_kv;
+    while (pos < end) {
+        const int r1 = (int)min<int64_t>((int64_t)L, row + (end - pos));
+        const int kvh = ul / pt.tiles, h0 = kvh * g + (ul % pt.tiles) * GT;
+        const size_t u = (size_t)b * upb + ul;
+        attend_segment<KV, D, GT>(a, b, kvh, h0, row, r1, (size_t)w + u, DIRECT && row == 0 && r1 == L);
+        pos += r1 - row;
+        row = 0;
+        if (++ul == upb && pos < end) {
+            ul = 0;
+            do { ++b; } while (s_pre[b + 1] == s_pre[b]);  // skip sequences without rows
+            L = a.lens[b];
         }
     }
 }
 
-// One workgroup per (sequence, query head): merge its splits by log-sum-exp weights.
-// skip_single: sequences with one split were already written by the split kernel.
+// One workgroup per (sequence, query head): merge the segments of the head's unit by their
+// log-sum-exp weights. skip_single: a unit covered by one workgroup was already written.
 template <int D>
 __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
-    const int32_t *__restrict__ lens, const float *__restrict__ part_ml,
-    const float *__restrict__ part_o, float *__restrict__ out, int32_t *__restrict__ err,
-    int h_q, int chunk, int n_splits, int max_len, int skip_single) {
-    constexpr int SG = kCombineBlock / D;  // split groups working side by side
+    const int32_t *__restrict__ lens, const float *__restrict__ part_ml, const float *__restrict__ part_o,
+    float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt, Partition pt, int skip_single) {
+    constexpr int SG = kCombineBlock / D;  // segment groups working side by side
     const int bh = blockIdx.x;
-    const int b = bh / h_q;
+    const int b = bh / h_q, h = bh % h_q;
     const int L = lens[b];
     float *dst = out + (size_t)bh * D;
-    if (L < 1 || L > max_len) {
+    if (L < 1 || L > pt.max_len) {
         for (int d = threadIdx.x; d < D; d += kCombineBlock) dst[d] = 0.f;
         if (threadIdx.x == 0) atomicOr(err, DA_DEV_ERR_LEN_RANGE);
         return;
     }
-    const int ns = (L + chunk - 1) / chunk;
-    if (skip_single && ns == 1) return;
-    const float *ml = part_ml + (size_t)bh * n_splits * 2;
-    const float *po = part_o + (size_t)bh * n_splits * D;
+    // rows before this sequence, and in total
+    __shared__ int64_t s_red[2][kCombineBlock / kWave];
+    const int64_t upb = (int64_t)pt.h_kv * pt.tiles;
+    int64_t before = 0, total = 0;
+    for (int bb = threadIdx.x; bb < pt.batch; bb += kCombineBlock) {
+        const int64_t r = unit_rows(lens[bb], pt.max_len) * upb;
+        total += r;
+        if (bb < b) before += r;
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off *= 2) {
+        before += __shfl_xor(before, off);
+        total += __shfl_xor(total, off);
+    }
+    if (threadIdx.x % kWave == 0) {
+        s_red[0][threadIdx.x / kWave] = before;
+        s_red[1][threadIdx.x / kWave] = total;
+    }
+    __syncthreads();
+    before = total = 0;
+#pragma unroll
+    for (int w = 0; w < kCombineBlock / kWave; ++w) { before += s_red[0][w]; total += s_red[1][w]; }
+
+    const int g = h_q / pt.h_kv, kvh = h / g, t = (h % g) / gt, hh = h % gt;
+    const int64_t ul = (int64_t)kvh * pt.tiles + t;
+    const int64_t u = b * upb + ul;
+    const int64_t P = before + ul * L, N = pt.nwg;
+    const int64_t wa = wg_owner(P, total, N), wb = wg_owner(P + L - 1, total, N);
+    if (skip_single && wa == wb) return;
 
     __shared__ float red[kCombineBlock / kWave];
     __shared__ float s_acc[SG][D], s_l[SG][D];
     float M = kNegBig;
-    for (int s = threadIdx.x; s < ns; s += kCombineBlock) M = fmaxf(M, ml[2 * s]);
+    for (int64_t w = wa + threadIdx.x; w <= wb; w += kCombineBlock)
+        if (wg_start(w, total, N) < wg_start(w + 1, total, N)) M = fmaxf(M, part_ml[((w + u) * gt + hh) * 2]);
 #pragma unroll
     for (int off = 1; off < kWave; off *= 2) M = fmaxf(M, __shfl_xor(M, off));
     if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = M;
@@ -427,20 +534,21 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
 
     const int d = threadIdx.x % D, sg = threadIdx.x / D;
     float acc = 0.f, ls = 0.f;
-#pragma unroll 4
-    for (int s = sg; s < ns; s += SG) {
-        const float f = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-        ls = fmaf(ml[2 * s + 1], f, ls);
-        acc = fmaf(po[(size_t)s * D + d], f, acc);
+    for (int64_t w = wa + sg; w <= wb; w += SG) {
+        if (wg_start(w, total, N) == wg_start(w + 1, total, N)) continue;  // empty workgroup
+        const size_t kk = (size_t)(w + u) * gt + hh;
+        const float f = __builtin_amdgcn_exp2f(part_ml[kk * 2] - M);
+        ls = fmaf(part_ml[kk * 2 + 1], f, ls);
+        acc = fmaf(part_o[kk * D + d], f, acc);
     }
     s_acc[sg][d] = acc;
     s_l[sg][d] = ls;
     __syncthreads();
     if (sg == 0) {
-        float a = s_acc[0][d], z = s_l[0][d];
+        float x = s_acc[0][d], z = s_l[0][d];
 #pragma unroll
-        for (int i = 1; i < SG; ++i) { a += s_acc[i][d]; z += s_l[i][d]; }
-        dst[d] = a / z;
+        for (int i = 1; i < SG; ++i) { x += s_acc[i][d]; z += s_l[i][d]; }
+        dst[d] = x / z;
     }
 }
 
@@ -464,13 +572,12 @@ int validate(const da_desc *d) {
     if (!d) return fail(DA_ERR_INVALID_ARG, "desc is NULL");
     if (d->batch < 1 || d->h_q < 1 || d->h_kv < 1 || d->cap < 1 || d->d_k < 1 || d->d_v < 1)
         return fail(DA_ERR_INVALID_ARG, "batch, heads, head sizes and cap must be positive");
-    if (d->batch > 65535 || d->h_q > 65535)
-        return fail(DA_ERR_UNSUPPORTED, "batch and h_q are limited to 65535 (grid dimensions)");
+    if (d->batch > kMaxBatch)
+        return fail(DA_ERR_UNSUPPORTED, "batch is limited to %d sequences per call (got %d)", kMaxBatch, d->batch);
     if (d->h_q % d->h_kv)
         return fail(DA_ERR_INVALID_ARG, "h_q (%d) is not a multiple of h_kv (%d)", d->h_q, d->h_kv);
     if (!std::isfinite(d->scale)) return fail(DA_ERR_INVALID_ARG, "scale is not finite");
-    if (d->chunk_rows < 0 || d->chunk_rows % 256)
-        return fail(DA_ERR_INVALID_ARG, "chunk_rows must be 0 or a positive multiple of 256");
+    if (d->block_rows < 0) return fail(DA_ERR_INVALID_ARG, "block_rows must be >= 0");
     if (!elem_size(d->q_dtype) || !elem_size(d->kv_dtype))
         return fail(DA_ERR_INVALID_ARG, "unknown dtype code");
     if (d->d_k != d->d_v || (d->d_k != 64 && d->d_k != 128))
@@ -483,24 +590,59 @@ int validate(const da_desc *d) {
     return DA_OK;
 }
 
-// Workspace layout: [error word, padded to 256 B][split (max, sum) pairs,
-// B*h_q*n_splits*2 fp32][split output rows, B*h_q*n_splits*d_v fp32], each section starting
-// on a 256-byte boundary.
+// Workspace layout: [error word, padded to 256 B][segment (max, sum) pairs,
+// (N + units) * GT * 2 fp32][segment output rows, (N + units) * GT * d_v fp32], each section
+// starting on a 256-byte boundary (N workgroups, units = batch * h_kv * head tiles).
 struct Plan {
-    int chunk, n_splits, gt;
+    int gt, tiles, nwg;
     size_t ml_off, o_off, bytes;
 };
 
 int heads_per_block(int g) { return g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1; }
 
-// Rows per split: the largest power-of-two multiple of 256 (up to 4096) that still gives
-// at least 2048 workgroups at max_len, so that 256 CUs stay busy, and the longest
-// sequence is cut in as few splits as that allows.
-int choose_chunk(const da_desc *d, int max_len, int gt) {
-    const long blocks_per_split = (long)d->batch * d->h_kv * (d->h_q / d->h_kv / gt);
-    int chunk = 256;
-    while (chunk < 4096 && blocks_per_split * ((max_len + 2 * chunk - 1) / (2 * chunk)) >= 2048) chunk *= 2;
-    return chunk;
+constexpr int kMinRowsPerBlock = 256;  // below this a workgroup's share is mostly overhead
+constexpr int kFallbackResident = 512; // workgroups planned for when no device is visible
+
+// Workgroups to launch for one split-kernel instantiation on the current device: every CU
+// gets the same number, min(what fits, kBlocksPerCu), cached per (device, kernel). Measured
+// on MI355X (256 CUs), counts that are not a multiple of the CU count leave some CUs with
+// more shares than others and run up to 15 % slower; two 4-wave workgroups per CU stream
+// faster than three.
+constexpr int kBlocksPerCu = 2;
+int resident_workgroups(const void *kernel) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void *>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return kFallbackResident;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({dev, kernel});
+    if (it != cache.end()) return it->second;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess || cus < 1 ||
+        per_cu < 1) {
+        (void)hipGetLastError();
+        return kFallbackResident;
+    }
+    return cache[{dev, kernel}] = cus * std::min(per_cu, kBlocksPerCu);
+}
+
+template <int KV, int D>
+const void *split_kernel_ptr(int gt) {
+    switch (gt) {
+    case 4: return reinterpret_cast<const void *>(&split_kv_attn_kernel<KV, D, 4, false>);
+    case 2: return reinterpret_cast<const void *>(&split_kv_attn_kernel<KV, D, 2, false>);
+    default: return reinterpret_cast<const void *>(&split_kv_attn_kernel<KV, D, 1, false>);
+    }
+}
+
+const void *split_kernel_ptr(int kv, int d, int gt) {
+    if (kv == DA_F32) return d == 64 ? split_kernel_ptr<DA_F32, 64>(gt) : split_kernel_ptr<DA_F32, 128>(gt);
+    if (kv == DA_BF16) return d == 64 ? split_kernel_ptr<DA_BF16, 64>(gt) : split_kernel_ptr<DA_BF16, 128>(gt);
+    return d == 64 ? split_kernel_ptr<DA_FP8_E4M3FN, 64>(gt) : split_kernel_ptr<DA_FP8_E4M3FN, 128>(gt);
 }
 
 int make_plan(const da_desc *d, int max_len, Plan *p) {
@@ -509,14 +651,22 @@ int make_plan(const da_desc *d, int max_len, Plan *p) {
     if (max_len < 1 || max_len > d->cap)
         return fail(DA_ERR_INVALID_ARG, "max_len (%d) must be in [1, cap = %d]", max_len, d->cap);
     p->gt = heads_per_block(d->h_q / d->h_kv);
-    p->chunk = d->chunk_rows ? d->chunk_rows : choose_chunk(d, max_len, p->gt);
-    p->n_splits = (max_len + p->chunk - 1) / p->chunk;
-
-    const size_t rows = (size_t)d->batch * d->h_q * p->n_splits;
+    p->tiles = d->h_q / d->h_kv / p->gt;
+    const int64_t units = (int64_t)d->batch * d->h_kv * p->tiles;
+    const int64_t rows_max = units * max_len;  // rows of all units at max_len
+    int64_t nwg;
+    if (d->block_rows) {
+        nwg = (rows_max + d->block_rows - 1) / d->block_rows;
+    } else {
+        nwg = resident_workgroups(split_kernel_ptr(d->kv_dtype, d->d_k, p->gt));
+        nwg = std::min<int64_t>(nwg, (rows_max + kMinRowsPerBlock - 1) / kMinRowsPerBlock);
+    }
+    p->nwg = (int)std::max<int64_t>(1, std::min<int64_t>(nwg, 1 << 20));
+    const size_t segs = (size_t)p->nwg + units;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     p->ml_off = kHeaderBytes;
-    p->o_off = p->ml_off + up(rows * 2 * sizeof(float));
-    p->bytes = p->o_off + up(rows * d->d_v * sizeof(float));
+    p->o_off = p->ml_off + up(segs * p->gt * 2 * sizeof(float));
+    p->bytes = p->o_off + up(segs * p->gt * d->d_v * sizeof(float));
     return DA_OK;
 }
 
@@ -549,9 +699,19 @@ void launch_split(int kv, int d, int gt, dim3 grid, hipStream_t st, const SplitA
     }
 }
 
-// Checks the run arguments and launches the split kernel: with out non-NULL, sequences that
-// fit one split are written to out directly (decode_attn_run); otherwise every split writes
-// its partial result (decode_attn_partial).
+Partition partition_of(const da_desc *desc, const Plan &p, int max_len) {
+    Partition pt;
+    pt.batch = desc->batch;
+    pt.h_kv = desc->h_kv;
+    pt.tiles = p.tiles;
+    pt.max_len = max_len;
+    pt.nwg = p.nwg;
+    return pt;
+}
+
+// Checks the run arguments and launches the split kernel: with out non-NULL, units that one
+// workgroup covers are written to out directly (decode_attn_run); otherwise every segment
+// writes its partial result (decode_attn_partial).
 int run_split(const da_desc *desc, const void *q, const void *k_cache, const void *v_cache, const int32_t *lens,
               int32_t max_len, const float *kv_scales, float *out, void *workspace, size_t ws_bytes,
               void *stream, const char *who) {
@@ -577,21 +737,15 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     args.part_ml = reinterpret_cast<float *>(ws + p.ml_off);
     args.part_o = reinterpret_cast<float *>(ws + p.o_off);
     args.out = out;
-    args.err = reinterpret_cast<int32_t *>(ws);
     args.h_q = desc->h_q;
-    args.h_kv = desc->h_kv;
     args.cap = desc->cap;
-    args.chunk = p.chunk;
-    args.n_splits = p.n_splits;
-    args.max_len = max_len;
+    args.pt = partition_of(desc, p, max_len);
     args.qk_scale = desc->scale * kLog2e;
-    const int g = desc->h_q / desc->h_kv;
-    const dim3 grid(p.n_splits, desc->h_kv * (g / p.gt), desc->batch);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (out)
-        launch_split<true>(desc->kv_dtype, desc->d_k, p.gt, grid, st, args);
+        launch_split<true>(desc->kv_dtype, desc->d_k, p.gt, dim3(p.nwg), st, args);
     else
-        launch_split<false>(desc->kv_dtype, desc->d_k, p.gt, grid, st, args);
+        launch_split<false>(desc->kv_dtype, desc->d_k, p.gt, dim3(p.nwg), st, args);
     return launch_status("split_kv_attn_kernel");
 }
 
@@ -610,13 +764,14 @@ int run_combine(const da_desc *desc, const int32_t *lens, int32_t max_len, float
     const float *po = reinterpret_cast<const float *>(ws + p.o_off);
     int32_t *err = reinterpret_cast<int32_t *>(ws);
     const dim3 grid(desc->batch * desc->h_q);
+    const Partition pt = partition_of(desc, p, max_len);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (desc->d_v == 64)
         hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineBlock), 0, st, lens, ml, po, out, err,
-                           desc->h_q, p.chunk, p.n_splits, max_len, skip_single);
+                           desc->h_q, p.gt, pt, skip_single);
     else
         hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, st, lens, ml, po, out, err,
-                           desc->h_q, p.chunk, p.n_splits, max_len, skip_single);
+                           desc->h_q, p.gt, pt, skip_single);
     return launch_status("lse_combine_kernel");
 }
 
@@ -647,13 +802,14 @@ int da_workspace_size(const da_desc *desc, int32_t max_len, size_t *bytes) {
     return DA_OK;
 }
 
-int da_plan(const da_desc *desc, int32_t max_len, int32_t *chunk_rows, int32_t *n_splits,
+int da_plan(const da_desc *desc, int32_t max_len, int32_t *rows_per_block, int32_t *n_blocks,
             int32_t *heads_per_block_out) {
     Plan p;
     const int rc = make_plan(desc, max_len, &p);
     if (rc) return rc;
-    if (chunk_rows) *chunk_rows = p.chunk;
-    if (n_splits) *n_splits = p.n_splits;
+    const int64_t rows_max = (int64_t)desc->batch * desc->h_kv * p.tiles * max_len;
+    if (rows_per_block) *rows_per_block = (int32_t)((rows_max + p.nwg - 1) / p.nwg);
+    if (n_blocks) *n_blocks = p.nwg;
     if (heads_per_block_out) *heads_per_block_out = p.gt;
     return DA_OK;
 }

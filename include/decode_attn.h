@@ -60,10 +60,12 @@ typedef enum { DA_F32 = 0, DA_BF16 = 1, DA_FP8_E4M3FN = 2 } da_dtype;
 
 /*
  * Problem descriptor. Supported: d_k == d_v in {64, 128}; (q_dtype, kv_dtype) in
- * {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN)}; any h_q that is a multiple of h_kv.
- * scale is the factor of Step I (1/sqrt(d_k) in the page's setting), applied once.
- * chunk_rows is the number of cache rows each split covers (a multiple of 256), or 0 to
- * let the library choose from the shape and max_len.
+ * {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN)}; any h_q that is a multiple of h_kv;
+ * batch <= 1024. scale is the factor of Step I (1/sqrt(d_k) in the page's setting), applied
+ * once. Work partition: the cache rows of all (sequence, KV head) pairs, taken in order,
+ * are cut into equal contiguous shares, one per workgroup. block_rows = 0 lets the library
+ * use one share per workgroup that fits on the device at once; block_rows > 0 asks for
+ * shares of about block_rows rows at max_len instead.
  */
 typedef struct {
     int32_t batch;
@@ -75,7 +77,7 @@ typedef struct {
     int32_t q_dtype;  /* da_dtype */
     int32_t kv_dtype; /* da_dtype */
     float scale;
-    int32_t chunk_rows;
+    int32_t block_rows;
 } da_desc;
 
 /*
@@ -89,9 +91,10 @@ int da_workspace_size(const da_desc *desc, int32_t max_len, size_t *bytes);
 
 /*
  * Chosen work partition for (desc, max_len), all outputs host int32 (any may be NULL):
- * rows per split, splits per sequence at max_len, query heads each workgroup serves.
+ * cache rows per workgroup when every sequence has max_len rows, workgroups launched,
+ * query heads each workgroup serves.
  */
-int da_plan(const da_desc *desc, int32_t max_len, int32_t *chunk_rows, int32_t *n_splits,
+int da_plan(const da_desc *desc, int32_t max_len, int32_t *rows_per_block, int32_t *n_blocks,
             int32_t *heads_per_block);
 
 /*
@@ -117,9 +120,9 @@ int kv_append(const da_desc *desc, void *k_cache, void *v_cache, int32_t *lens,
  * Attention", §2 Steps I-III, §6 group selection). max_len is a host-side upper bound on
  * every lens[b] (1 <= max_len <= cap) that sizes the work partition. kv_scales is required
  * for an fp8 cache and ignored otherwise. out is fp32 [batch, h_q, d_v]. Two kernels: the
- * split kernel (a sequence that fits one split is written to out directly, the others leave
- * per-split partial results) and the log-sum-exp combine of the multi-split sequences. The
- * result equals decode_attn_partial followed by decode_attn_combine.
+ * split kernel (a (sequence, KV head) whose rows one workgroup covers is written to out
+ * directly, the others leave per-segment partial results) and the log-sum-exp combine of
+ * the rest. The result equals decode_attn_partial followed by decode_attn_combine.
  */
 int decode_attn_run(const da_desc *desc, const void *q, const void *k_cache,
                     const void *v_cache, const int32_t *lens, int32_t max_len,
@@ -127,9 +130,9 @@ int decode_attn_run(const da_desc *desc, const void *q, const void *k_cache,
                     void *stream);
 
 /*
- * First stage of decode_attn_run: each (sequence, KV head, split of chunk_rows rows) reads
- * its K and V rows once for all query heads of the group and writes, per query head, the
- * split's running max (base-2 exponent domain), its sum of exponentials and its
+ * First stage of decode_attn_run: each workgroup reads its share of K and V rows once for
+ * all query heads of the group and writes, per (sequence, KV head) segment of its share and
+ * per query head, the running max (base-2 exponent domain), the sum of exponentials and the
  * unnormalised output row to the workspace.
  */
 int decode_attn_partial(const da_desc *desc, const void *q, const void *k_cache,
@@ -137,7 +140,7 @@ int decode_attn_partial(const da_desc *desc, const void *q, const void *k_cache,
                         const float *kv_scales, void *workspace, size_t ws_bytes, void *stream);
 
 /*
- * Second stage: merges the splits of every (b, h) by their log-sum-exp weights into out
+ * Second stage: merges the segments of every (b, h) by their log-sum-exp weights into out
  * (an exact rewriting of Step II's normalisation over the whole row range).
  */
 int decode_attn_combine(const da_desc *desc, const int32_t *lens, int32_t max_len, float *out,

@@ -26,9 +26,9 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-def desc_of(w: workloads.Workload, chunk_rows: int = 0) -> da.Desc:
+def desc_of(w: workloads.Workload, block_rows: int = 0) -> da.Desc:
     return da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, workloads.TORCH_DTYPE[w.q_dtype],
-                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, chunk_rows)
+                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, block_rows)
 
 
 def to_gpu(case: dict, dev="cuda") -> dict:
@@ -51,10 +51,10 @@ def check_close(got: torch.Tensor, ref: np.ndarray, kv: str, what: str = "") -> 
     return worst
 
 
-def run_gpu(w: workloads.Workload, c: dict, chunk_rows: int = 0, max_len: int | None = None,
+def run_gpu(w: workloads.Workload, c: dict, block_rows: int = 0, max_len: int | None = None,
             lens_key: str = "lens_final"):
     """Appends `steps` rows (if any) then attends once; returns out (GPU) and the GPU caches."""
-    desc = desc_of(w, chunk_rows)
+    desc = desc_of(w, block_rows)
     g = to_gpu(c)
     lens = g["lens_init"].clone()
     ml = int(c["lens_final"].max()) if max_len is None else max_len

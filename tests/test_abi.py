@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def _desc(**kw):
     base = dict(batch=2, h_q=8, h_kv=2, d_k=128, d_v=128, cap=1024, q_dtype=1, kv_dtype=1,
-                scale=0.088, chunk_rows=0)
+                scale=0.088, block_rows=0)
     base.update(kw)
     return da._CDesc(**base)
 
@@ -65,7 +65,8 @@ def _ws_size(lib, desc, max_len):
     (dict(d_k=128, d_v=64), 100, -2),          # d_k != d_v
     (dict(q_dtype=0, kv_dtype=1), 100, -2),    # dtype pair not built
     (dict(kv_dtype=7), 100, -1),               # unknown dtype code
-    (dict(chunk_rows=100), 100, -1),           # chunk not a multiple of 256
+    (dict(block_rows=-1), 100, -1),            # negative workgroup share
+    (dict(batch=1025), 100, -2),               # more sequences than one call takes
     (dict(scale=float("nan")), 100, -1),
 ])
 def test_invalid_descriptors_are_rejected(lib, kw, max_len, code):
@@ -74,18 +75,29 @@ def test_invalid_descriptors_are_rejected(lib, kw, max_len, code):
     assert lib.da_last_error()  # a message was recorded
 
 
+def _plan(lib, d, max_len):
+    r, n, g = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    assert lib.da_plan(ctypes.byref(d), max_len, ctypes.byref(r), ctypes.byref(n), ctypes.byref(g)) == 0
+    return r.value, n.value, g.value
+
+
 def test_workspace_size_and_plan(lib):
+    """The partition covers every row at max_len; the workspace holds one (max, sum, row)
+    slot per segment (workgroups + units) and per head of a workgroup."""
     d = _desc(batch=16, h_q=32, h_kv=8, cap=32768)
     rc, n = _ws_size(lib, d, 32768)
     assert rc == 0
-    c, s, g = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    assert lib.da_plan(ctypes.byref(d), 32768, ctypes.byref(c), ctypes.byref(s), ctypes.byref(g)) == 0
-    assert c.value % 256 == 0 and s.value == -(-32768 // c.value) and g.value == 4
-    rows = 16 * 32 * s.value
-    assert n >= 256 + rows * 2 * 4 + rows * 128 * 4
-    d2 = _desc(batch=16, h_q=32, h_kv=8, cap=32768, chunk_rows=512)
-    assert lib.da_plan(ctypes.byref(d2), 1000, ctypes.byref(c), ctypes.byref(s), None) == 0
-    assert (c.value, s.value) == (512, 2)
+    rows_per_block, nblocks, gt = _plan(lib, d, 32768)
+    units = 16 * 8 * (32 // 8 // gt)
+    assert gt == 4 and rows_per_block * nblocks >= units * 32768 and rows_per_block >= 256
+    segs = nblocks + units
+    assert n >= 256 + segs * gt * 2 * 4 + segs * gt * 128 * 4
+    d2 = _desc(batch=16, h_q=32, h_kv=8, cap=32768, block_rows=512)
+    assert _plan(lib, d2, 1000) == (512, -(-128 * 1000 // 512), 4)
+    # grouped heads per workgroup: the largest of 4, 2, 1 dividing g
+    assert _plan(lib, _desc(h_q=6, h_kv=2), 100)[2] == 1
+    assert _plan(lib, _desc(h_q=12, h_kv=2), 100)[2] == 2
+    assert _plan(lib, _desc(h_q=64, h_kv=2), 100)[2] == 4
 
 
 def test_null_and_misaligned_pointers_fail_before_launch(lib):

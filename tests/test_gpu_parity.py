@@ -77,7 +77,7 @@ def test_parity_small(kv, d, h_q, h_kv, lens, chunk):
     w = W(kv_dtype=kv, d=d, h_q=h_q, h_kv=h_kv, lens=lens, seed=100 + CASES.index((kv, d, h_q, h_kv, lens, chunk)))
     c = workloads.generate(w)
     log(f"case {kv} d={d} h_q={h_q} h_kv={h_kv} chunk={chunk} lens={c['lens_final'].tolist()}")
-    out, _, _, err = run_gpu(w, c, chunk_rows=chunk)
+    out, _, _, err = run_gpu(w, c, block_rows=chunk)
     assert err == 0
     check_close(out, oracle_out(w, c), kv)
 
@@ -101,9 +101,42 @@ def test_parity_tile_and_split_boundaries(kv):
     c["lens_final"] = torch.tensor(edges, dtype=torch.int32)
     c["lens_init"] = c["lens_final"] - steps
     log(f"case boundaries {kv} lens={edges}")
-    out, _, _, err = run_gpu(w, c, chunk_rows=256, max_len=1024)
+    out, _, _, err = run_gpu(w, c, block_rows=256, max_len=1024)
     assert err == 0
     check_close(out, oracle_out(w, c), kv)
+
+
+@pytest.mark.parametrize("block_rows", [1, 37, 100, 1000])
+def test_parity_uneven_workgroup_shares(block_rows):
+    """Workgroup shares that are not multiples of a tile and cross (sequence, KV head)
+    boundaries many times, including one-row sequences."""
+    w = W(B=5, h_q=8, h_kv=2, cap=700, lens=("uniform", 1, 700), seed=60 + block_rows)
+    c = workloads.generate(w)
+    c["lens_final"][1] = 1
+    c["lens_init"][1] = 1
+    log(f"case block_rows={block_rows} lens={c['lens_final'].tolist()}")
+    out, _, _, err = run_gpu(w, c, block_rows=block_rows)
+    assert err == 0
+    check_close(out, oracle_out(w, c), "bf16")
+
+
+def test_invalid_lengths_between_valid_ones():
+    """Sequences with an out-of-range length hold no rows of the partition: their output
+    is zeroed and flagged, and the sequences around them are unaffected."""
+    w = W(B=4, h_q=8, h_kv=2, cap=600, lens=("const", 600), seed=71)
+    c = workloads.generate(w)
+    desc = desc_of(w, 100)
+    g = to_gpu(c)
+    lens = torch.tensor([300, 0, 600, 500], dtype=torch.int32)
+    ws = da.Workspace(desc, 550)
+    out = torch.full((w.B, w.h_q, w.d), 3.0, device="cuda")
+    da.decode_attn_run(desc, g["q"], g["k_cache"], g["v_cache"], lens.cuda(), 550, None, out, ws)
+    assert da.da_read_device_error(ws) == da.DEV_ERR_LEN_RANGE
+    o = out.cpu()
+    assert torch.equal(o[1], torch.zeros(8, 128)) and torch.equal(o[2], torch.zeros(8, 128))
+    ok = torch.tensor([300, 1, 1, 500], dtype=torch.int32)
+    ref = oracle_out(w, c, lens=ok)
+    check_close(o[[0, 3]], ref[[0, 3]], "bf16")
 
 
 def test_single_row_returns_that_value_row_exactly():
@@ -185,8 +218,8 @@ def test_workspace_reuse_across_calls():
 def test_runs_are_bitwise_deterministic():
     w = W(B=4, h_q=32, h_kv=8, cap=3000, lens=("uniform", 1, 3000), seed=41)
     c = workloads.generate(w)
-    a, _, _, _ = run_gpu(w, c, chunk_rows=256)
-    b, _, _, _ = run_gpu(w, c, chunk_rows=256)
+    a, _, _, _ = run_gpu(w, c, block_rows=256)
+    b, _, _, _ = run_gpu(w, c, block_rows=256)
     assert torch.equal(a, b)
 
 
