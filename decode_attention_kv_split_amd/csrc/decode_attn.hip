@@ -30,6 +30,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <type_traits>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -433,11 +434,275 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
     __syncthreads();  // the LDS arrays are reused by the next segment
 }
 
-// Workgroup w walks its share of the rows, one segment per unit it crosses.
-// DIRECT (decode_attn_run): a unit covered by a single workgroup is written to out directly
-// and lse_combine_kernel skips it; otherwise every segment leaves a partial result.
-template <int KV, int D, int GT, bool DIRECT>
-__global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a) {
+// ------------------------------------------------------------------ MFMA flavour (g >= 8)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// Two e4m3fn codes (bytes 2*HI, 2*HI+1 of w) -> two bf16 packed in a word; exact, since every
+// e4m3fn value is a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+    const bf16x2v_t r = {(__bf16)f[0], (__bf16)f[1]};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight elements (one lane's load) as bf16x8.
+template <int KV>
+__device__ __forceinline__ uint4 to_bf16x8(const typename std::conditional<KV == DA_BF16, uint4, uint2>::type &v) {
+    if constexpr (KV == DA_BF16) {
+        return v;
+    } else {
+        return uint4{fp8x2_to_bf16x2<false>(v.x), fp8x2_to_bf16x2<true>(v.x), fp8x2_to_bf16x2<false>(v.y),
+                     fp8x2_to_bf16x2<true>(v.y)};
+    }
+}
+
+// Steps I-III over rows [r0, r1) of (b, kvh) for query heads h0 .. h0+GT-1 on the matrix cores.
+// Per 16-row tile and wave:
+//   * Step I as S = K_tile . Q^T with v_mfma_f32_16x16x32_bf16: the K rows are the A operand
+//     exactly as stored (lane l loads row l%16, elements 8*(l/16) .. of each 32-wide block),
+//     q of 16 heads is the B operand. The result gives lane l the scores of rows
+//     4*(l/16)+i (i < 4) for head l%16.
+//   * Step II online on that layout: the tile max per head reduces over the 4 lane groups;
+//     O is rescaled (through a 16-float LDS transpose) only when some head's max grew.
+//   * Step III as O += P . V_tile with v_mfma_f32_16x16x16_bf16: the score layout above is
+//     exactly the A-operand layout of P. V is staged row-major in LDS (as bf16) and read back
+//     as the B operand with ds_read_b64_tr_b16. P is split into bf16 hi + lo parts (two
+//     MFMAs) so that P.V keeps ~16 bits of P's precision.
+// GT = 8, 16 or 32 heads (HT = 1 or 2 MFMA tiles of 16; heads past GT are zero padding).
+template <int KV, int D, int GT>
+__device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
+                                                    size_t k, bool direct) {
+    static_assert(KV == DA_BF16 || KV == DA_FP8_E4M3FN, "MFMA flavour takes bf16 or fp8 caches");
+    using LVec = typename std::conditional<KV == DA_BF16, uint4, uint2>::type;  // 8 elements
+    constexpr int HT = (GT + 15) / 16;
+    constexpr int KB = D / 32;           // 32-wide k blocks of Step I
+    constexpr int NB = D / 16;           // 16-wide d blocks of Step III
+    constexpr int ESZ = Kv<KV>::kEsz;
+    constexpr uint32_t ROWB = D * ESZ;   // bytes per cache row
+    constexpr int TR = 16;               // rows per wave tile
+    constexpr int STEP = TR * kWaves;    // rows per workgroup iteration
+    constexpr int VROW = D + 8;          // staged V row, bf16 elements (16-byte pad)
+    constexpr int VL = D / 8;            // lanes per row of a V load
+    constexpr int VRPI = kWave / VL;     // V rows per load instruction
+    constexpr int VLD = TR / VRPI;       // V loads per tile
+    const int h_q = a.h_q;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int lr = lane % 16, lg = lane / 16;
+    const int vrow = lane / VL, vcol = (lane % VL) * 8;
+
+    const size_t slot = (size_t)b * a.pt.h_kv + kvh;
+    const size_t slot_bytes = (size_t)a.cap * ROWB;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const char *>(a.kc) + slot * slot_bytes, r1 * ROWB);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const char *>(a.vc) + slot * slot_bytes, r1 * ROWB);
+    float vscale = 1.f, sc = a.qk_scale;
+    if constexpr (KV == DA_FP8_E4M3FN) {
+        sc *= a.kv_scales[slot * 2 + 0];
+        vscale = a.kv_scales[slot * 2 + 1];
+    }
+
+    // q^T as the B operand of Step I: lane l holds q[head ht*16 + l%16][kb*32 + 8*(l/16) ..+8].
+    bf16x8_t qb[HT][KB];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const int head = ht * 16 + lr;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            uint4 x = {0u, 0u, 0u, 0u};
+            if (head < GT)
+                x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) +
+                                                      ((size_t)b * h_q + h0 + head) * D + kb * 32 + 8 * lg);
+            qb[ht][kb] = __builtin_bit_cast(bf16x8_t, x);
+        }
+    }
+
+    float m[HT], lp[HT];
+    f32x4_t o[HT][NB];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        m[ht] = kNegBig;
+        lp[ht] = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[ht][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    __shared__ __align__(16) uint16_t s_v[kWaves][TR * VROW];
+    __shared__ __align__(16) float s_c[kWaves][HT * 16];
+
+    auto process = [&](const LVec (&kt)[KB], const LVec (&vt)[VLD], int tb) {
+        // stage this tile's V rows (as bf16) in the wave's LDS tile
+#pragma unroll
+        for (int u = 0; u < VLD; ++u)
+            *reinterpret_cast<uint4 *>(&s_v[wave][(vrow + u * VRPI) * VROW + vcol]) = to_bf16x8<KV>(vt[u]);
+        // Step I
+        bf16x8_t ka[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) ka[kb] = __builtin_bit_cast(bf16x8_t, to_bf16x8<KV>(kt[kb]));
+        bool grew = false;
+        float corr[HT];
+        bf16x4_t phi[HT], plo[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qb[ht][kb], sacc, 0, 0, 0);
+            // Step II (online): rows tb + 4*lg + i, head ht*16 + lr
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * lg + i < r1) ? sacc[i] * sc : -INFINITY;
+            float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float mn = fmaxf(m[ht], tmax);
+            corr[ht] = __builtin_amdgcn_exp2f(m[ht] - mn);
+            grew |= mn > m[ht];
+            m[ht] = mn;
+            float p[4], ps = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - mn); ps += p[i]; }
+            lp[ht] = fmaf(lp[ht], corr[ht], ps);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                phi[ht][i] = (__bf16)p[i];
+                plo[ht][i] = (__bf16)(p[i] - (float)phi[ht][i]);
+            }
+        }
+        if (__builtin_amdgcn_ballot_w64(grew)) {
+            // corr is held per head = l%16; O rows are heads 4*(l/16)+i: transpose via LDS
+            if (lg == 0) {
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) s_c[wave][ht * 16 + lr] = corr[ht];
+            }
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                const float4 c4 = *reinterpret_cast<const float4 *>(&s_c[wave][ht * 16 + 4 * lg]);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    o[ht][nb][0] *= c4.x; o[ht][nb][1] *= c4.y; o[ht][nb][2] *= c4.z; o[ht][nb][3] *= c4.w;
+                }
+            }
+        }
+        // Step III
+        typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int e = (4 * lg + lr / 4) * VROW + nb * 16 + 4 * (lane % 4);
+            const i16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)((__attribute__((address_space(3))) uint16_t *)&s_v[wave][0] + e));
+            const bf16x4_t bv = __builtin_bit_cast(bf16x4_t, t);
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                o[ht][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi[ht], bv, o[ht][nb], 0, 0, 0);
+                o[ht][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo[ht], bv, o[ht][nb], 0, 0, 0);
+            }
+        }
+    };
+
+    // Software pipeline over two register buffers (as in the VALU flavour).
+    LVec ka_[KB], va_[VLD], kb_[KB], vb_[VLD];
+    auto load = [&](LVec (&kt)[KB], LVec (&vt)[VLD], int tb) {
+        const uint32_t koff = (tb + lr) * ROWB + lg * 8 * ESZ;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) kt[kb] = buffer_load<LVec>(krs, koff + kb * 32 * ESZ, 0);
+        const uint32_t voff = (tb + vrow) * ROWB + vcol * ESZ;
+#pragma unroll
+        for (int u = 0; u < VLD; ++u) vt[u] = buffer_load<LVec>(vrs, voff + u * VRPI * ROWB, 0);
+    };
+    int base = r0 + wave * TR;
+    const int ntiles = base < r1 ? (r1 - base + STEP - 1) / STEP : 0;
+    if (ntiles > 0) load(ka_, va_, base);
+    for (int t = 0; t + 1 < ntiles; t += 2) {
+        load(kb_, vb_, base + STEP);
+        __builtin_amdgcn_sched_barrier(0);
+        process(ka_, va_, base);
+        load(ka_, va_, base + 2 * STEP);  // past the end this reads zeros and is not processed
+        __builtin_amdgcn_sched_barrier(0);
+        process(kb_, vb_, base + STEP);
+        base += 2 * STEP;
+    }
+    if (ntiles & 1) process(ka_, va_, base);
+
+    // The lane groups of a wave share each head's running max: their sums add directly.
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        lp[ht] += __shfl_xor(lp[ht], 16);
+        lp[ht] += __shfl_xor(lp[ht], 32);
+    }
+
+    // Merge the four waves pairwise through LDS: (0,2), (1,3), then (0,1).
+    __shared__ float s_mm[kWaves][HT * 16], s_ll[kWaves][HT * 16];
+    __shared__ __align__(16) float s_oo[2][HT * 16][D];
+    if (lg == 0) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) { s_mm[wave][ht * 16 + lr] = m[ht]; s_ll[wave][ht * 16 + lr] = lp[ht]; }
+    }
+    auto put_o = [&](int slot_) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s_oo[slot_][ht * 16 + 4 * lg + i][nb * 16 + lr] = o[ht][nb][i];
+    };
+    auto merge_o = [&](int slot_, int other) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int head = ht * 16 + 4 * lg + i;
+                const float ms = s_mm[wave][head], mo = s_mm[other][head];
+                const float M = fmaxf(ms, mo);
+                const float fs = __builtin_amdgcn_exp2f(ms - M), fo = __builtin_amdgcn_exp2f(mo - M);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    o[ht][nb][i] = fmaf(o[ht][nb][i], fs, s_oo[slot_][head][nb * 16 + lr] * fo);
+                const float Ls = fmaf(s_ll[wave][head], fs, s_ll[other][head] * fo);
+                if (lr == 0) { s_mm[wave][head] = M; s_ll[wave][head] = Ls; }
+            }
+    };
+    __syncthreads();
+    if (wave >= 2) put_o(wave - 2);
+    __syncthreads();
+    if (wave < 2) merge_o(wave, wave + 2);
+    __syncthreads();
+    if (wave == 1) put_o(0);
+    __syncthreads();
+    if (wave == 0) {
+        merge_o(0, 1);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int head = ht * 16 + 4 * lg + i;
+                if (head >= GT) continue;
+                const float M = s_mm[0][head], Ls = s_ll[0][head];
+                const size_t row = (size_t)b * h_q + h0 + head;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float v = o[ht][nb][i] * vscale;
+                    if (direct)
+                        a.out[row * D + nb * 16 + lr] = v / Ls;
+                    else
+                        a.part_o[(k * GT + head) * D + nb * 16 + lr] = v;
+                }
+                if (!direct && lr == 0) {
+                    a.part_ml[(k * GT + head) * 2 + 0] = M;
+                    a.part_ml[(k * GT + head) * 2 + 1] = Ls;
+                }
+            }
+    }
+    __syncthreads();  // the LDS arrays are reused by the next segment
+}
+
+// Workgroup w walks its share of the rows and calls seg(b, kvh, h0, r0, r1, k, whole) once per
+// unit it crosses: rows [r0, r1) of (sequence b, KV head kvh) for query heads h0 .. h0+gt-1,
+// partial slot k, whole = the segment is the entire unit.
+template <class SegFn>
+__device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn &&seg) {
     __shared__ int64_t s_pre[kMaxBatch + 1];
     __shared__ int64_t s_wave[kWaves];
     const Partition &pt = a.pt;
@@ -454,15 +719,15 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a
     }
     int b = lo;
     int L = a.lens[b];
-    int64_t off = pos - s_pre[b];
+    const int64_t off = pos - s_pre[b];
     int ul = (int)(off / L);     // unit within the sequence
     int row = (int)(off % L);
-    const int upb = a.pt.h_kv * pt.tiles, g = a.h_q / a.pt.h_kv;
+    const int upb = pt.h_kv * pt.tiles, g = a.h_q / pt.h_kv;
     while (pos < end) {
         const int r1 = (int)min<int64_t>((int64_t)L, row + (end - pos));
-        const int kvh = ul / pt.tiles, h0 = kvh * g + (ul % pt.tiles) * GT;
+        const int kvh = ul / pt.tiles, h0 = kvh * g + (ul % pt.tiles) * gt;
         const size_t u = (size_t)b * upb + ul;
-        attend_segment<KV, D, GT>(a, b, kvh, h0, row, r1, (size_t)w + u, DIRECT && row == 0 && r1 == L);
+        seg(b, kvh, h0, row, r1, (size_t)w + u, row == 0 && r1 == L);
         pos += r1 - row;
         row = 0;
         if (++ul == upb && pos < end) {
@@ -471,6 +736,24 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a
             L = a.lens[b];
         }
     }
+}
+
+// VALU flavour (any group size; GT in {1, 2, 4}). DIRECT (decode_attn_run): a unit covered by
+// a single workgroup is written to out directly and lse_combine_kernel skips it; otherwise
+// every segment leaves a partial result.
+template <int KV, int D, int GT, bool DIRECT>
+__global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a) {
+    walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole) {
+        attend_segment<KV, D, GT>(a, b, kvh, h0, r0, r1, k, DIRECT && whole);
+    });
+}
+
+// Matrix-core flavour (bf16 / fp8 caches, GT in {8, 16, 32}).
+template <int KV, int D, int GT, bool DIRECT>
+__global__ __launch_bounds__(kBlock) void split_kv_attn_mfma_kernel(const SplitArgs a) {
+    walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole) {
+        attend_segment_mfma<KV, D, GT>(a, b, kvh, h0, r0, r1, k, DIRECT && whole);
+    });
 }
 
 // One workgroup per (sequence, query head): merge the segments of the head's unit by their
@@ -595,10 +878,19 @@ int validate(const da_desc *d) {
 // starting on a 256-byte boundary (N workgroups, units = batch * h_kv * head tiles).
 struct Plan {
     int gt, tiles, nwg;
+    bool mfma;  // matrix-core flavour
     size_t ml_off, o_off, bytes;
 };
 
-int heads_per_block(int g) { return g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1; }
+// Flavour and query heads per workgroup: groups of 8 or more query heads over a bf16 / fp8
+// cache run on the matrix cores with 8, 16 or 32 heads per workgroup; everything else on the
+// vector ALUs with 4, 2 or 1.
+bool use_mfma(const da_desc *d) { return d->kv_dtype != DA_F32 && (d->h_q / d->h_kv) % 8 == 0; }
+int heads_per_block(const da_desc *d) {
+    const int g = d->h_q / d->h_kv;
+    if (use_mfma(d)) return g % 32 == 0 ? 32 : g % 16 == 0 ? 16 : 8;
+    return g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
+}
 
 constexpr int kMinRowsPerBlock = 256;  // below this a workgroup's share is mostly overhead
 constexpr int kFallbackResident = 512; // workgroups planned for when no device is visible
@@ -631,7 +923,16 @@ int resident_workgroups(const void *kernel) {
 }
 
 template <int KV, int D>
-const void *split_kernel_ptr(int gt) {
+const void *split_kernel_ptr(int gt, bool mfma) {
+    if constexpr (KV != DA_F32) {
+        if (mfma) {
+            switch (gt) {
+            case 32: return reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 32, false>);
+            case 16: return reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 16, false>);
+            default: return reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 8, false>);
+            }
+        }
+    }
     switch (gt) {
     case 4: return reinterpret_cast<const void *>(&split_kv_attn_kernel<KV, D, 4, false>);
     case 2: return reinterpret_cast<const void *>(&split_kv_attn_kernel<KV, D, 2, false>);
@@ -639,10 +940,10 @@ const void *split_kernel_ptr(int gt) {
     }
 }
 
-const void *split_kernel_ptr(int kv, int d, int gt) {
-    if (kv == DA_F32) return d == 64 ? split_kernel_ptr<DA_F32, 64>(gt) : split_kernel_ptr<DA_F32, 128>(gt);
-    if (kv == DA_BF16) return d == 64 ? split_kernel_ptr<DA_BF16, 64>(gt) : split_kernel_ptr<DA_BF16, 128>(gt);
-    return d == 64 ? split_kernel_ptr<DA_FP8_E4M3FN, 64>(gt) : split_kernel_ptr<DA_FP8_E4M3FN, 128>(gt);
+const void *split_kernel_ptr(int kv, int d, int gt, bool mfma) {
+    if (kv == DA_F32) return d == 64 ? split_kernel_ptr<DA_F32, 64>(gt, false) : split_kernel_ptr<DA_F32, 128>(gt, false);
+    if (kv == DA_BF16) return d == 64 ? split_kernel_ptr<DA_BF16, 64>(gt, mfma) : split_kernel_ptr<DA_BF16, 128>(gt, mfma);
+    return d == 64 ? split_kernel_ptr<DA_FP8_E4M3FN, 64>(gt, mfma) : split_kernel_ptr<DA_FP8_E4M3FN, 128>(gt, mfma);
 }
 
 int make_plan(const da_desc *d, int max_len, Plan *p) {
@@ -650,7 +951,8 @@ int make_plan(const da_desc *d, int max_len, Plan *p) {
     if (rc) return rc;
     if (max_len < 1 || max_len > d->cap)
         return fail(DA_ERR_INVALID_ARG, "max_len (%d) must be in [1, cap = %d]", max_len, d->cap);
-    p->gt = heads_per_block(d->h_q / d->h_kv);
+    p->mfma = use_mfma(d);
+    p->gt = heads_per_block(d);
     p->tiles = d->h_q / d->h_kv / p->gt;
     const int64_t units = (int64_t)d->batch * d->h_kv * p->tiles;
     const int64_t rows_max = units * max_len;  // rows of all units at max_len
@@ -658,7 +960,7 @@ int make_plan(const da_desc *d, int max_len, Plan *p) {
     if (d->block_rows) {
         nwg = (rows_max + d->block_rows - 1) / d->block_rows;
     } else {
-        nwg = resident_workgroups(split_kernel_ptr(d->kv_dtype, d->d_k, p->gt));
+        nwg = resident_workgroups(split_kernel_ptr(d->kv_dtype, d->d_k, p->gt, p->mfma));
         nwg = std::min<int64_t>(nwg, (rows_max + kMinRowsPerBlock - 1) / kMinRowsPerBlock);
     }
     p->nwg = (int)std::max<int64_t>(1, std::min<int64_t>(nwg, 1 << 20));
@@ -685,8 +987,27 @@ void launch_split_gt(int gt, dim3 grid, hipStream_t st, const SplitArgs &args) {
     }
 }
 
+template <int KV, int D, bool DIRECT>
+void launch_split_mfma_gt(int gt, dim3 grid, hipStream_t st, const SplitArgs &args) {
+    switch (gt) {
+    case 32: hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 32, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
+    case 16: hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 16, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
+    default: hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 8, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
+    }
+}
+
 template <bool DIRECT>
-void launch_split(int kv, int d, int gt, dim3 grid, hipStream_t st, const SplitArgs &args) {
+void launch_split(int kv, int d, int gt, bool mfma, dim3 grid, hipStream_t st, const SplitArgs &args) {
+    if (mfma) {
+        if (kv == DA_BF16) {
+            if (d == 64) launch_split_mfma_gt<DA_BF16, 64, DIRECT>(gt, grid, st, args);
+            else launch_split_mfma_gt<DA_BF16, 128, DIRECT>(gt, grid, st, args);
+        } else {
+            if (d == 64) launch_split_mfma_gt<DA_FP8_E4M3FN, 64, DIRECT>(gt, grid, st, args);
+            else launch_split_mfma_gt<DA_FP8_E4M3FN, 128, DIRECT>(gt, grid, st, args);
+        }
+        return;
+    }
     if (kv == DA_F32) {
         if (d == 64) launch_split_gt<DA_F32, 64, DIRECT>(gt, grid, st, args);
         else launch_split_gt<DA_F32, 128, DIRECT>(gt, grid, st, args);
@@ -743,9 +1064,9 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     args.qk_scale = desc->scale * kLog2e;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (out)
-        launch_split<true>(desc->kv_dtype, desc->d_k, p.gt, dim3(p.nwg), st, args);
+        launch_split<true>(desc->kv_dtype, desc->d_k, p.gt, p.mfma, dim3(p.nwg), st, args);
     else
-        launch_split<false>(desc->kv_dtype, desc->d_k, p.gt, dim3(p.nwg), st, args);
+        launch_split<false>(desc->kv_dtype, desc->d_k, p.gt, p.mfma, dim3(p.nwg), st, args);
     return launch_status("split_kv_attn_kernel");
 }
 
