@@ -98,8 +98,16 @@ constexpr int kLoadNonTemporal = 2;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// The base and size are the same in every lane of the wave; taking them through readfirstlane
+// keeps the resource in scalar registers even where the compiler cannot prove that (a
+// per-lane resource would wrap every buffer load in a loop over distinct values).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    // readfirstlane yields an int: keep each half 32 bits wide (no sign extension)
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
 }
 
 template <typename Vec>
@@ -441,6 +449,12 @@ typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+// s_waitcnt immediate (gfx9 layout) that waits until at most n vector-memory operations of
+// this wave are outstanding, without waiting on the LDS / export counters.
+constexpr int vmcnt_only(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
 // Two e4m3fn codes (bytes 2*HI, 2*HI+1 of w) -> two bf16 packed in a word; exact, since every
 // e4m3fn value is a bf16 value.
 template <bool HI>
@@ -461,87 +475,61 @@ __device__ __forceinline__ uint4 to_bf16x8(const typename std::conditional<KV ==
     }
 }
 
-// Steps I-III over rows [r0, r1) of (b, kvh) for query heads h0 .. h0+GT-1 on the matrix cores.
+// Steps I-III on the matrix cores for query heads h0 .. h0+GT-1 of one (sequence, KV head).
 // Per 16-row tile and wave:
 //   * Step I as S = K_tile . Q^T with v_mfma_f32_16x16x32_bf16: the K rows are the A operand
-//     exactly as stored (lane l loads row l%16, elements 8*(l/16) .. of each 32-wide block),
-//     q of 16 heads is the B operand. The result gives lane l the scores of rows
-//     4*(l/16)+i (i < 4) for head l%16.
+//     as stored (lane l holds row l%16, elements 8*(l/16) .. of each 32-wide block), q of 16
+//     heads is the B operand. The result gives lane l the scores of rows 4*(l/16)+i (i < 4)
+//     for head l%16.
 //   * Step II online on that layout: the tile max per head reduces over the 4 lane groups;
 //     O is rescaled (through a 16-float LDS transpose) only when some head's max grew.
 //   * Step III as O += P . V_tile with v_mfma_f32_16x16x16_bf16: the score layout above is
-//     exactly the A-operand layout of P. V is staged row-major in LDS (as bf16) and read back
-//     as the B operand with ds_read_b64_tr_b16. P is split into bf16 hi + lo parts (two
-//     MFMAs) so that P.V keeps ~16 bits of P's precision.
+//     exactly the A-operand layout of P; V, staged in LDS as bf16, is read back as the B
+//     operand with ds_read_b64_tr_b16. P is split into bf16 hi + lo parts (two MFMAs) so that
+//     P.V keeps ~16 bits of P's precision.
 // GT = 8, 16 or 32 heads (HT = 1 or 2 MFMA tiles of 16; heads past GT are zero padding).
-template <int KV, int D, int GT>
-__device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
-                                                    size_t k, bool direct) {
-    static_assert(KV == DA_BF16 || KV == DA_FP8_E4M3FN, "MFMA flavour takes bf16 or fp8 caches");
-    using LVec = typename std::conditional<KV == DA_BF16, uint4, uint2>::type;  // 8 elements
-    constexpr int HT = (GT + 15) / 16;
-    constexpr int KB = D / 32;           // 32-wide k blocks of Step I
-    constexpr int NB = D / 16;           // 16-wide d blocks of Step III
-    constexpr int ESZ = Kv<KV>::kEsz;
-    constexpr uint32_t ROWB = D * ESZ;   // bytes per cache row
-    constexpr int TR = 16;               // rows per wave tile
-    constexpr int STEP = TR * kWaves;    // rows per workgroup iteration
-    constexpr int VROW = D + 8;          // staged V row, bf16 elements (16-byte pad)
-    constexpr int VL = D / 8;            // lanes per row of a V load
-    constexpr int VRPI = kWave / VL;     // V rows per load instruction
-    constexpr int VLD = TR / VRPI;       // V loads per tile
-    const int h_q = a.h_q;
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int lr = lane % 16, lg = lane / 16;
-    const int vrow = lane / VL, vcol = (lane % VL) * 8;
+template <int D, int GT>
+struct MfmaAttn {
+    static constexpr int HT = (GT + 15) / 16;
+    static constexpr int KB = D / 32;  // 32-wide k blocks of Step I
+    static constexpr int NB = D / 16;  // 16-wide d blocks of Step III
+    typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
-    const size_t slot = (size_t)b * a.pt.h_kv + kvh;
-    const size_t slot_bytes = (size_t)a.cap * ROWB;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const char *>(a.kc) + slot * slot_bytes, r1 * ROWB);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const char *>(a.vc) + slot * slot_bytes, r1 * ROWB);
-    float vscale = 1.f, sc = a.qk_scale;
-    if constexpr (KV == DA_FP8_E4M3FN) {
-        sc *= a.kv_scales[slot * 2 + 0];
-        vscale = a.kv_scales[slot * 2 + 1];
-    }
+    bf16x8_t qb[HT][KB];
+    float m[HT], lp[HT];
+    f32x4_t o[HT][NB];
+    float sc;
+    int lane, lr, lg, wave;
 
     // q^T as the B operand of Step I: lane l holds q[head ht*16 + l%16][kb*32 + 8*(l/16) ..+8].
-    bf16x8_t qb[HT][KB];
+    __device__ __forceinline__ void init(const SplitArgs &a, int b, int h0, float score_scale) {
+        lane = threadIdx.x % kWave;
+        wave = threadIdx.x / kWave;
+        lr = lane % 16;
+        lg = lane / 16;
+        sc = score_scale;
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const int head = ht * 16 + lr;
+        for (int ht = 0; ht < HT; ++ht) {
+            const int head = ht * 16 + lr;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            uint4 x = {0u, 0u, 0u, 0u};
-            if (head < GT)
-                x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) +
-                                                      ((size_t)b * h_q + h0 + head) * D + kb * 32 + 8 * lg);
-            qb[ht][kb] = __builtin_bit_cast(bf16x8_t, x);
+            for (int kb = 0; kb < KB; ++kb) {
+                uint4 x = {0u, 0u, 0u, 0u};
+                if (head < GT)
+                    x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) +
+                                                          ((size_t)b * a.h_q + h0 + head) * D + kb * 32 + 8 * lg);
+                qb[ht][kb] = __builtin_bit_cast(bf16x8_t, x);
+            }
+            m[ht] = kNegBig;
+            lp[ht] = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) o[ht][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
 
-    float m[HT], lp[HT];
-    f32x4_t o[HT][NB];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        m[ht] = kNegBig;
-        lp[ht] = 0.f;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[ht][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-
-    __shared__ __align__(16) uint16_t s_v[kWaves][TR * VROW];
-    __shared__ __align__(16) float s_c[kWaves][HT * 16];
-
-    auto process = [&](const LVec (&kt)[KB], const LVec (&vt)[VLD], int tb) {
-        // stage this tile's V rows (as bf16) in the wave's LDS tile
-#pragma unroll
-        for (int u = 0; u < VLD; ++u)
-            *reinterpret_cast<uint4 *>(&s_v[wave][(vrow + u * VRPI) * VROW + vcol]) = to_bf16x8<KV>(vt[u]);
-        // Step I
-        bf16x8_t ka[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) ka[kb] = __builtin_bit_cast(bf16x8_t, to_bf16x8<KV>(kt[kb]));
+    // One tile of rows tb .. tb+15 (rows at or past r1 masked): ka = the K rows as A operands;
+    // vaddr(nb) = this lane's LDS address for the transpose read of d block nb.
+    template <class VAddr>
+    __device__ __forceinline__ void tile(const bf16x8_t (&ka)[KB], VAddr &&vaddr, int tb, int r1, float *s_c) {
         bool grew = false;
         float corr[HT];
         bf16x4_t phi[HT], plo[HT];
@@ -550,7 +538,6 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
             f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qb[ht][kb], sacc, 0, 0, 0);
-            // Step II (online): rows tb + 4*lg + i, head ht*16 + lr
             float x[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * lg + i < r1) ? sacc[i] * sc : -INFINITY;
@@ -575,24 +562,20 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
             // corr is held per head = l%16; O rows are heads 4*(l/16)+i: transpose via LDS
             if (lg == 0) {
 #pragma unroll
-                for (int ht = 0; ht < HT; ++ht) s_c[wave][ht * 16 + lr] = corr[ht];
+                for (int ht = 0; ht < HT; ++ht) s_c[ht * 16 + lr] = corr[ht];
             }
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
-                const float4 c4 = *reinterpret_cast<const float4 *>(&s_c[wave][ht * 16 + 4 * lg]);
+                const float4 c4 = *reinterpret_cast<const float4 *>(&s_c[ht * 16 + 4 * lg]);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     o[ht][nb][0] *= c4.x; o[ht][nb][1] *= c4.y; o[ht][nb][2] *= c4.z; o[ht][nb][3] *= c4.w;
                 }
             }
         }
-        // Step III
-        typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int e = (4 * lg + lr / 4) * VROW + nb * 16 + 4 * (lane % 4);
-            const i16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4 *)((__attribute__((address_space(3))) uint16_t *)&s_v[wave][0] + e));
+            const i16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)vaddr(nb));
             const bf16x4_t bv = __builtin_bit_cast(bf16x4_t, t);
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
@@ -600,10 +583,137 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
                 o[ht][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo[ht], bv, o[ht][nb], 0, 0, 0);
             }
         }
-    };
+    }
 
-    // Software pipeline over two register buffers (as in the VALU flavour).
-    LVec ka_[KB], va_[VLD], kb_[KB], vb_[VLD];
+    // Merge the four waves pairwise through LDS ((0,2), (1,3), then (0,1)) and write the
+    // segment's result: s_oo holds 2 * HT*16 * D floats, s_mm / s_ll kWaves * HT*16 each.
+    __device__ __forceinline__ void finish(const SplitArgs &a, int b, int h0, size_t k, bool direct, float vscale,
+                                           float *s_oo, float *s_mm, float *s_ll) {
+        constexpr int HP = HT * 16;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {  // the lane groups share each head's max: sums add
+            lp[ht] += __shfl_xor(lp[ht], 16);
+            lp[ht] += __shfl_xor(lp[ht], 32);
+        }
+        __syncthreads();  // every wave is done with the LDS the merge reuses
+        if (lg == 0) {
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) { s_mm[wave * HP + ht * 16 + lr] = m[ht]; s_ll[wave * HP + ht * 16 + lr] = lp[ht]; }
+        }
+        auto put_o = [&](int slot) {
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s_oo[(slot * HP + ht * 16 + 4 * lg + i) * D + nb * 16 + lr] = o[ht][nb][i];
+        };
+        auto merge_o = [&](int slot, int other) {
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int head = ht * 16 + 4 * lg + i;
+                    const float ms = s_mm[wave * HP + head], mo = s_mm[other * HP + head];
+                    const float M = fmaxf(ms, mo);
+                    const float fs = __builtin_amdgcn_exp2f(ms - M), fo = __builtin_amdgcn_exp2f(mo - M);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        o[ht][nb][i] = fmaf(o[ht][nb][i], fs, s_oo[(slot * HP + head) * D + nb * 16 + lr] * fo);
+                    const float Ls = fmaf(s_ll[wave * HP + head], fs, s_ll[other * HP + head] * fo);
+                    if (lr == 0) { s_mm[wave * HP + head] = M; s_ll[wave * HP + head] = Ls; }
+                }
+        };
+        __syncthreads();
+        if (wave >= 2) put_o(wave - 2);
+        __syncthreads();
+        if (wave < 2) merge_o(wave, wave + 2);
+        __syncthreads();
+        if (wave == 1) put_o(0);
+        __syncthreads();
+        if (wave == 0) {
+            merge_o(0, 1);
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int head = ht * 16 + 4 * lg + i;
+                    if (head >= GT) continue;
+                    const float M = s_mm[head], Ls = s_ll[head];
+                    const size_t row = (size_t)b * a.h_q + h0 + head;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const float v = o[ht][nb][i] * vscale;
+                        if (direct)
+                            a.out[row * D + nb * 16 + lr] = v / Ls;
+                        else
+                            a.part_o[(k * GT + head) * D + nb * 16 + lr] = v;
+                    }
+                    if (!direct && lr == 0) {
+                        a.part_ml[(k * GT + head) * 2 + 0] = M;
+                        a.part_ml[(k * GT + head) * 2 + 1] = Ls;
+                    }
+                }
+        }
+        __syncthreads();  // the LDS arrays are reused by the next segment
+    }
+};
+
+// Matrix-core segment with the tiles staged through registers (bf16 or fp8 caches): K rows
+// are loaded straight into A-operand order and V rows are widened to bf16 and stored
+// row-major in the wave's LDS tile for the transpose read.
+template <int KV, int D, int GT, int NBUF>
+__device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
+                                                    size_t k, bool direct) {
+    static_assert(KV == DA_BF16 || KV == DA_FP8_E4M3FN, "MFMA flavour takes bf16 or fp8 caches");
+    using LVec = typename std::conditional<KV == DA_BF16, uint4, uint2>::type;  // 8 elements
+    using A = MfmaAttn<D, GT>;
+    constexpr int KB = A::KB, HP = A::HT * 16;
+    constexpr int ESZ = Kv<KV>::kEsz;
+    constexpr uint32_t ROWB = D * ESZ;   // bytes per cache row
+    constexpr int TR = 16;               // rows per wave tile
+    constexpr int STEP = TR * kWaves;    // rows per workgroup iteration
+    constexpr int VROW = D + 8;          // staged V row, bf16 elements (16-byte pad)
+    constexpr int VL = D / 8;            // lanes per row of a V load
+    constexpr int VRPI = kWave / VL;     // V rows per load instruction
+    constexpr int VLD = TR / VRPI;       // V loads per tile
+
+    const size_t slot = (size_t)b * a.pt.h_kv + kvh;
+    const size_t slot_bytes = (size_t)a.cap * ROWB;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const char *>(a.kc) + slot * slot_bytes, r1 * ROWB);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const char *>(a.vc) + slot * slot_bytes, r1 * ROWB);
+    float vscale = 1.f, sc = a.qk_scale;
+    if constexpr (KV == DA_FP8_E4M3FN) {
+        sc *= a.kv_scales[slot * 2 + 0];
+        vscale = a.kv_scales[slot * 2 + 1];
+    }
+    A at;
+    at.init(a, b, h0, sc);
+    const int lane = at.lane, wave = at.wave, lr = at.lr, lg = at.lg;
+    const int vrow = lane / VL, vcol = (lane % VL) * 8;
+
+    __shared__ __align__(16) uint16_t s_v[kWaves][TR * VROW];
+    __shared__ __align__(16) float s_c[kWaves][HP];
+    __shared__ __align__(16) float s_oo[2 * HP * D];
+    __shared__ float s_mm[kWaves * HP], s_ll[kWaves * HP];
+
+    auto process = [&](const LVec (&kt)[KB], const LVec (&vt)[VLD], int tb) {
+#pragma unroll
+        for (int u = 0; u < VLD; ++u)
+            *reinterpret_cast<uint4 *>(&s_v[wave][(vrow + u * VRPI) * VROW + vcol]) = to_bf16x8<KV>(vt[u]);
+        bf16x8_t ka[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) ka[kb] = __builtin_bit_cast(bf16x8_t, to_bf16x8<KV>(kt[kb]));
+        at.tile(ka, [&](int nb) {
+            return (__attribute__((address_space(3))) uint16_t *)&s_v[wave][0] +
+                   (4 * lg + lr / 4) * VROW + nb * 16 + 4 * (lane % 4);
+        }, tb, r1, &s_c[wave][0]);
+    };
+    // Software pipeline over a ring of NBUF register buffers: NBUF - 1 tiles of this wave are
+    // in flight while one is computed. The ring is unrolled so every buffer index is static;
+    // tiles past the segment's end read zeros and are fully masked (p = 0), so every load is
+    // consumed on every path (a load used on one path only would be sunk to its use).
+    LVec kr[NBUF][KB], vr[NBUF][VLD];
     auto load = [&](LVec (&kt)[KB], LVec (&vt)[VLD], int tb) {
         const uint32_t koff = (tb + lr) * ROWB + lg * 8 * ESZ;
 #pragma unroll
@@ -612,88 +722,294 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
 #pragma unroll
         for (int u = 0; u < VLD; ++u) vt[u] = buffer_load<LVec>(vrs, voff + u * VRPI * ROWB, 0);
     };
-    int base = r0 + wave * TR;
+    const int base = r0 + wave * TR;
     const int ntiles = base < r1 ? (r1 - base + STEP - 1) / STEP : 0;
-    if (ntiles > 0) load(ka_, va_, base);
-    for (int t = 0; t + 1 < ntiles; t += 2) {
-        load(kb_, vb_, base + STEP);
-        __builtin_amdgcn_sched_barrier(0);
-        process(ka_, va_, base);
-        load(ka_, va_, base + 2 * STEP);  // past the end this reads zeros and is not processed
-        __builtin_amdgcn_sched_barrier(0);
-        process(kb_, vb_, base + STEP);
-        base += 2 * STEP;
-    }
-    if (ntiles & 1) process(ka_, va_, base);
-
-    // The lane groups of a wave share each head's running max: their sums add directly.
+    if (ntiles > 0) {
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        lp[ht] += __shfl_xor(lp[ht], 16);
-        lp[ht] += __shfl_xor(lp[ht], 32);
-    }
-
-    // Merge the four waves pairwise through LDS: (0,2), (1,3), then (0,1).
-    __shared__ float s_mm[kWaves][HT * 16], s_ll[kWaves][HT * 16];
-    __shared__ __align__(16) float s_oo[2][HT * 16][D];
-    if (lg == 0) {
+        for (int j = 0; j + 1 < NBUF; ++j) load(kr[j], vr[j], base + j * STEP);
+        for (int t = 0; t < ntiles; t += NBUF) {
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) { s_mm[wave][ht * 16 + lr] = m[ht]; s_ll[wave][ht * 16 + lr] = lp[ht]; }
+            for (int j = 0; j < NBUF; ++j) {
+                load(kr[(j + NBUF - 1) % NBUF], vr[(j + NBUF - 1) % NBUF], base + (t + j + NBUF - 1) * STEP);
+                __builtin_amdgcn_sched_barrier(0);
+                process(kr[j], vr[j], base + (t + j) * STEP);
+            }
+        }
     }
+    at.finish(a, b, h0, k, direct, vscale, s_oo, s_mm, s_ll);
+}
+
+// Matrix-core segment with workgroup-wide LDS stages filled by DMA (buffer_load ... lds), so
+// that no registers hold K or V in flight and 64 KiB per CU are outstanding.
+//   * A stage holds RS rows of K and V (16 KiB each: 64 bf16 or 128 fp8 rows of d = 128),
+//     every 16-row tile chunk-major: 16-byte chunk c of row r at byte (c*16 + r)*16. One DMA
+//     instruction fills 1 KiB in lane order (lane i: chunk 4q + i/16, row i%16), so the K
+//     A operand of k block kb is one contiguous KiB and the V transpose reads of a d block a
+//     contiguous 512 bytes: neither read has bank conflicts. Two stages alternate (separate
+//     arrays); all 256 threads fill each, and barriers mark a stage filled / consumed.
+//   * Each wave owns one 16-head tile (its own q operand, running max, sums and O) and a
+//     share of the stage's P.V blocks: 16-row blocks for bf16 (Step III by
+//     v_mfma_f32_16x16x16_bf16, V read by ds_read_b64_tr_b16), 32-row blocks for fp8 (Step III
+//     by v_mfma_f32_16x16x32_bf16 with P's 8 rows per lane taken from the block's two score
+//     tiles, V read as fp8 by ds_read_b64_tr_b8 and widened in registers). Step I always
+//     uses v_mfma_f32_16x16x32_bf16 (fp8 K widened to bf16 after its LDS read).
+//   * At the end the waves holding the same head tile merge through LDS.
+template <int KV, int D, int GT>
+__device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
+                                                      size_t k, bool direct) {
+    static_assert(KV == DA_BF16 || KV == DA_FP8_E4M3FN, "matrix-core flavour takes bf16 or fp8 caches");
+    constexpr int HT = (GT + 15) / 16;
+    constexpr int KB = D / 32, NB = D / 16;
+    constexpr int ESZ = Kv<KV>::kEsz;
+    constexpr uint32_t ROWB = D * ESZ;         // bytes per cache row
+    constexpr int TILE = 16 * ROWB;            // K (or V) bytes of a 16-row tile
+    constexpr int HALF = 16384;                // K (or V) bytes per stage
+    constexpr int RS = HALF / ROWB;            // rows per stage
+    constexpr int PVR = KV == DA_BF16 ? 16 : 32;  // rows per P.V block
+    constexpr int NBLK = RS / PVR;             // P.V blocks per stage
+    constexpr int WPH = kWaves / HT;           // waves per head tile
+    constexpr int IPW = NBLK / WPH;            // blocks per wave per stage
+    constexpr int DPW = HALF / 1024 / kWaves;  // K (and V) DMA instructions per wave per stage
+    constexpr int VM_STAGE = 2 * DPW;          // DMA ops of one stage per wave
+    static_assert(NBLK % WPH == 0 && (HALF / 1024) % kWaves == 0, "stage split");
+    const int h_q = a.h_q;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int lr = lane % 16, lg = lane / 16;
+    const int ht = wave % HT;  // this wave's head tile
+    const int wb = wave / HT;  // this wave's first P.V block in a stage
+
+    __shared__ __align__(16) char s_a[2 * HALF];
+    __shared__ __align__(16) char s_b[2 * HALF];
+    __shared__ __align__(16) float s_c[kWaves][16];
+    __shared__ float s_mm[kWaves][16], s_ll[kWaves][16];
+    typedef __attribute__((address_space(3))) void lds_void;
+    typedef __attribute__((address_space(3))) char lds_char;
+
+    const size_t slot = (size_t)b * a.pt.h_kv + kvh;
+    const size_t slot_bytes = (size_t)a.cap * ROWB;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const char *>(a.kc) + slot * slot_bytes, r1 * ROWB);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const char *>(a.vc) + slot * slot_bytes, r1 * ROWB);
+    float vscale = 1.f, sc = a.qk_scale;
+    if constexpr (KV == DA_FP8_E4M3FN) {
+        sc *= a.kv_scales[slot * 2 + 0];
+        vscale = a.kv_scales[slot * 2 + 1];
+    }
+    // q^T of this wave's 16 heads as the B operand of Step I (zero past GT)
+    bf16x8_t qb[KB];
+    {
+        const int head = ht * 16 + lr;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            uint4 x = {0u, 0u, 0u, 0u};
+            if (head < GT)
+                x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) +
+                                                      ((size_t)b * h_q + h0 + head) * D + kb * 32 + 8 * lg);
+            qb[kb] = __builtin_bit_cast(bf16x8_t, x);
+        }
+    }
+    float m = kNegBig, lp = 0.f;
+    f32x4_t o[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Rows at or past r1 are never fetched, so their stage bytes must be finite: the stages
+    // start zeroed (they may hold the previous segment's merge data otherwise).
+    for (int i = threadIdx.x; i < 2 * HALF / 16; i += kBlock) {
+        reinterpret_cast<uint4 *>(s_a)[i] = uint4{0u, 0u, 0u, 0u};
+        reinterpret_cast<uint4 *>(s_b)[i] = uint4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+
+    auto issue = [&](char *st, int sb) {
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) {
+            const int x = wave * DPW + j;  // DMA slot of the stage: tile x / (TILE/1024), part x % ...
+            const int t = x / (TILE / 1024), qq = x % (TILE / 1024);
+            const uint32_t off = (sb + 16 * t + lr) * ROWB + (4 * qq + lg) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(st + t * TILE + qq * 1024), 16, off, 0, 0,
+                                                     kLoadNonTemporal);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(st + HALF + t * TILE + qq * 1024), 16, off, 0,
+                                                     0, kLoadNonTemporal);
+        }
+    };
+
+    // Online softmax over NR rows held 4 per 16-row score tile: x[] are the scaled, masked
+    // scores; returns P split into bf16 hi / lo in the lane's row order and rescales O.
+    auto softmax = [&](float *x, auto &phi, auto &plo, int nr) {
+        float tmax = x[0];
+        for (int i = 1; i < nr; ++i) tmax = fmaxf(tmax, x[i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mn = fmaxf(m, tmax);
+        const float corr = __builtin_amdgcn_exp2f(m - mn);
+        const bool grew = mn > m;
+        m = mn;
+        float ps = 0.f;
+        for (int i = 0; i < nr; ++i) {
+            const float p = __builtin_amdgcn_exp2f(x[i] - mn);
+            ps += p;
+            phi[i] = (__bf16)p;
+            plo[i] = (__bf16)(p - (float)phi[i]);
+        }
+        lp = fmaf(lp, corr, ps);
+        if (__builtin_amdgcn_ballot_w64(grew)) {
+            // corr is held per head = l%16; O rows are heads 4*(l/16)+i: transpose via LDS
+            if (lg == 0) s_c[wave][lr] = corr;
+            const float4 c4 = *reinterpret_cast<const float4 *>(&s_c[wave][4 * lg]);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                o[nb][0] *= c4.x; o[nb][1] *= c4.y; o[nb][2] *= c4.z; o[nb][3] *= c4.w;
+            }
+        }
+    };
+
+    // Step I for the 16-row tile at byte `kt` of the stage's K half: lane l gets the scores of
+    // rows 4*(l/16)+i for head l%16.
+    auto scores = [&](const char *kt) {
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            uint4 raw;
+            if constexpr (KV == DA_BF16) {
+                raw = *reinterpret_cast<const uint4 *>(kt + kb * 1024 + lane * 16);
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2 *>(kt + ((kb * 2 + lg / 2) * 16 + lr) * 16 + 8 * (lg % 2));
+                raw = to_bf16x8<KV>(v);
+            }
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, raw), qb[kb], sacc, 0, 0, 0);
+        }
+        return sacc;
+    };
+
+    auto process = [&](const char *st, int sb) {
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+            const int blk = wb + j * WPH;  // P.V block of the stage
+            const int rb = sb + blk * PVR; // its first cache row
+            if constexpr (KV == DA_BF16) {
+                const f32x4_t sacc = scores(st + blk * TILE);
+                float x[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = (rb + 4 * lg + i < r1) ? sacc[i] * sc : -INFINITY;
+                bf16x4_t phi, plo;
+                softmax(x, phi, plo, 4);
+                const char *vt = st + HALF + blk * TILE;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int r = 4 * lg + lr / 4, d0 = nb * 16 + 4 * (lane % 4);
+                    const i16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t *)(lds_char *)(vt + ((d0 / 8) * 16 + r) * 16 + (d0 % 8) * 2));
+                    const bf16x4_t bv = __builtin_bit_cast(bf16x4_t, t);
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, o[nb], 0, 0, 0);
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, o[nb], 0, 0, 0);
+                }
+            } else {
+                // rows of lane group g: 4g+e (tile 0) and 16+4g+e (tile 1), e < 4
+                const f32x4_t s0 = scores(st + (2 * blk) * TILE);
+                const f32x4_t s1 = scores(st + (2 * blk + 1) * TILE);
+                float x[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[i] = (rb + 4 * lg + i < r1) ? s0[i] * sc : -INFINITY;
+                    x[4 + i] = (rb + 16 + 4 * lg + i < r1) ? s1[i] * sc : -INFINITY;
+                }
+                bf16x8_t phi, plo;
+                softmax(x, phi, plo, 8);
+                // V rows in the same order: lane s of group g reads row(g, s/2), bytes
+                // 16*nb + 8*(s%2) .. +8; the transpose read hands lane l the 8 rows of column l%16.
+                const int e = lr / 2;
+                const int rr = e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4;
+                const char *vt = st + HALF + (2 * blk + rr / 16) * TILE + (rr % 16) * 16 + 8 * (lr % 2);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) i32x2_t *)(lds_char *)(vt + nb * 256));
+                    const uint4 w = to_bf16x8<KV>(uint2{(uint32_t)t[0], (uint32_t)t[1]});
+                    const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, w);
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, bv, o[nb], 0, 0, 0);
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, bv, o[nb], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // Stages alternate between s_a and s_b; before reading a stage each wave waits for its own
+    // DMA into it (the other stage's may stay outstanding), then a barrier covers the others.
+    const int nst = (r1 - r0 + RS - 1) / RS;
+    issue(s_a, r0);
+    issue(s_b, r0 + RS);
+    for (int st = 0; st < nst; st += 2) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(VM_STAGE));
+        __syncthreads();
+        process(s_a, r0 + st * RS);
+        __syncthreads();
+        issue(s_a, r0 + (st + 2) * RS);  // past the end this fetches nothing
+        if (st + 1 < nst) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(VM_STAGE));
+            __syncthreads();
+            process(s_b, r0 + (st + 1) * RS);
+            __syncthreads();
+            issue(s_b, r0 + (st + 3) * RS);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // no DMA into the stages is outstanding past this point
+
+    // Merge: lane groups share each head's max (sums add); then waves holding the same head
+    // tile merge through LDS and one wave per head tile writes.
+    lp += __shfl_xor(lp, 16);
+    lp += __shfl_xor(lp, 32);
+    __syncthreads();
+    float *s_oo = reinterpret_cast<float *>(s_a);  // [2][16][D] floats, reusing stage a
+    if (lg == 0) { s_mm[wave][lr] = m; s_ll[wave][lr] = lp; }
     auto put_o = [&](int slot_) {
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s_oo[slot_][ht * 16 + 4 * lg + i][nb * 16 + lr] = o[ht][nb][i];
+            for (int i = 0; i < 4; ++i) s_oo[(slot_ * 16 + 4 * lg + i) * D + nb * 16 + lr] = o[nb][i];
     };
     auto merge_o = [&](int slot_, int other) {
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
+        for (int i = 0; i < 4; ++i) {
+            const int hd = 4 * lg + i;
+            const float ms = s_mm[wave][hd], mo = s_mm[other][hd];
+            const float M = fmaxf(ms, mo);
+            const float fs = __builtin_amdgcn_exp2f(ms - M), fo = __builtin_amdgcn_exp2f(mo - M);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int head = ht * 16 + 4 * lg + i;
-                const float ms = s_mm[wave][head], mo = s_mm[other][head];
-                const float M = fmaxf(ms, mo);
-                const float fs = __builtin_amdgcn_exp2f(ms - M), fo = __builtin_amdgcn_exp2f(mo - M);
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    o[ht][nb][i] = fmaf(o[ht][nb][i], fs, s_oo[slot_][head][nb * 16 + lr] * fo);
-                const float Ls = fmaf(s_ll[wave][head], fs, s_ll[other][head] * fo);
-                if (lr == 0) { s_mm[wave][head] = M; s_ll[wave][head] = Ls; }
-            }
+            for (int nb = 0; nb < NB; ++nb) o[nb][i] = fmaf(o[nb][i], fs, s_oo[(slot_ * 16 + hd) * D + nb * 16 + lr] * fo);
+            const float Ls = fmaf(s_ll[wave][hd], fs, s_ll[other][hd] * fo);
+            if (lr == 0) { s_mm[wave][hd] = M; s_ll[wave][hd] = Ls; }
+        }
     };
     __syncthreads();
     if (wave >= 2) put_o(wave - 2);
     __syncthreads();
     if (wave < 2) merge_o(wave, wave + 2);
-    __syncthreads();
-    if (wave == 1) put_o(0);
-    __syncthreads();
-    if (wave == 0) {
-        merge_o(0, 1);
+    if constexpr (HT == 1) {
+        __syncthreads();
+        if (wave == 1) put_o(0);
+        __syncthreads();
+        if (wave == 0) merge_o(0, 1);
+    }
+    if (wave < HT) {  // wave ht now holds head tile ht
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
+        for (int i = 0; i < 4; ++i) {
+            const int hd = ht * 16 + 4 * lg + i;
+            if (hd >= GT) continue;
+            const float M = s_mm[wave][4 * lg + i], Ls = s_ll[wave][4 * lg + i];
+            const size_t row = (size_t)b * h_q + h0 + hd;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int head = ht * 16 + 4 * lg + i;
-                if (head >= GT) continue;
-                const float M = s_mm[0][head], Ls = s_ll[0][head];
-                const size_t row = (size_t)b * h_q + h0 + head;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const float v = o[ht][nb][i] * vscale;
-                    if (direct)
-                        a.out[row * D + nb * 16 + lr] = v / Ls;
-                    else
-                        a.part_o[(k * GT + head) * D + nb * 16 + lr] = v;
-                }
-                if (!direct && lr == 0) {
-                    a.part_ml[(k * GT + head) * 2 + 0] = M;
-                    a.part_ml[(k * GT + head) * 2 + 1] = Ls;
-                }
+            for (int nb = 0; nb < NB; ++nb) {
+                const float v = o[nb][i] * vscale;
+                if (direct)
+                    a.out[row * D + nb * 16 + lr] = v / Ls;
+                else
+                    a.part_o[(k * GT + hd) * D + nb * 16 + lr] = v;
             }
+            if (!direct && lr == 0) {
+                a.part_ml[(k * GT + hd) * 2 + 0] = M;
+                a.part_ml[(k * GT + hd) * 2 + 1] = Ls;
+            }
+        }
     }
     __syncthreads();  // the LDS arrays are reused by the next segment
 }
@@ -701,13 +1017,22 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
 // Workgroup w walks its share of the rows and calls seg(b, kvh, h0, r0, r1, k, whole) once per
 // unit it crosses: rows [r0, r1) of (sequence b, KV head kvh) for query heads h0 .. h0+gt-1,
 // partial slot k, whole = the segment is the entire unit.
+// Values read from LDS are per-lane to the compiler; the segment bounds are the same in every
+// lane, and reading them through readfirstlane keeps them (and the buffer resources built from
+// them) in scalar registers: a per-lane resource would wrap every buffer load in a loop.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 template <class SegFn>
 __device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn &&seg) {
     __shared__ int64_t s_pre[kMaxBatch + 1];
     __shared__ int64_t s_wave[kWaves];
     const Partition &pt = a.pt;
     sequence_prefix(a.lens, pt, s_pre, s_wave);
-    const int64_t Tot = s_pre[pt.batch], N = pt.nwg, w = blockIdx.x;
+    const int64_t Tot = uniform64(s_pre[pt.batch]), N = pt.nwg, w = blockIdx.x;
     int64_t pos = wg_start(w, Tot, N);
     const int64_t end = wg_start(w + 1, Tot, N);
     if (pos >= end) return;
@@ -715,11 +1040,11 @@ __device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn 
     int lo = 0, hi = pt.batch;  // invariant: s_pre[lo] <= pos < s_pre[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) / 2;
-        if (s_pre[mid] <= pos) lo = mid; else hi = mid;
+        if (uniform64(s_pre[mid]) <= pos) lo = mid; else hi = mid;
     }
     int b = lo;
     int L = a.lens[b];
-    const int64_t off = pos - s_pre[b];
+    const int64_t off = pos - uniform64(s_pre[b]);
     int ul = (int)(off / L);     // unit within the sequence
     int row = (int)(off % L);
     const int upb = pt.h_kv * pt.tiles, g = a.h_q / pt.h_kv;
@@ -732,7 +1057,7 @@ __device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn 
         row = 0;
         if (++ul == upb && pos < end) {
             ul = 0;
-            do { ++b; } while (s_pre[b + 1] == s_pre[b]);  // skip sequences without rows
+            do { ++b; } while (uniform64(s_pre[b + 1]) == uniform64(s_pre[b]));  // skip sequences without rows
             L = a.lens[b];
         }
     }
@@ -748,11 +1073,24 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a
     });
 }
 
-// Matrix-core flavour (bf16 / fp8 caches, GT in {8, 16, 32}).
+// Matrix-core flavour (GT in {8, 16, 32}; bf16 or fp8 caches).
+// Register targets: GT = 32 keeps all of the register file (one wave per SIMD); smaller
+// groups are held to 256 registers so that two waves fit per SIMD.
+template <int GT>
+struct MfmaWaves { static constexpr int kMin = GT == 32 ? 1 : 2; };
+
+// Register ring depth of the bf16 matrix-core segment (tiles of 16 rows per wave); deeper
+// rings measured no faster and need more registers.
+constexpr int kMfmaRing = 2;
+
 template <int KV, int D, int GT, bool DIRECT>
-__global__ __launch_bounds__(kBlock) void split_kv_attn_mfma_kernel(const SplitArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MfmaWaves<GT>::kMin)))
+void split_kv_attn_mfma_kernel(const SplitArgs a) {
     walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole) {
-        attend_segment_mfma<KV, D, GT>(a, b, kvh, h0, r0, r1, k, DIRECT && whole);
+        if constexpr (KV == DA_FP8_E4M3FN)
+            attend_segment_staged<KV, D, GT>(a, b, kvh, h0, r0, r1, k, DIRECT && whole);
+        else
+            attend_segment_mfma<KV, D, GT, kMfmaRing>(a, b, kvh, h0, r0, r1, k, DIRECT && whole);
     });
 }
 
