@@ -442,7 +442,7 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
     __syncthreads();  // the LDS arrays are reused by the next segment
 }
 
-// ------------------------------------------------------------------ MFMA flavour (g >= 8)
+// ------------------------------------------------------------------ MFMA flavour (g a multiple of 4)
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
@@ -487,7 +487,7 @@ __device__ __forceinline__ uint4 to_bf16x8(const typename std::conditional<KV ==
 //     exactly the A-operand layout of P; V, staged in LDS as bf16, is read back as the B
 //     operand with ds_read_b64_tr_b16. P is split into bf16 hi + lo parts (two MFMAs) so that
 //     P.V keeps ~16 bits of P's precision.
-// GT = 8, 16 or 32 heads (HT = 1 or 2 MFMA tiles of 16; heads past GT are zero padding).
+// GT = 4, 8, 16 or 32 heads (HT = 1 or 2 MFMA tiles of 16; heads past GT are zero padding).
 template <int D, int GT>
 struct MfmaAttn {
     static constexpr int HT = (GT + 15) / 16;
@@ -1073,7 +1073,7 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a
     });
 }
 
-// Matrix-core flavour (GT in {8, 16, 32}; bf16 or fp8 caches).
+// Matrix-core flavour (GT in {4, 8, 16, 32}; bf16 or fp8 caches).
 // Register targets: GT = 32 keeps all of the register file (one wave per SIMD); smaller
 // groups are held to 256 registers so that two waves fit per SIMD.
 template <int GT>
@@ -1220,13 +1220,15 @@ struct Plan {
     size_t ml_off, o_off, bytes;
 };
 
-// Flavour and query heads per workgroup: groups of 8 or more query heads over a bf16 / fp8
-// cache run on the matrix cores with 8, 16 or 32 heads per workgroup; everything else on the
-// vector ALUs with 4, 2 or 1.
-bool use_mfma(const da_desc *d) { return d->kv_dtype != DA_F32 && (d->h_q / d->h_kv) % 8 == 0; }
+// Flavour and query heads per workgroup: groups that are a multiple of 4 query heads over a
+// bf16 / fp8 cache run on the matrix cores with 4, 8, 16 or 32 heads per workgroup (fewer than
+// 16 heads pad the 16-wide head tile with zero queries: the matrix cores still take the
+// arithmetic off the vector ALUs, measured equal or faster at g = 4); everything else runs on
+// the vector ALUs with 4, 2 or 1.
+bool use_mfma(const da_desc *d) { return d->kv_dtype != DA_F32 && (d->h_q / d->h_kv) % 4 == 0; }
 int heads_per_block(const da_desc *d) {
     const int g = d->h_q / d->h_kv;
-    if (use_mfma(d)) return g % 32 == 0 ? 32 : g % 16 == 0 ? 16 : 8;
+    if (use_mfma(d)) return g % 32 == 0 ? 32 : g % 16 == 0 ? 16 : g % 8 == 0 ? 8 : 4;
     return g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
 }
 
@@ -1267,6 +1269,7 @@ const void *split_kernel_ptr(int gt, bool mfma) {
             switch (gt) {
             case 32: return reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 32, false>);
             case 16: return reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 16, false>);
+            case 4: return reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 4, false>);
             default: return reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 8, false>);
             }
         }
@@ -1330,6 +1333,7 @@ void launch_split_mfma_gt(int gt, dim3 grid, hipStream_t st, const SplitArgs &ar
     switch (gt) {
     case 32: hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 32, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
     case 16: hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 16, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
+    case 4: hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 4, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
     default: hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 8, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
     }
 }

@@ -94,8 +94,9 @@ def test_workspace_size_and_plan(lib):
     assert n >= 256 + segs * gt * 2 * 4 + segs * gt * 128 * 4
     d2 = _desc(batch=16, h_q=32, h_kv=8, cap=32768, block_rows=512)
     assert _plan(lib, d2, 1000) == (512, -(-128 * 1000 // 512), 4)
-    # query heads per workgroup: groups of 8 or more (bf16 / fp8) go to the matrix cores with
-    # 32, 16 or 8 heads; the rest to the vector ALUs with the largest of 4, 2, 1 dividing g
+    # query heads per workgroup: groups that are a multiple of 4 (bf16 / fp8) go to the matrix
+    # cores with 32, 16, 8 or 4 heads; the rest to the vector ALUs with the largest of 4, 2, 1
+    # dividing g
     assert _plan(lib, _desc(h_q=6, h_kv=2), 100)[2] == 1
     assert _plan(lib, _desc(h_q=12, h_kv=2), 100)[2] == 2
     assert _plan(lib, _desc(h_q=8, h_kv=2), 100)[2] == 4
