@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <climits>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -504,7 +505,7 @@ struct MfmaAttn {
     // q^T as the B operand of Step I: lane l holds q[head ht*16 + l%16][kb*32 + 8*(l/16) ..+8].
     __device__ __forceinline__ void init(const SplitArgs &a, int b, int h0, float score_scale) {
         lane = threadIdx.x % kWave;
-        wave = threadIdx.x / kWave;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
         lr = lane % 16;
         lg = lane / 16;
         sc = score_scale;
@@ -672,16 +673,34 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
     constexpr int ESZ = Kv<KV>::kEsz;
     constexpr uint32_t ROWB = D * ESZ;   // bytes per cache row
     constexpr int TR = 16;               // rows per wave tile
-    constexpr int STEP = TR * kWaves;    // rows per workgroup iteration
+    constexpr int STEP = TR * kWaves;    // rows per workgroup step
     constexpr int VROW = D + 8;          // staged V row, bf16 elements (16-byte pad)
     constexpr int VL = D / 8;            // lanes per row of a V load
     constexpr int VRPI = kWave / VL;     // V rows per load instruction
     constexpr int VLD = TR / VRPI;       // V loads per tile
 
+    // Rows of the segment per wave: the whole 64-row steps interleaved by 16-row tile (wave w
+    // takes tile w of each step, so a workgroup reads one contiguous 16 KiB run at a time),
+    // then the tail of fewer than 64 rows split in four nearly equal parts, one short tile
+    // per wave. The waves then reach the merge together; a tail handed out by whole tiles
+    // would leave up to one tile more on some waves.
+    const int wq = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nfull = (r1 - r0) / STEP, tail = (r1 - r0) % STEP;
+    const int ts = r0 + nfull * STEP + tail * wq / kWaves;        // this wave's tail rows
+    const int te = r0 + nfull * STEP + tail * (wq + 1) / kWaves;  // [ts, te)
     const size_t slot = (size_t)b * a.pt.h_kv + kvh;
     const size_t slot_bytes = (size_t)a.cap * ROWB;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const char *>(a.kc) + slot * slot_bytes, r1 * ROWB);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const char *>(a.vc) + slot * slot_bytes, r1 * ROWB);
+    // resources of the whole steps (rows below r1) and of this wave's tail (rows below te):
+    // rows past them read as zeros without a memory access
+    const char *kslot = static_cast<const char *>(a.kc) + slot * slot_bytes;
+    const char *vslot = static_cast<const char *>(a.vc) + slot * slot_bytes;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kslot, r1 * ROWB), vrs = make_rsrc(vslot, r1 * ROWB);
+    const __amdgpu_buffer_rsrc_t krt = make_rsrc(kslot, te * ROWB), vrt = make_rsrc(vslot, te * ROWB);
+    // tile t of this wave: its first row and the end of its rows; tiles past the last start
+    // at r1 (nothing fetched, everything masked)
+    const int ntiles = nfull + (te > ts ? 1 : 0);
+    auto tile_row = [&](int t) { return t < nfull ? r0 + t * STEP + wq * TR : t < ntiles ? ts : r1; };
+    auto tile_end = [&](int t) { return t < nfull ? r1 : te; };
     float vscale = 1.f, sc = a.qk_scale;
     if constexpr (KV == DA_FP8_E4M3FN) {
         sc *= a.kv_scales[slot * 2 + 0];
@@ -697,7 +716,7 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
     __shared__ __align__(16) float s_oo[2 * HP * D];
     __shared__ float s_mm[kWaves * HP], s_ll[kWaves * HP];
 
-    auto process = [&](const LVec (&kt)[KB], const LVec (&vt)[VLD], int tb) {
+    auto process = [&](const LVec (&kt)[KB], const LVec (&vt)[VLD], int t) {
 #pragma unroll
         for (int u = 0; u < VLD; ++u)
             *reinterpret_cast<uint4 *>(&s_v[wave][(vrow + u * VRPI) * VROW + vcol]) = to_bf16x8<KV>(vt[u]);
@@ -707,32 +726,33 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
         at.tile(ka, [&](int nb) {
             return (__attribute__((address_space(3))) uint16_t *)&s_v[wave][0] +
                    (4 * lg + lr / 4) * VROW + nb * 16 + 4 * (lane % 4);
-        }, tb, r1, &s_c[wave][0]);
+        }, tile_row(t), tile_end(t), &s_c[wave][0]);
     };
     // Software pipeline over a ring of NBUF register buffers: NBUF - 1 tiles of this wave are
     // in flight while one is computed. The ring is unrolled so every buffer index is static;
     // tiles past the segment's end read zeros and are fully masked (p = 0), so every load is
     // consumed on every path (a load used on one path only would be sunk to its use).
     LVec kr[NBUF][KB], vr[NBUF][VLD];
-    auto load = [&](LVec (&kt)[KB], LVec (&vt)[VLD], int tb) {
+    auto load = [&](LVec (&kt)[KB], LVec (&vt)[VLD], int t) {
+        const int tb = tile_row(t);
+        const bool in_tail = t >= nfull;
+        const __amdgpu_buffer_rsrc_t kr_ = in_tail ? krt : krs, vr_ = in_tail ? vrt : vrs;
         const uint32_t koff = (tb + lr) * ROWB + lg * 8 * ESZ;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kt[kb] = buffer_load<LVec>(krs, koff + kb * 32 * ESZ, 0);
+        for (int kb = 0; kb < KB; ++kb) kt[kb] = buffer_load<LVec>(kr_, koff + kb * 32 * ESZ, 0);
         const uint32_t voff = (tb + vrow) * ROWB + vcol * ESZ;
 #pragma unroll
-        for (int u = 0; u < VLD; ++u) vt[u] = buffer_load<LVec>(vrs, voff + u * VRPI * ROWB, 0);
+        for (int u = 0; u < VLD; ++u) vt[u] = buffer_load<LVec>(vr_, voff + u * VRPI * ROWB, 0);
     };
-    const int base = r0 + wave * TR;
-    const int ntiles = base < r1 ? (r1 - base + STEP - 1) / STEP : 0;
     if (ntiles > 0) {
 #pragma unroll
-        for (int j = 0; j + 1 < NBUF; ++j) load(kr[j], vr[j], base + j * STEP);
+        for (int j = 0; j + 1 < NBUF; ++j) load(kr[j], vr[j], j);
         for (int t = 0; t < ntiles; t += NBUF) {
 #pragma unroll
             for (int j = 0; j < NBUF; ++j) {
-                load(kr[(j + NBUF - 1) % NBUF], vr[(j + NBUF - 1) % NBUF], base + (t + j + NBUF - 1) * STEP);
+                load(kr[(j + NBUF - 1) % NBUF], vr[(j + NBUF - 1) % NBUF], t + j + NBUF - 1);
                 __builtin_amdgcn_sched_barrier(0);
-                process(kr[j], vr[j], base + (t + j) * STEP);
+                process(kr[j], vr[j], t + j);
             }
         }
     }
@@ -1014,9 +1034,6 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     __syncthreads();  // the LDS arrays are reused by the next segment
 }
 
-// Workgroup w walks its share of the rows and calls seg(b, kvh, h0, r0, r1, k, whole) once per
-// unit it crosses: rows [r0, r1) of (sequence b, KV head kvh) for query heads h0 .. h0+gt-1,
-// partial slot k, whole = the segment is the entire unit.
 // Values read from LDS are per-lane to the compiler; the segment bounds are the same in every
 // lane, and reading them through readfirstlane keeps them (and the buffer resources built from
 // them) in scalar registers: a per-lane resource would wrap every buffer load in a loop.
@@ -1026,41 +1043,227 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <class SegFn>
-__device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn &&seg) {
-    __shared__ int64_t s_pre[kMaxBatch + 1];
-    __shared__ int64_t s_wave[kWaves];
-    const Partition &pt = a.pt;
-    sequence_prefix(a.lens, pt, s_pre, s_wave);
-    const int64_t Tot = uniform64(s_pre[pt.batch]), N = pt.nwg, w = blockIdx.x;
-    int64_t pos = wg_start(w, Tot, N);
-    const int64_t end = wg_start(w + 1, Tot, N);
-    if (pos >= end) return;
-    // the sequence holding row `pos`: the last b with s_pre[b] <= pos (it has rows)
-    int lo = 0, hi = pt.batch;  // invariant: s_pre[lo] <= pos < s_pre[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) / 2;
-        if (uniform64(s_pre[mid]) <= pos) lo = mid; else hi = mid;
+// The segments of one workgroup, in order: rows [r0, r1) of (sequence sb, KV head kvh) for
+// query heads h0 .. h0+gt-1, partial slot k, whole = the segment is the entire unit. Every
+// field is the same in all lanes (scalar registers); copies of a walk advance independently.
+struct SegWalk {
+    const int32_t *lens;
+    const int64_t *pre;  // exclusive prefix of rows per sequence (LDS), pre[batch] = T
+    int64_t pos, end, w;
+    int b, L, ul, row, upb, g, gt, tiles;
+    bool has;  // a current segment
+    int ord;   // its ordinal within the workgroup (counts on past the last)
+    int sb, kvh, h0, r0, r1;
+    size_t k;
+    bool whole;
+
+    // Positions the walk on the workgroup's first segment; pre must hold the prefix.
+    __device__ __forceinline__ void start(const SplitArgs &a, int gt_, const int64_t *s_pre) {
+        const Partition &pt = a.pt;
+        lens = a.lens;
+        pre = s_pre;
+        gt = gt_;
+        tiles = pt.tiles;
+        upb = pt.h_kv * pt.tiles;
+        g = a.h_q / pt.h_kv;
+        const int64_t Tot = uniform64(s_pre[pt.batch]), N = pt.nwg;
+        w = blockIdx.x;
+        pos = wg_start(w, Tot, N);
+        end = wg_start(w + 1, Tot, N);
+        ord = -1;
+        b = 0, L = 1, ul = 0, row = 0;
+        if (pos < end) {
+            // the sequence holding row `pos`: the last b with pre[b] <= pos (it has rows)
+            int lo = 0, hi = pt.batch;  // invariant: pre[lo] <= pos < pre[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) / 2;
+                if (uniform64(s_pre[mid]) <= pos) lo = mid; else hi = mid;
+            }
+            b = lo;
+            L = lens[b];
+            const int64_t off = pos - uniform64(s_pre[b]);
+            ul = (int)(off / L);  // unit within the sequence
+            row = (int)(off % L);
+        }
+        next();
     }
-    int b = lo;
-    int L = a.lens[b];
-    const int64_t off = pos - uniform64(s_pre[b]);
-    int ul = (int)(off / L);     // unit within the sequence
-    int row = (int)(off % L);
-    const int upb = pt.h_kv * pt.tiles, g = a.h_q / pt.h_kv;
-    while (pos < end) {
-        const int r1 = (int)min<int64_t>((int64_t)L, row + (end - pos));
-        const int kvh = ul / pt.tiles, h0 = kvh * g + (ul % pt.tiles) * gt;
-        const size_t u = (size_t)b * upb + ul;
-        seg(b, kvh, h0, row, r1, (size_t)w + u, row == 0 && r1 == L);
-        pos += r1 - row;
+    __device__ __forceinline__ void next() {
+        ++ord;
+        has = pos < end;
+        if (!has) return;
+        r0 = row;
+        r1 = (int)min<int64_t>((int64_t)L, row + (end - pos));
+        kvh = ul / tiles;
+        h0 = kvh * g + (ul % tiles) * gt;
+        sb = b;
+        k = (size_t)w + (size_t)b * upb + ul;
+        whole = r0 == 0 && r1 == L;
+        pos += r1 - r0;
         row = 0;
         if (++ul == upb && pos < end) {
             ul = 0;
-            do { ++b; } while (uniform64(s_pre[b + 1]) == uniform64(s_pre[b]));  // skip sequences without rows
-            L = a.lens[b];
+            do { ++b; } while (uniform64(pre[b + 1]) == uniform64(pre[b]));  // skip sequences without rows
+            L = lens[b];
         }
     }
+};
+
+// Computes the sequence prefix in LDS and returns the walk on the workgroup's first segment.
+__device__ __forceinline__ SegWalk first_segment(const SplitArgs &a, int gt) {
+    __shared__ int64_t s_pre[kMaxBatch + 1];
+    __shared__ int64_t s_wave[kWaves];
+    sequence_prefix(a.lens, a.pt, s_pre, s_wave);
+    SegWalk wk;
+    wk.start(a, gt, s_pre);
+    return wk;
+}
+
+// Workgroup w walks its share of the rows and calls seg(b, kvh, h0, r0, r1, k, whole) once per
+// unit it crosses.
+template <class SegFn>
+__device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn &&seg) {
+    for (SegWalk wk = first_segment(a, gt); wk.has; wk.next())
+        seg(wk.sb, wk.kvh, wk.h0, wk.r0, wk.r1, wk.k, wk.whole);
+}
+
+// Matrix-core flavour over all of a workgroup's segments as one stream of tiles (bf16 or fp8
+// caches, tiles staged through registers). Each wave owns the 16-row tiles r0 + 16*wave +
+// 64*j of every segment. A ring of NBUF register buffers keeps NBUF - 1 of the wave's tiles in
+// flight; the load side runs that far ahead of the compute side across segment boundaries, so
+// the next segment's rows are already arriving while the four waves merge and write the
+// segment that just ended (a merge per segment would otherwise drain the pipeline and refill
+// it from cold). The compute side finishes every segment of the workgroup in order, also
+// those in which this wave has no tile, so all waves pass the merge barriers alike.
+//   K rows are loaded straight into A-operand order; V rows are widened to bf16 and stored
+//   row-major in the wave's LDS tile for the transpose read.
+template <int KV, int D, int GT, int NBUF, bool DIRECT>
+__device__ __forceinline__ void attend_stream_mfma(const SplitArgs &a, const SegWalk &first) {
+    static_assert(KV == DA_BF16 || KV == DA_FP8_E4M3FN, "MFMA flavour takes bf16 or fp8 caches");
+    using LVec = typename std::conditional<KV == DA_BF16, uint4, uint2>::type;  // 8 elements
+    using A = MfmaAttn<D, GT>;
+    constexpr int KB = A::KB, HP = A::HT * 16;
+    constexpr int ESZ = Kv<KV>::kEsz;
+    constexpr uint32_t ROWB = D * ESZ;   // bytes per cache row
+    constexpr int TR = 16;               // rows per wave tile
+    constexpr int STEP = TR * kWaves;    // rows per workgroup iteration
+    constexpr int VROW = D + 8;          // staged V row, bf16 elements (16-byte pad)
+    constexpr int VL = D / 8;            // lanes per row of a V load
+    constexpr int VRPI = kWave / VL;     // V rows per load instruction
+    constexpr int VLD = TR / VRPI;       // V loads per tile
+    if (!first.has) return;  // the same in every wave: no merge barrier is reached
+
+    // wave index through readfirstlane: every branch around the merge barriers below is then a
+    // scalar branch, taken or skipped by the whole wave
+    const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lr = lane % 16, lg = lane / 16;
+    const int vrow = lane / VL, vcol = (lane % VL) * 8;
+    const size_t slot_bytes = (size_t)a.cap * ROWB;
+
+    __shared__ __align__(16) uint16_t s_v[kWaves][TR * VROW];
+    __shared__ __align__(16) float s_c[kWaves][HP];
+    __shared__ __align__(16) float s_oo[2 * HP * D];
+    __shared__ float s_mm[kWaves * HP], s_ll[kWaves * HP];
+
+    // Load side: walk lw at this wave's tile ltb, with resources covering rows [0, r1) of the
+    // segment (rows past r1 read as zeros); past the last segment the resources are empty.
+    SegWalk lw = first;
+    int ltb = 0;
+    __amdgpu_buffer_rsrc_t krs, vrs;
+    auto lsettle = [&]() {
+        while (lw.has && lw.r0 + wave * TR >= lw.r1) lw.next();  // segments with no tile of this wave
+        ltb = lw.r0 + wave * TR;
+        const size_t slot = (size_t)lw.sb * a.pt.h_kv + lw.kvh;
+        const uint32_t nbytes = lw.has ? (uint32_t)lw.r1 * ROWB : 0u;
+        krs = make_rsrc(static_cast<const char *>(a.kc) + (lw.has ? slot * slot_bytes : 0), nbytes);
+        vrs = make_rsrc(static_cast<const char *>(a.vc) + (lw.has ? slot * slot_bytes : 0), nbytes);
+    };
+    auto ladvance = [&]() {
+        if (!lw.has) return;
+        ltb += STEP;
+        if (ltb >= lw.r1) {
+            lw.next();
+            lsettle();
+        }
+    };
+    auto load = [&](LVec (&kt)[KB], LVec (&vt)[VLD]) {
+        const uint32_t koff = (ltb + lr) * ROWB + lg * 8 * ESZ;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) kt[kb] = buffer_load<LVec>(krs, koff + kb * 32 * ESZ, 0);
+        const uint32_t voff = (ltb + vrow) * ROWB + vcol * ESZ;
+#pragma unroll
+        for (int u = 0; u < VLD; ++u) vt[u] = buffer_load<LVec>(vrs, voff + u * VRPI * ROWB, 0);
+    };
+
+    // Compute side: walk cw at this wave's tile ctb; fw = the segment being accumulated.
+    SegWalk cw = first, fw = first;
+    int ctb = 0;
+    auto csettle = [&]() {
+        while (cw.has && cw.r0 + wave * TR >= cw.r1) cw.next();
+        ctb = cw.r0 + wave * TR;
+    };
+    A at;
+    float vscale = 1.f;
+    auto begin = [&]() {  // q of fw's heads, scales, empty accumulators
+        float sc = a.qk_scale;
+        if constexpr (KV == DA_FP8_E4M3FN) {
+            const size_t slot = (size_t)fw.sb * a.pt.h_kv + fw.kvh;
+            sc *= a.kv_scales[slot * 2 + 0];
+            vscale = a.kv_scales[slot * 2 + 1];
+        }
+        at.init(a, fw.sb, fw.h0, sc);
+    };
+    auto finish_to = [&](int ord) {  // merge and write every segment before ordinal ord
+        while (fw.has && fw.ord < ord) {
+            at.finish(a, fw.sb, fw.h0, fw.k, DIRECT && fw.whole, vscale, s_oo, s_mm, s_ll);
+            fw.next();
+            if (fw.has) begin();
+        }
+    };
+    auto process = [&](const LVec (&kt)[KB], const LVec (&vt)[VLD]) {
+        finish_to(cw.ord);
+        // past the last tile the loads were empty: the tile is fully masked (p = 0)
+        const int tb = cw.has ? ctb : 0, r1 = cw.has ? cw.r1 : 0;
+#pragma unroll
+        for (int u = 0; u < VLD; ++u)
+            *reinterpret_cast<uint4 *>(&s_v[wave][(vrow + u * VRPI) * VROW + vcol]) = to_bf16x8<KV>(vt[u]);
+        bf16x8_t ka[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) ka[kb] = __builtin_bit_cast(bf16x8_t, to_bf16x8<KV>(kt[kb]));
+        at.tile(ka, [&](int nb) {
+            return (__attribute__((address_space(3))) uint16_t *)&s_v[wave][0] +
+                   (4 * lg + lr / 4) * VROW + nb * 16 + 4 * (lane % 4);
+        }, tb, r1, &s_c[wave][0]);
+        if (cw.has) {
+            ctb += STEP;
+            if (ctb >= cw.r1) {
+                cw.next();
+                csettle();
+            }
+        }
+    };
+
+    begin();
+    lsettle();
+    csettle();
+    // The ring is unrolled so that every buffer index is static, and every loaded buffer is
+    // consumed on every path (a load used on one path only would be sunk to its use).
+    LVec kr[NBUF][KB], vr[NBUF][VLD];
+#pragma unroll
+    for (int j = 0; j + 1 < NBUF; ++j) {
+        load(kr[j], vr[j]);
+        ladvance();
+    }
+    for (;;) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+            load(kr[(j + NBUF - 1) % NBUF], vr[(j + NBUF - 1) % NBUF]);
+            ladvance();
+            __builtin_amdgcn_sched_barrier(0);
+            process(kr[j], vr[j]);
+        }
+        if (!cw.has) break;
+    }
+    finish_to(INT_MAX);
 }
 
 // VALU flavour (any group size; GT in {1, 2, 4}). DIRECT (decode_attn_run): a unit covered by
@@ -1086,12 +1289,15 @@ constexpr int kMfmaRing = 2;
 template <int KV, int D, int GT, bool DIRECT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MfmaWaves<GT>::kMin)))
 void split_kv_attn_mfma_kernel(const SplitArgs a) {
-    walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole) {
-        if constexpr (KV == DA_FP8_E4M3FN)
+    if constexpr (KV == DA_FP8_E4M3FN) {
+        walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole) {
             attend_segment_staged<KV, D, GT>(a, b, kvh, h0, r0, r1, k, DIRECT && whole);
-        else
+        });
+    } else {
+        walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole) {
             attend_segment_mfma<KV, D, GT, kMfmaRing>(a, b, kvh, h0, r0, r1, k, DIRECT && whole);
-    });
+        });
+    }
 }
 
 // One workgroup per (sequence, query head): merge the segments of the head's unit by their
