@@ -28,6 +28,7 @@ from ._lib import DA_BF16, DA_F32, DA_FP8_E4M3FN, lib, library_path  # noqa: F40
 __all__ = [
     "Desc", "DecodeAttnError", "Workspace", "da_workspace_size", "da_plan", "da_workspace_init",
     "kv_append", "decode_attn_run", "decode_attn_partial", "decode_attn_combine",
+    "decode_attn_append_run", "decode_attn_append_partial", "decode_attn_append_combine",
     "da_read_device_error", "da_status_string", "da_last_error", "library_path",
     "DA_F32", "DA_BF16", "DA_FP8_E4M3FN", "DEV_ERR_APPEND_FULL", "DEV_ERR_LEN_RANGE",
 ]
@@ -202,6 +203,46 @@ def decode_attn_combine(desc: Desc, lens, max_len: int, out, workspace) -> None:
     cd = desc.c()
     _check(lib().decode_attn_combine(ctypes.byref(cd), ln, int(max_len), op, wp, wn, _stream(out)),
            "decode_attn_combine")
+
+
+def _append_args(desc: Desc, k_cache, k_new, v_new):
+    dev = k_cache.device
+    kn = _dev(k_new, "k_new", (desc.batch, desc.h_kv, desc.d), desc.kv_dtype, dev)
+    vn = _dev(v_new, "v_new", (desc.batch, desc.h_kv, desc.d), desc.kv_dtype, dev)
+    return kn, vn
+
+
+def decode_attn_append_run(desc: Desc, q, k_cache, v_cache, lens, k_new, v_new, max_len: int, kv_scales, out,
+                           workspace) -> None:
+    """One decode step: append the new K/V rows, attend over lens + 1 rows, lens += 1."""
+    qp, kc, vc, ln, sc = _attn_args(desc, q, k_cache, v_cache, lens, kv_scales)
+    kn, vn = _append_args(desc, k_cache, k_new, v_new)
+    op = _dev(out, "out", (desc.batch, desc.h_q, desc.d), torch.float32, q.device)
+    wp, wn, _ = _ws(workspace)
+    cd = desc.c()
+    _check(lib().decode_attn_append_run(ctypes.byref(cd), qp, kc, vc, ln, kn, vn, int(max_len), sc, op, wp, wn,
+                                        _stream(q)), "decode_attn_append_run")
+
+
+def decode_attn_append_partial(desc: Desc, q, k_cache, v_cache, lens, k_new, v_new, max_len: int, kv_scales,
+                               workspace) -> None:
+    """First stage of the fused step: append + per-split partials (lens unchanged)."""
+    qp, kc, vc, ln, sc = _attn_args(desc, q, k_cache, v_cache, lens, kv_scales)
+    kn, vn = _append_args(desc, k_cache, k_new, v_new)
+    wp, wn, _ = _ws(workspace)
+    cd = desc.c()
+    _check(lib().decode_attn_append_partial(ctypes.byref(cd), qp, kc, vc, ln, kn, vn, int(max_len), sc, wp, wn,
+                                            _stream(q)), "decode_attn_append_partial")
+
+
+def decode_attn_append_combine(desc: Desc, lens, max_len: int, out, workspace) -> None:
+    """Second stage of the fused step: merge into out, then lens += 1 where appended."""
+    ln = _dev(lens, "lens", (desc.batch,), torch.int32)
+    op = _dev(out, "out", (desc.batch, desc.h_q, desc.d), torch.float32, lens.device)
+    wp, wn, _ = _ws(workspace)
+    cd = desc.c()
+    _check(lib().decode_attn_append_combine(ctypes.byref(cd), ln, int(max_len), op, wp, wn, _stream(out)),
+           "decode_attn_append_combine")
 
 
 def da_read_device_error(workspace) -> int:

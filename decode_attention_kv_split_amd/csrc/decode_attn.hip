@@ -25,7 +25,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
-#include <climits>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -190,8 +189,15 @@ constexpr int kMaxBatch = 1024;
 
 struct Partition {
     int batch, h_kv, tiles, max_len, nwg;
+    int append_cap;  // > 0: this pass first appends one row per (sequence, KV head); the cache capacity
 };
 
+// Rows a pass attends over for a sequence whose stored length is L: with an append in the
+// same pass, L + 1 when the new row fits (L in [0, cap)); otherwise L (that append is skipped
+// and flagged, as kv_append does).
+__device__ __forceinline__ int attended_len(int L, int append_cap) {
+    return (append_cap > 0 && L >= 0 && L < append_cap) ? L + 1 : L;
+}
 __device__ __forceinline__ int64_t unit_rows(int L, int max_len) { return (L >= 1 && L <= max_len) ? L : 0; }
 __device__ __forceinline__ int64_t wg_start(int64_t w, int64_t T, int64_t N) { return w * T / N; }
 __device__ __forceinline__ int64_t wg_owner(int64_t x, int64_t T, int64_t N) { return ((x + 1) * N - 1) / T; }
@@ -208,7 +214,7 @@ __device__ void sequence_prefix(const int32_t *__restrict__ lens, const Partitio
     for (int i = 0; i < kMaxBatch / kBlock; ++i) {
         const int bb = threadIdx.x * per + i;
         local[i] = sum;
-        if (i < per && bb < pt.batch) sum += unit_rows(lens[bb], pt.max_len) * upb;
+        if (i < per && bb < pt.batch) sum += unit_rows(attended_len(lens[bb], pt.append_cap), pt.max_len) * upb;
     }
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     int64_t incl = sum;
@@ -241,6 +247,12 @@ struct SplitArgs {
     int h_q, cap;
     Partition pt;
     float qk_scale;           // scale * log2(e)
+    // fused append (pt.append_cap > 0): the new rows [B, h_kv, row_bytes] of K and V, the
+    // workspace copy of the stored lengths (read by the combine, which then updates lens) and
+    // the workspace error word
+    const void *k_new, *v_new;
+    int32_t *lens_copy, *err;
+    int row_bytes;
 };
 
 // Steps I-III over rows [r0, r1) of one (sequence b, KV head kvh) for query heads
@@ -1050,12 +1062,14 @@ struct SegWalk {
     const int32_t *lens;
     const int64_t *pre;  // exclusive prefix of rows per sequence (LDS), pre[batch] = T
     int64_t pos, end, w;
-    int b, L, ul, row, upb, g, gt, tiles;
+    int b, L, ul, row, upb, g, gt, tiles, append_cap;
     bool has;  // a current segment
     int ord;   // its ordinal within the workgroup (counts on past the last)
     int sb, kvh, h0, r0, r1;
+    int slen;      // rows of the segment's sequence (the walk state moves on past them)
     size_t k;
     bool whole;
+    bool new_row;  // this pass appended the unit's last row (row slen - 1)
 
     // Positions the walk on the workgroup's first segment; pre must hold the prefix.
     __device__ __forceinline__ void start(const SplitArgs &a, int gt_, const int64_t *s_pre) {
@@ -1066,6 +1080,7 @@ struct SegWalk {
         tiles = pt.tiles;
         upb = pt.h_kv * pt.tiles;
         g = a.h_q / pt.h_kv;
+        append_cap = pt.append_cap;
         const int64_t Tot = uniform64(s_pre[pt.batch]), N = pt.nwg;
         w = blockIdx.x;
         pos = wg_start(w, Tot, N);
@@ -1080,7 +1095,7 @@ struct SegWalk {
                 if (uniform64(s_pre[mid]) <= pos) lo = mid; else hi = mid;
             }
             b = lo;
-            L = lens[b];
+            L = attended_len(lens[b], append_cap);
             const int64_t off = pos - uniform64(s_pre[b]);
             ul = (int)(off / L);  // unit within the sequence
             row = (int)(off % L);
@@ -1097,13 +1112,15 @@ struct SegWalk {
         h0 = kvh * g + (ul % tiles) * gt;
         sb = b;
         k = (size_t)w + (size_t)b * upb + ul;
+        slen = L;
         whole = r0 == 0 && r1 == L;
+        new_row = append_cap > 0 && L != lens[b];
         pos += r1 - r0;
         row = 0;
         if (++ul == upb && pos < end) {
             ul = 0;
             do { ++b; } while (uniform64(pre[b + 1]) == uniform64(pre[b]));  // skip sequences without rows
-            L = lens[b];
+            L = attended_len(lens[b], append_cap);
         }
     }
 };
@@ -1112,6 +1129,14 @@ struct SegWalk {
 __device__ __forceinline__ SegWalk first_segment(const SplitArgs &a, int gt) {
     __shared__ int64_t s_pre[kMaxBatch + 1];
     __shared__ int64_t s_wave[kWaves];
+    if (a.pt.append_cap > 0 && blockIdx.x == 0) {
+        // the combine reads the stored lengths from this copy, so that it may update lens
+        for (int b = threadIdx.x; b < a.pt.batch; b += kBlock) {
+            const int L = a.lens[b];
+            a.lens_copy[b] = L;
+            if (L < 0 || L >= a.pt.append_cap) atomicOr(a.err, DA_DEV_ERR_APPEND_FULL);
+        }
+    }
     sequence_prefix(a.lens, a.pt, s_pre, s_wave);
     SegWalk wk;
     wk.start(a, gt, s_pre);
@@ -1120,150 +1145,32 @@ __device__ __forceinline__ SegWalk first_segment(const SplitArgs &a, int gt) {
 
 // Workgroup w walks its share of the rows and calls seg(b, kvh, h0, r0, r1, k, whole) once per
 // unit it crosses.
+// With a fused append, a segment that ends at a unit's new last row first stores that row of
+// K and V into the cache itself; the barrier (a workgroup-scope release and acquire) makes the
+// stores visible to the loads of every wave of the workgroup. Only workgroups holding that
+// row read it in this pass, and each of them writes it (the same bytes) before reading.
 template <class SegFn>
 __device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn &&seg) {
-    for (SegWalk wk = first_segment(a, gt); wk.has; wk.next())
-        seg(wk.sb, wk.kvh, wk.h0, wk.r0, wk.r1, wk.k, wk.whole);
-}
-
-// Matrix-core flavour over all of a workgroup's segments as one stream of tiles (bf16 or fp8
-// caches, tiles staged through registers). Each wave owns the 16-row tiles r0 + 16*wave +
-// 64*j of every segment. A ring of NBUF register buffers keeps NBUF - 1 of the wave's tiles in
-// flight; the load side runs that far ahead of the compute side across segment boundaries, so
-// the next segment's rows are already arriving while the four waves merge and write the
-// segment that just ended (a merge per segment would otherwise drain the pipeline and refill
-// it from cold). The compute side finishes every segment of the workgroup in order, also
-// those in which this wave has no tile, so all waves pass the merge barriers alike.
-//   K rows are loaded straight into A-operand order; V rows are widened to bf16 and stored
-//   row-major in the wave's LDS tile for the transpose read.
-template <int KV, int D, int GT, int NBUF, bool DIRECT>
-__device__ __forceinline__ void attend_stream_mfma(const SplitArgs &a, const SegWalk &first) {
-    static_assert(KV == DA_BF16 || KV == DA_FP8_E4M3FN, "MFMA flavour takes bf16 or fp8 caches");
-    using LVec = typename std::conditional<KV == DA_BF16, uint4, uint2>::type;  // 8 elements
-    using A = MfmaAttn<D, GT>;
-    constexpr int KB = A::KB, HP = A::HT * 16;
-    constexpr int ESZ = Kv<KV>::kEsz;
-    constexpr uint32_t ROWB = D * ESZ;   // bytes per cache row
-    constexpr int TR = 16;               // rows per wave tile
-    constexpr int STEP = TR * kWaves;    // rows per workgroup iteration
-    constexpr int VROW = D + 8;          // staged V row, bf16 elements (16-byte pad)
-    constexpr int VL = D / 8;            // lanes per row of a V load
-    constexpr int VRPI = kWave / VL;     // V rows per load instruction
-    constexpr int VLD = TR / VRPI;       // V loads per tile
-    if (!first.has) return;  // the same in every wave: no merge barrier is reached
-
-    // wave index through readfirstlane: every branch around the merge barriers below is then a
-    // scalar branch, taken or skipped by the whole wave
-    const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int lr = lane % 16, lg = lane / 16;
-    const int vrow = lane / VL, vcol = (lane % VL) * 8;
-    const size_t slot_bytes = (size_t)a.cap * ROWB;
-
-    __shared__ __align__(16) uint16_t s_v[kWaves][TR * VROW];
-    __shared__ __align__(16) float s_c[kWaves][HP];
-    __shared__ __align__(16) float s_oo[2 * HP * D];
-    __shared__ float s_mm[kWaves * HP], s_ll[kWaves * HP];
-
-    // Load side: walk lw at this wave's tile ltb, with resources covering rows [0, r1) of the
-    // segment (rows past r1 read as zeros); past the last segment the resources are empty.
-    SegWalk lw = first;
-    int ltb = 0;
-    __amdgpu_buffer_rsrc_t krs, vrs;
-    auto lsettle = [&]() {
-        while (lw.has && lw.r0 + wave * TR >= lw.r1) lw.next();  // segments with no tile of this wave
-        ltb = lw.r0 + wave * TR;
-        const size_t slot = (size_t)lw.sb * a.pt.h_kv + lw.kvh;
-        const uint32_t nbytes = lw.has ? (uint32_t)lw.r1 * ROWB : 0u;
-        krs = make_rsrc(static_cast<const char *>(a.kc) + (lw.has ? slot * slot_bytes : 0), nbytes);
-        vrs = make_rsrc(static_cast<const char *>(a.vc) + (lw.has ? slot * slot_bytes : 0), nbytes);
-    };
-    auto ladvance = [&]() {
-        if (!lw.has) return;
-        ltb += STEP;
-        if (ltb >= lw.r1) {
-            lw.next();
-            lsettle();
-        }
-    };
-    auto load = [&](LVec (&kt)[KB], LVec (&vt)[VLD]) {
-        const uint32_t koff = (ltb + lr) * ROWB + lg * 8 * ESZ;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kt[kb] = buffer_load<LVec>(krs, koff + kb * 32 * ESZ, 0);
-        const uint32_t voff = (ltb + vrow) * ROWB + vcol * ESZ;
-#pragma unroll
-        for (int u = 0; u < VLD; ++u) vt[u] = buffer_load<LVec>(vrs, voff + u * VRPI * ROWB, 0);
-    };
-
-    // Compute side: walk cw at this wave's tile ctb; fw = the segment being accumulated.
-    SegWalk cw = first, fw = first;
-    int ctb = 0;
-    auto csettle = [&]() {
-        while (cw.has && cw.r0 + wave * TR >= cw.r1) cw.next();
-        ctb = cw.r0 + wave * TR;
-    };
-    A at;
-    float vscale = 1.f;
-    auto begin = [&]() {  // q of fw's heads, scales, empty accumulators
-        float sc = a.qk_scale;
-        if constexpr (KV == DA_FP8_E4M3FN) {
-            const size_t slot = (size_t)fw.sb * a.pt.h_kv + fw.kvh;
-            sc *= a.kv_scales[slot * 2 + 0];
-            vscale = a.kv_scales[slot * 2 + 1];
-        }
-        at.init(a, fw.sb, fw.h0, sc);
-    };
-    auto finish_to = [&](int ord) {  // merge and write every segment before ordinal ord
-        while (fw.has && fw.ord < ord) {
-            at.finish(a, fw.sb, fw.h0, fw.k, DIRECT && fw.whole, vscale, s_oo, s_mm, s_ll);
-            fw.next();
-            if (fw.has) begin();
-        }
-    };
-    auto process = [&](const LVec (&kt)[KB], const LVec (&vt)[VLD]) {
-        finish_to(cw.ord);
-        // past the last tile the loads were empty: the tile is fully masked (p = 0)
-        const int tb = cw.has ? ctb : 0, r1 = cw.has ? cw.r1 : 0;
-#pragma unroll
-        for (int u = 0; u < VLD; ++u)
-            *reinterpret_cast<uint4 *>(&s_v[wave][(vrow + u * VRPI) * VROW + vcol]) = to_bf16x8<KV>(vt[u]);
-        bf16x8_t ka[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) ka[kb] = __builtin_bit_cast(bf16x8_t, to_bf16x8<KV>(kt[kb]));
-        at.tile(ka, [&](int nb) {
-            return (__attribute__((address_space(3))) uint16_t *)&s_v[wave][0] +
-                   (4 * lg + lr / 4) * VROW + nb * 16 + 4 * (lane % 4);
-        }, tb, r1, &s_c[wave][0]);
-        if (cw.has) {
-            ctb += STEP;
-            if (ctb >= cw.r1) {
-                cw.next();
-                csettle();
+    for (SegWalk wk = first_segment(a, gt); wk.has; wk.next()) {
+        if (wk.new_row && wk.r1 == wk.slen) {
+            const int n16 = a.row_bytes / 16;
+            const size_t slot = (size_t)wk.sb * a.pt.h_kv + wk.kvh;
+            const int t = threadIdx.x;
+            if (t < 2 * n16) {
+                const bool v = t >= n16;
+                const uint4 x = reinterpret_cast<const uint4 *>(
+                    static_cast<const char *>(v ? a.v_new : a.k_new) + slot * a.row_bytes)[t % n16];
+                char *dst = const_cast<char *>(static_cast<const char *>(v ? a.vc : a.kc)) +
+                            (slot * a.cap + (wk.slen - 1)) * (size_t)a.row_bytes;
+                reinterpret_cast<uint4 *>(dst)[t % n16] = x;
             }
+            __syncthreads();
+            // a row shorter than a cache line shares its line with the previous row, which
+            // another workgroup on this CU may hold, stale, in the vector L1: drop it
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
-    };
-
-    begin();
-    lsettle();
-    csettle();
-    // The ring is unrolled so that every buffer index is static, and every loaded buffer is
-    // consumed on every path (a load used on one path only would be sunk to its use).
-    LVec kr[NBUF][KB], vr[NBUF][VLD];
-#pragma unroll
-    for (int j = 0; j + 1 < NBUF; ++j) {
-        load(kr[j], vr[j]);
-        ladvance();
+        seg(wk.sb, wk.kvh, wk.h0, wk.r0, wk.r1, wk.k, wk.whole);
     }
-    for (;;) {
-#pragma unroll
-        for (int j = 0; j < NBUF; ++j) {
-            load(kr[(j + NBUF - 1) % NBUF], vr[(j + NBUF - 1) % NBUF]);
-            ladvance();
-            __builtin_amdgcn_sched_barrier(0);
-            process(kr[j], vr[j]);
-        }
-        if (!cw.has) break;
-    }
-    finish_to(INT_MAX);
 }
 
 // VALU flavour (any group size; GT in {1, 2, 4}). DIRECT (decode_attn_run): a unit covered by
@@ -1302,14 +1209,18 @@ void split_kv_attn_mfma_kernel(const SplitArgs a) {
 
 // One workgroup per (sequence, query head): merge the segments of the head's unit by their
 // log-sum-exp weights. skip_single: a unit covered by one workgroup was already written.
+// With a fused append (pt.append_cap > 0) the stored lengths come from the split kernel's
+// workspace copy, and the workgroup of head 0 writes each sequence's new length to lens_upd.
 template <int D>
 __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
-    const int32_t *__restrict__ lens, const float *__restrict__ part_ml, const float *__restrict__ part_o,
-    float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt, Partition pt, int skip_single) {
+    const int32_t *__restrict__ lens, int32_t *__restrict__ lens_upd, const float *__restrict__ part_ml,
+    const float *__restrict__ part_o, float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt,
+    Partition pt, int skip_single) {
     constexpr int SG = kCombineBlock / D;  // segment groups working side by side
     const int bh = blockIdx.x;
     const int b = bh / h_q, h = bh % h_q;
-    const int L = lens[b];
+    const int L = attended_len(lens[b], pt.append_cap);
+    if (lens_upd && h == 0 && threadIdx.x == 0) lens_upd[b] = L;
     float *dst = out + (size_t)bh * D;
     if (L < 1 || L > pt.max_len) {
         for (int d = threadIdx.x; d < D; d += kCombineBlock) dst[d] = 0.f;
@@ -1321,7 +1232,7 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     const int64_t upb = (int64_t)pt.h_kv * pt.tiles;
     int64_t before = 0, total = 0;
     for (int bb = threadIdx.x; bb < pt.batch; bb += kCombineBlock) {
-        const int64_t r = unit_rows(lens[bb], pt.max_len) * upb;
+        const int64_t r = unit_rows(attended_len(lens[bb], pt.append_cap), pt.max_len) * upb;
         total += r;
         if (bb < b) before += r;
     }
@@ -1423,7 +1334,7 @@ int validate(const da_desc *d) {
 struct Plan {
     int gt, tiles, nwg;
     bool mfma;  // matrix-core flavour
-    size_t ml_off, o_off, bytes;
+    size_t lens_off, ml_off, o_off, bytes;  // workspace: header, lengths copy, (max, sum), rows
 };
 
 // Flavour and query heads per workgroup: groups that are a multiple of 4 query heads over a
@@ -1513,7 +1424,8 @@ int make_plan(const da_desc *d, int max_len, Plan *p) {
     p->nwg = (int)std::max<int64_t>(1, std::min<int64_t>(nwg, 1 << 20));
     const size_t segs = (size_t)p->nwg + units;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    p->ml_off = kHeaderBytes;
+    p->lens_off = kHeaderBytes;
+    p->ml_off = p->lens_off + up((size_t)d->batch * sizeof(int32_t));
     p->o_off = p->ml_off + up(segs * p->gt * 2 * sizeof(float));
     p->bytes = p->o_off + up(segs * p->gt * d->d_v * sizeof(float));
     return DA_OK;
@@ -1568,13 +1480,14 @@ void launch_split(int kv, int d, int gt, bool mfma, dim3 grid, hipStream_t st, c
     }
 }
 
-Partition partition_of(const da_desc *desc, const Plan &p, int max_len) {
+Partition partition_of(const da_desc *desc, const Plan &p, int max_len, bool append) {
     Partition pt;
     pt.batch = desc->batch;
     pt.h_kv = desc->h_kv;
     pt.tiles = p.tiles;
     pt.max_len = max_len;
     pt.nwg = p.nwg;
+    pt.append_cap = append ? desc->cap : 0;
     return pt;
 }
 
@@ -1582,13 +1495,16 @@ Partition partition_of(const da_desc *desc, const Plan &p, int max_len) {
 // workgroup covers are written to out directly (decode_attn_run); otherwise every segment
 // writes its partial result (decode_attn_partial).
 int run_split(const da_desc *desc, const void *q, const void *k_cache, const void *v_cache, const int32_t *lens,
-              int32_t max_len, const float *kv_scales, float *out, void *workspace, size_t ws_bytes,
-              void *stream, const char *who) {
+              const void *k_new, const void *v_new, int32_t max_len, const float *kv_scales, float *out,
+              void *workspace, size_t ws_bytes, void *stream, const char *who) {
     Plan p;
     int rc = make_plan(desc, max_len, &p);
     if (rc) return rc;
     if (!q || !k_cache || !v_cache || !lens || !workspace)
         return fail(DA_ERR_INVALID_ARG, "%s: a buffer pointer is NULL", who);
+    const bool append = k_new || v_new;
+    if (append && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)))
+        return fail(DA_ERR_INVALID_ARG, "%s: k_new and v_new must both be 16-byte aligned device pointers", who);
     if (desc->kv_dtype == DA_FP8_E4M3FN && !kv_scales)
         return fail(DA_ERR_INVALID_ARG, "%s: an fp8 cache needs kv_scales", who);
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace) ||
@@ -1608,8 +1524,13 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     args.out = out;
     args.h_q = desc->h_q;
     args.cap = desc->cap;
-    args.pt = partition_of(desc, p, max_len);
+    args.pt = partition_of(desc, p, max_len, append);
     args.qk_scale = desc->scale * kLog2e;
+    args.k_new = k_new;
+    args.v_new = v_new;
+    args.lens_copy = reinterpret_cast<int32_t *>(ws + p.lens_off);
+    args.err = reinterpret_cast<int32_t *>(ws);
+    args.row_bytes = desc->d_k * elem_size(desc->kv_dtype);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (out)
         launch_split<true>(desc->kv_dtype, desc->d_k, p.gt, p.mfma, dim3(p.nwg), st, args);
@@ -1618,8 +1539,8 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     return launch_status("split_kv_attn_kernel");
 }
 
-int run_combine(const da_desc *desc, const int32_t *lens, int32_t max_len, float *out, void *workspace,
-                size_t ws_bytes, void *stream, int skip_single, const char *who) {
+int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out, void *workspace,
+                size_t ws_bytes, void *stream, int skip_single, bool append, const char *who) {
     Plan p;
     int rc = make_plan(desc, max_len, &p);
     if (rc) return rc;
@@ -1633,13 +1554,16 @@ int run_combine(const da_desc *desc, const int32_t *lens, int32_t max_len, float
     const float *po = reinterpret_cast<const float *>(ws + p.o_off);
     int32_t *err = reinterpret_cast<int32_t *>(ws);
     const dim3 grid(desc->batch * desc->h_q);
-    const Partition pt = partition_of(desc, p, max_len);
+    const Partition pt = partition_of(desc, p, max_len, append);
+    // appending: stored lengths from the split kernel's copy, new lengths written to lens
+    const int32_t *lsrc = append ? reinterpret_cast<const int32_t *>(ws + p.lens_off) : lens;
+    int32_t *lupd = append ? lens : nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (desc->d_v == 64)
-        hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineBlock), 0, st, lens, ml, po, out, err,
+        hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, ml, po, out, err,
                            desc->h_q, p.gt, pt, skip_single);
     else
-        hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, st, lens, ml, po, out, err,
+        hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, ml, po, out, err,
                            desc->h_q, p.gt, pt, skip_single);
     return launch_status("lse_combine_kernel");
 }
@@ -1714,23 +1638,50 @@ int kv_append(const da_desc *desc, void *k_cache, void *v_cache, int32_t *lens, 
 int decode_attn_partial(const da_desc *desc, const void *q, const void *k_cache, const void *v_cache,
                         const int32_t *lens, int32_t max_len, const float *kv_scales, void *workspace,
                         size_t ws_bytes, void *stream) {
-    return run_split(desc, q, k_cache, v_cache, lens, max_len, kv_scales, nullptr, workspace, ws_bytes, stream,
-                     "decode_attn_partial");
+    return run_split(desc, q, k_cache, v_cache, lens, nullptr, nullptr, max_len, kv_scales, nullptr, workspace,
+                     ws_bytes, stream, "decode_attn_partial");
 }
 
 int decode_attn_combine(const da_desc *desc, const int32_t *lens, int32_t max_len, float *out, void *workspace,
                         size_t ws_bytes, void *stream) {
-    return run_combine(desc, lens, max_len, out, workspace, ws_bytes, stream, 0, "decode_attn_combine");
+    return run_combine(desc, const_cast<int32_t *>(lens), max_len, out, workspace, ws_bytes, stream, 0, false,
+                       "decode_attn_combine");
 }
 
 int decode_attn_run(const da_desc *desc, const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *lens, int32_t max_len, const float *kv_scales, float *out, void *workspace,
                     size_t ws_bytes, void *stream) {
     if (!out) return fail(DA_ERR_INVALID_ARG, "decode_attn_run: out is NULL");
-    const int rc = run_split(desc, q, k_cache, v_cache, lens, max_len, kv_scales, out, workspace, ws_bytes, stream,
-                             "decode_attn_run");
+    const int rc = run_split(desc, q, k_cache, v_cache, lens, nullptr, nullptr, max_len, kv_scales, out, workspace,
+                             ws_bytes, stream, "decode_attn_run");
     if (rc) return rc;
-    return run_combine(desc, lens, max_len, out, workspace, ws_bytes, stream, 1, "decode_attn_run");
+    return run_combine(desc, const_cast<int32_t *>(lens), max_len, out, workspace, ws_bytes, stream, 1, false,
+                       "decode_attn_run");
+}
+
+int decode_attn_append_partial(const da_desc *desc, const void *q, void *k_cache, void *v_cache,
+                               const int32_t *lens, const void *k_new, const void *v_new, int32_t max_len,
+                               const float *kv_scales, void *workspace, size_t ws_bytes, void *stream) {
+    if (!k_new || !v_new) return fail(DA_ERR_INVALID_ARG, "decode_attn_append_partial: k_new or v_new is NULL");
+    return run_split(desc, q, k_cache, v_cache, lens, k_new, v_new, max_len, kv_scales, nullptr, workspace,
+                     ws_bytes, stream, "decode_attn_append_partial");
+}
+
+int decode_attn_append_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out, void *workspace,
+                               size_t ws_bytes, void *stream) {
+    return run_combine(desc, lens, max_len, out, workspace, ws_bytes, stream, 0, true,
+                       "decode_attn_append_combine");
+}
+
+int decode_attn_append_run(const da_desc *desc, const void *q, void *k_cache, void *v_cache, int32_t *lens,
+                           const void *k_new, const void *v_new, int32_t max_len, const float *kv_scales,
+                           float *out, void *workspace, size_t ws_bytes, void *stream) {
+    if (!out) return fail(DA_ERR_INVALID_ARG, "decode_attn_append_run: out is NULL");
+    if (!k_new || !v_new) return fail(DA_ERR_INVALID_ARG, "decode_attn_append_run: k_new or v_new is NULL");
+    const int rc = run_split(desc, q, k_cache, v_cache, lens, k_new, v_new, max_len, kv_scales, out, workspace,
+                             ws_bytes, stream, "decode_attn_append_run");
+    if (rc) return rc;
+    return run_combine(desc, lens, max_len, out, workspace, ws_bytes, stream, 1, true, "decode_attn_append_run");
 }
 
 int da_read_device_error(const void *workspace, void *stream, int32_t *code) {

@@ -146,6 +146,42 @@ int decode_attn_partial(const da_desc *desc, const void *q, const void *k_cache,
 int decode_attn_combine(const da_desc *desc, const int32_t *lens, int32_t max_len, float *out,
                         void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * One decode step with the append fused into the attention pass (page "MoA-Structured Decode
+ * Attention", §5 accumulation, then §2 Steps I-III): the same results, cache bytes, lengths
+ * and error bits as kv_append(k_new, v_new) followed by decode_attn_run, in two kernels
+ * instead of three. The split kernel attends over lens[b] + 1 rows (lens[b] rows for a
+ * sequence whose append is skipped because lens[b] is outside [0, cap); that raises
+ * DA_DEV_ERR_APPEND_FULL); each workgroup whose share ends at a sequence's new last row
+ * stores that row into the cache before reading it. The combine kernel then sets
+ * lens[b] += 1 for the appended sequences. max_len bounds the lengths after the append
+ * (lens[b] + 1 <= max_len <= cap). k_cache, v_cache and lens are written; k_new and v_new
+ * are [batch, h_kv, d] rows in the cache's type, fp8 rows quantised with their slot's scale.
+ * The workspace's error word must be the one the caller reads (it is not optional here).
+ */
+int decode_attn_append_run(const da_desc *desc, const void *q, void *k_cache, void *v_cache,
+                           int32_t *lens, const void *k_new, const void *v_new, int32_t max_len,
+                           const float *kv_scales, float *out, void *workspace, size_t ws_bytes,
+                           void *stream);
+
+/*
+ * First stage of decode_attn_append_run: stores the new rows where the attention pass reads
+ * them and writes the per-segment partial results, plus a copy of the stored lengths in the
+ * workspace. lens is read, not changed: decode_attn_append_combine, on the same workspace and
+ * stream, updates it.
+ */
+int decode_attn_append_partial(const da_desc *desc, const void *q, void *k_cache, void *v_cache,
+                               const int32_t *lens, const void *k_new, const void *v_new,
+                               int32_t max_len, const float *kv_scales, void *workspace,
+                               size_t ws_bytes, void *stream);
+
+/*
+ * Second stage of decode_attn_append_run: merges every (b, h) into out using the lengths
+ * copied by decode_attn_append_partial, then writes the new lengths to lens.
+ */
+int decode_attn_append_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
+                               void *workspace, size_t ws_bytes, void *stream);
+
 /* Waits for the stream, then copies the error word into *code (host). For tests and tools. */
 int da_read_device_error(const void *workspace, void *stream, int32_t *code);
 

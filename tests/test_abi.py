@@ -119,6 +119,19 @@ def test_null_and_misaligned_pointers_fail_before_launch(lib):
     assert lib.da_workspace_init(FAKE, 16, None) == -3
 
 
+def test_fused_append_needs_both_new_rows(lib):
+    d = _desc()
+    args = (ctypes.byref(d), FAKE, FAKE, FAKE, FAKE)
+    assert lib.decode_attn_append_run(*args, None, FAKE, 100, None, FAKE, FAKE, 1 << 30, None) == -1
+    assert lib.decode_attn_append_run(*args, FAKE, None, 100, None, FAKE, FAKE, 1 << 30, None) == -1
+    assert lib.decode_attn_append_run(*args, ctypes.c_void_p(0x10008), FAKE, 100, None, FAKE, FAKE,
+                                      1 << 30, None) == -1  # misaligned
+    assert lib.decode_attn_append_run(*args, FAKE, FAKE, 100, None, None, FAKE, 1 << 30, None) == -1  # no out
+    assert lib.decode_attn_append_partial(*args, FAKE, None, 100, None, FAKE, 1 << 30, None) == -1
+    rc, n = _ws_size(lib, d, 1000)
+    assert lib.decode_attn_append_combine(ctypes.byref(d), FAKE, 1000, FAKE, FAKE, n - 1, None) == -3
+
+
 def test_small_workspace_is_rejected(lib):
     d = _desc()
     rc, n = _ws_size(lib, d, 1000)

@@ -200,8 +200,8 @@ def test_two_stage_path_matches_fused_run():
 
 
 def test_workspace_reuse_across_calls():
-    """The fused merge's arrival counters return to zero after every call: one workspace
-    serves a sequence of calls with different lengths (single- and multi-split sequences)."""
+    """One workspace serves a sequence of calls with different lengths (single- and
+    multi-split sequences): nothing from an earlier call leaks into a later one."""
     w = W(B=5, h_q=8, h_kv=2, cap=2000, lens=("const", 2000), seed=47)
     c = workloads.generate(w)
     desc = desc_of(w, 256)
