@@ -1,21 +1,24 @@
 #!/usr/bin/env python3
 """Decode-attention benchmark on one MI355X: µs per decode step and achieved HBM GB/s.
 
-A step is one pass of the whole hot path over the workload's batch: for a workload
-that appends (the grouped-query one does), the lengths are reset to their pre-append
-values and one K/V row per (sequence, KV head) is appended; then decode_attn_run runs
-the split-KV attention kernel and the log-sum-exp combine. Inputs are seeded synthetic
-tensors (workloads.py) already resident in HBM when timing starts; R rotating
-copies of the cache (R * cache bytes >= 2 GiB) keep the 256 MB Infinity Cache from
-serving one step's reads out of the previous step's.
+A step is one pass of the whole hot path over the workload's batch. For a workload that
+appends (the grouped-query one does) it is one decode step, decode_attn_append_run: one
+K/V row per (sequence, KV head) is appended and attention runs over the grown cache, the
+split-KV attention kernel (which stores the new rows) then the log-sum-exp combine (which
+updates the lengths). As in a decode loop the sequences grow by one row per step of their
+cache copy, and the bytes of every step are counted at its own lengths. A workload without
+an append runs decode_attn_run. Inputs are seeded synthetic tensors (workloads.py) already
+resident in HBM when timing starts; R rotating copies of the cache (R * cache bytes >=
+2 GiB) keep the 256 MB Infinity Cache from serving one step's reads out of the previous
+step's.
 
 Prints ONE JSON line:
   value       = KV-cache bytes per step / wall-clock time per step   (GB/s, 1e9 B/s)
   ms_per_step = wall-clock per step over the timed region, bracketed by synchronisation
   roofline    = the split-KV attention kernel, timed with HIP events around it on the
-                stream it runs on (the timed steps call decode_attn_run in its two-stage
-                form, decode_attn_partial then decode_attn_combine, with the events around
-                the first):
+                stream it runs on (the timed steps call the step in its two-stage form,
+                the partial then the combine entry point, with the events around the
+                first):
                 algorithmic bytes per launch (the KV rows of every sequence plus q) / mean
                 launch duration, against the 8 TB/s HBM3E peak; `traffic` is
                 the HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, read
@@ -52,6 +55,8 @@ def parse_args():
                    help="override: every sequence this long (the 8K/16K/32K sweep)")
     p.add_argument("--block-rows", type=int, default=0, help="rows per split (0 = library choice)")
     p.add_argument("--rotations", type=int, default=0, help="cache copies to rotate (0 = auto)")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the step replayed from a captured HIP graph (one step per cache copy)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle timing budget")
     p.add_argument("--copy-calibration", action="store_true",
@@ -111,49 +116,64 @@ def main() -> int:
         w = w.resized(lens=("const", args.const_len), cap=max(w.cap, args.const_len))
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    t_gen = time.perf_counter()
     c = workloads.generate(w, poison=False)
-    t_gen = time.perf_counter() - t_gen
     lens_final = c["lens_final"]
-    max_len = int(lens_final.max())
     esz = workloads.ELEM_BYTES[w.kv_dtype]
-    kv_bytes = int(lens_final.to(torch.int64).sum()) * w.h_kv * 2 * w.d * esz
+    row_bytes = w.h_kv * 2 * w.d * esz  # K and V bytes of one row of every KV head
     q_bytes = w.B * w.h_q * w.d * workloads.ELEM_BYTES[w.q_dtype]
     cache_bytes = 2 * c["k_cache"].numel() * esz
-    R = args.rotations or max(2, min(8, math.ceil((2 << 30) / max(kv_bytes, 1))))
+    appends = w.steps > 0
+    # use u of a cache copy (u = step // R) attends over lens_init + 1 + u rows when appending
+    lens_first = (c["lens_init"] + 1 if appends else lens_final).to(torch.int64)
+    kv_bytes0 = int(lens_first.sum()) * row_bytes
+    R = args.rotations or max(2, min(8, math.ceil((2 << 30) / max(kv_bytes0, 1))))
+    graph_reps = max(1, args.steps // R) if args.graph else 0
+    uses = -(-(args.warmup + args.steps) // R) + graph_reps
+    max_len = int(lens_first.max()) + (uses - 1 if appends else 0)
+    if max_len > w.cap:
+        print(f"bench.py: {uses} appends per cache copy overflow cap {w.cap}; use fewer steps",
+              file=sys.stderr)
+        return 2
+
+    def step_kv_bytes(i):
+        return kv_bytes0 + (w.B * (i // R) * row_bytes if appends else 0)
 
     desc = da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, workloads.TORCH_DTYPE[w.q_dtype],
                    workloads.TORCH_DTYPE[w.kv_dtype], w.scale, args.block_rows)
     plan = da.da_plan(desc, max_len)
     q = c["q"].to(dev)
     scales = c["kv_scales"].to(dev) if c["kv_scales"] is not None else None
-    lens_init = c["lens_init"].to(dev)
-    k_new = c["k_new"][0].contiguous().to(dev) if w.steps else None
-    v_new = c["v_new"][0].contiguous().to(dev) if w.steps else None
+    lens_init = c["lens_init"].to(dev) if appends else lens_final.to(dev)
+    k_new = c["k_new"][0].contiguous().to(dev) if appends else None
+    v_new = c["v_new"][0].contiguous().to(dev) if appends else None
     slots = []
     k0, v0 = c["k_cache"].to(dev), c["v_cache"].to(dev)
     del c
     for r in range(R):
         kc = k0 if r == 0 else k0.clone()
         vc = v0 if r == 0 else v0.clone()
-        slots.append((kc, vc, (lens_init if not w.steps else lens_init.clone())))
-    if w.steps == 0:
-        slots = [(kc, vc, lens_init) for kc, vc, _ in slots]
+        slots.append((kc, vc, lens_init.clone() if appends else lens_init))
     ws = da.Workspace(desc, max_len, device=dev)
     out = torch.empty(w.B, w.h_q, w.d, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(i, ev=None):
         kc, vc, lens = slots[i % R]
-        if w.steps:
-            lens.copy_(lens_init)
-            da.kv_append(desc, kc, vc, lens, k_new, v_new, ws)
         if ev is None:
-            da.decode_attn_run(desc, q, kc, vc, lens, max_len, scales, out, ws)
+            if appends:
+                da.decode_attn_append_run(desc, q, kc, vc, lens, k_new, v_new, max_len, scales, out, ws)
+            else:
+                da.decode_attn_run(desc, q, kc, vc, lens, max_len, scales, out, ws)
+            return
+        ev[0].record(stream)
+        if appends:
+            da.decode_attn_append_partial(desc, q, kc, vc, lens, k_new, v_new, max_len, scales, ws)
         else:
-            ev[0].record(stream)
             da.decode_attn_partial(desc, q, kc, vc, lens, max_len, scales, ws)
-            ev[1].record(stream)
+        ev[1].record(stream)
+        if appends:
+            da.decode_attn_append_combine(desc, lens, max_len, out, ws)
+        else:
             da.decode_attn_combine(desc, lens, max_len, out, ws)
 
     for i in range(args.warmup):
@@ -172,7 +192,37 @@ def main() -> int:
     end.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    assert da.da_read_device_error(ws) == 0, "device error flagged during the timed steps"
 
+    graph = None
+    if args.graph:
+        # one step per cache copy captured on a side stream, replayed graph_reps times; the
+        # lengths live on the device, so every replay appends and attends one row further
+        base = args.warmup + args.steps
+        base += (-base) % R  # the next step of copy 0
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for r in range(R):
+                    step(base + r)
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(graph_reps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        assert da.da_read_device_error(ws) == 0, "device error flagged during the graph replays"
+        n = graph_reps * R
+        g_ms = g0.elapsed_time(g1) / n
+        g_bytes = sum(step_kv_bytes(base + i) for i in range(n)) / n
+        graph = {"us_per_step": round(g_ms * 1e3, 2), "GBs": round(g_bytes / (g_ms * 1e-3) / 1e9, 2),
+                 "steps": n, "launch": "HIP graph of one step per cache copy, replayed"}
+
+    timed = range(args.warmup, args.warmup + args.steps)
+    kv_bytes = sum(step_kv_bytes(i) for i in timed) / args.steps  # mean over the timed steps
     wall_ms = (t1 - t0) * 1e3 / args.steps
     gpu_ms = start.elapsed_time(end) / args.steps
     split_ms = [a.elapsed_time(b) for a, b in evs]
@@ -202,10 +252,10 @@ def main() -> int:
         "config": {
             "workload": w.name, "batch": w.B, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
             "cap": w.cap, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype,
-            "lens": (f"const {max_len}" if w.lens[0] == "const"
+            "lens": (f"const {int(lens_final.max())}" if w.lens[0] == "const"
                      else f"uniform[{w.lens[1]},{w.lens[2]}] seed {w.seed}"),
-            "sum_lens": int(lens_final.sum()), "max_len": max_len,
-            "appends_per_step": int(w.steps > 0), "kv_bytes_per_step": kv_bytes,
+            "sum_lens_first_step": int(lens_first.sum()), "max_len": max_len,
+            "appends_per_step": int(appends), "kv_bytes_per_step": round(kv_bytes),
             "rotations": R, "cache_bytes_per_copy": cache_bytes, **plan,
         },
         "roofline": {
@@ -216,15 +266,17 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": algo_bytes,
+            "algorithmic_bytes_per_launch": round(algo_bytes),
             "launch_us_mean": round(split_ms_mean * 1e3, 2),
             "launch_us_p10": round(split_sorted[len(split_sorted) // 10] * 1e3, 2),
             "launch_us_p90": round(split_sorted[(9 * len(split_sorted)) // 10] * 1e3, 2),
         },
         "cpu_baseline": None,
     }
+    if graph is not None:
+        result["graph_replay"] = graph
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, kv_bytes)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, kv_bytes0)
     print(json.dumps(result), flush=True)
     return 0
 

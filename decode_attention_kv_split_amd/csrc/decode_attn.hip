@@ -1216,7 +1216,7 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     const int32_t *__restrict__ lens, int32_t *__restrict__ lens_upd, const float *__restrict__ part_ml,
     const float *__restrict__ part_o, float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt,
     Partition pt, int skip_single) {
-    constexpr int SG = kCombineBlock / D;  // segment groups working side by side
+    constexpr int SG = kCombineBlock / (D / 4);  // segment groups working side by side
     const int bh = blockIdx.x;
     const int b = bh / h_q, h = bh % h_q;
     const int L = attended_len(lens[b], pt.append_cap);
@@ -1258,7 +1258,8 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     if (skip_single && wa == wb) return;
 
     __shared__ float red[kCombineBlock / kWave];
-    __shared__ float s_acc[SG][D], s_l[SG][D];
+    __shared__ float4 s_acc[SG][D / 4];
+    __shared__ float s_l[SG];
     float M = kNegBig;
     for (int64_t w = wa + threadIdx.x; w <= wb; w += kCombineBlock)
         if (wg_start(w, total, N) < wg_start(w + 1, total, N)) M = fmaxf(M, part_ml[((w + u) * gt + hh) * 2]);
@@ -1270,23 +1271,53 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
 #pragma unroll
     for (int w = 1; w < kCombineBlock / kWave; ++w) M = fmaxf(M, red[w]);
 
-    const int d = threadIdx.x % D, sg = threadIdx.x / D;
-    float acc = 0.f, ls = 0.f;
-    for (int64_t w = wa + sg; w <= wb; w += SG) {
-        if (wg_start(w, total, N) == wg_start(w + 1, total, N)) continue;  // empty workgroup
-        const size_t kk = (size_t)(w + u) * gt + hh;
-        const float f = __builtin_amdgcn_exp2f(part_ml[kk * 2] - M);
-        ls = fmaf(part_ml[kk * 2 + 1], f, ls);
-        acc = fmaf(part_o[kk * D + d], f, acc);
+    // SG segment groups side by side, D/4 threads each holding 4 output columns; every
+    // iteration issues the loads of UN segments before using any of them.
+    constexpr int UN = 4;
+    const int c4 = threadIdx.x % (D / 4), sg = threadIdx.x / (D / 4);
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    float ls = 0.f;
+    for (int64_t w0 = wa + sg; w0 <= wb; w0 += SG * UN) {
+        float mj[UN], lj[UN];
+        float4 oj[UN];
+#pragma unroll
+        for (int j = 0; j < UN; ++j) {
+            const int64_t w = w0 + j * SG;
+            mj[j] = -INFINITY;  // an empty or absent segment weighs 0
+            lj[j] = 0.f;
+            oj[j] = float4{0.f, 0.f, 0.f, 0.f};
+            if (w <= wb && wg_start(w, total, N) < wg_start(w + 1, total, N)) {
+                const size_t kk = (size_t)(w + u) * gt + hh;
+                mj[j] = part_ml[kk * 2];
+                lj[j] = part_ml[kk * 2 + 1];
+                oj[j] = reinterpret_cast<const float4 *>(part_o + kk * D)[c4];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < UN; ++j) {
+            const float f = __builtin_amdgcn_exp2f(mj[j] - M);
+            ls = fmaf(lj[j], f, ls);
+            acc.x = fmaf(oj[j].x, f, acc.x);
+            acc.y = fmaf(oj[j].y, f, acc.y);
+            acc.z = fmaf(oj[j].z, f, acc.z);
+            acc.w = fmaf(oj[j].w, f, acc.w);
+        }
     }
-    s_acc[sg][d] = acc;
-    s_l[sg][d] = ls;
+    s_acc[sg][c4] = acc;
+    if (c4 == 0) s_l[sg] = ls;
     __syncthreads();
     if (sg == 0) {
-        float x = s_acc[0][d], z = s_l[0][d];
+        float4 x = s_acc[0][c4];
+        float z = s_l[0];
 #pragma unroll
-        for (int i = 1; i < SG; ++i) { x += s_acc[i][d]; z += s_l[i][d]; }
-        dst[d] = x / z;
+        for (int i = 1; i < SG; ++i) {
+            x.x += s_acc[i][c4].x;
+            x.y += s_acc[i][c4].y;
+            x.z += s_acc[i][c4].z;
+            x.w += s_acc[i][c4].w;
+            z += s_l[i];
+        }
+        reinterpret_cast<float4 *>(dst)[c4] = float4{x.x / z, x.y / z, x.z / z, x.w / z};
     }
 }
 
