@@ -85,6 +85,13 @@ def profiled_traffic(workload: str):
     return float(kv["hbm_bytes_per_launch"])
 
 
+def split_kernel_name(w) -> str:
+    """The split kernel the library launches for this workload: query groups that are a
+    multiple of 4 over a bf16 / fp8 cache run on the matrix cores."""
+    mfma = w.kv_dtype != "f32" and (w.h_q // w.h_kv) % 4 == 0
+    return "split_kv_attn_mfma_kernel" if mfma else "split_kv_attn_kernel"
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -259,7 +266,7 @@ def main() -> int:
             "rotations": R, "cache_bytes_per_copy": cache_bytes, **plan,
         },
         "roofline": {
-            "kernel": "split_kv_attn_kernel",
+            "kernel": split_kernel_name(w),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
