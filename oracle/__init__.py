@@ -10,7 +10,8 @@ arrays into it and builds it with gcc when the shared object is missing.
 decimal arithmetic used to pin the C code on tiny inputs.
 
 Element type codes: 0 = fp32, 1 = bf16 (raw uint16 bits), 2 = fp8 e4m3fn
-(raw uint8 codes).
+(raw uint8 codes), 3 = int8 (two's-complement codes); fp8 and int8 values are
+code times the slot's scale.
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ import subprocess
 
 import numpy as np
 
-F32, BF16, FP8_E4M3FN = 0, 1, 2
+F32, BF16, FP8_E4M3FN, INT8 = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -46,6 +47,8 @@ def _open(path: str):
     lib.oracle_bf16_to_f64.restype = D
     lib.oracle_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3fn_to_f64.restype = D
+    lib.oracle_int8_to_f64.argtypes = [ctypes.c_int8]
+    lib.oracle_int8_to_f64.restype = D
     lib.oracle_head_f64.argtypes = [I, I, I, D, P, P, P, P, P, P, P, P, P]
     lib.oracle_head_f64.restype = I
     lib.oracle_decode_f64_traced.argtypes = [I] * 8 + [F] + [P] * 6 + [I] + [P] * 3
@@ -92,7 +95,7 @@ def _np(x):
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8).numpy()
-    return t.numpy()
+    return t.numpy()  # fp32, int8 (two's-complement codes), int32
 
 
 def _dtype_code(a: np.ndarray) -> int:
@@ -102,6 +105,8 @@ def _dtype_code(a: np.ndarray) -> int:
         return BF16
     if a.dtype == np.uint8:
         return FP8_E4M3FN
+    if a.dtype == np.int8:
+        return INT8
     raise TypeError(f"unsupported element type {a.dtype}")
 
 
@@ -111,6 +116,10 @@ def bf16_to_f64(bits: int) -> float:
 
 def e4m3fn_to_f64(code: int) -> float:
     return _load().oracle_e4m3fn_to_f64(int(code))
+
+
+def int8_to_f64(code: int) -> float:
+    return _load().oracle_int8_to_f64(int(code))
 
 
 def head_f64(q, K, V, scale: float):
@@ -137,7 +146,7 @@ def decode_f64(q, k_cache, v_cache, lens, scale: float, kv_scales=None,
     """Batched GQA decode attention in fp64.
 
     q [B, h_q, d_k]; k_cache [B, h_kv, cap, d_k]; v_cache [B, h_kv, cap, d_v];
-    lens [B] int32 (rows attended); kv_scales [B, h_kv, 2] fp32 for fp8 caches.
+    lens [B] int32 (rows attended); kv_scales [B, h_kv, 2] fp32 for fp8 / int8 caches.
     Returns out [B, h_q, d_v] float64 (and the read maps when ``marks``).
     """
     q, k_cache, v_cache, lens, kv_scales = map(_np, (q, k_cache, v_cache, lens, kv_scales))

@@ -30,7 +30,12 @@
  * (OCP definition: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits,
  * subnormals at exponent 0, the two all-ones codes 0x7F / 0xFF are NaN, no
  * infinities). An fp8 element's value is decode(code) * scale, computed in
- * double, which is exact.
+ * double, which is exact. An int8 element is its two's-complement code, also
+ * times its slot's scale (symmetric 8-bit quantisation, the same per-(sequence,
+ * KV head, K or V) scale as fp8). The decode-attention roofline page names
+ * int8 and fp8 KV together as the lever that halves the bytes read per step
+ * (its flop/byte derivation: AI = 2g with one byte per element); it fixes no
+ * scale granularity, so both 8-bit types share the fp8 slots.
  */
 #include <math.h>
 #include <omp.h>
@@ -41,6 +46,7 @@
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
 #define ORACLE_FP8_E4M3FN 2
+#define ORACLE_INT8 3
 
 double oracle_bf16_to_f64(uint16_t bits) {
     uint32_t w = ((uint32_t)bits) << 16;
@@ -62,20 +68,27 @@ double oracle_e4m3fn_to_f64(uint8_t code) {
     return sign ? -v : v;
 }
 
+double oracle_int8_to_f64(int8_t code) { return (double)code; }
+
 static int elem_bytes(int dtype) {
     switch (dtype) {
     case ORACLE_F32: return 4;
     case ORACLE_BF16: return 2;
     case ORACLE_FP8_E4M3FN: return 1;
+    case ORACLE_INT8: return 1;
     default: return 0;
     }
 }
+
+/* Element types whose values carry a per-slot scale. */
+static int scaled(int dtype) { return dtype == ORACLE_FP8_E4M3FN || dtype == ORACLE_INT8; }
 
 /* Element idx of a flat array of the given dtype, widened to double. */
 static double load_elem(const void *base, int dtype, size_t idx) {
     switch (dtype) {
     case ORACLE_F32: return (double)((const float *)base)[idx];
     case ORACLE_BF16: return oracle_bf16_to_f64(((const uint16_t *)base)[idx]);
+    case ORACLE_INT8: return oracle_int8_to_f64(((const int8_t *)base)[idx]);
     default: return oracle_e4m3fn_to_f64(((const uint8_t *)base)[idx]);
     }
 }
@@ -130,7 +143,7 @@ int oracle_head_f64(int n, int d_k, int d_v, double scale, const double *q,
  *   k_cache  [B, h_kv, cap, d_k]      dtype kv_dtype
  *   v_cache  [B, h_kv, cap, d_v]      dtype kv_dtype
  *   lens     [B]                      rows attended per sequence (1..cap)
- *   kv_scales[B, h_kv, 2] fp32        (K scale, V scale); only for fp8, else NULL
+ *   kv_scales[B, h_kv, 2] fp32        (K scale, V scale); only for fp8 / int8, else NULL
  *   out      [B, h_q, d_v]  double
  * The optional byte maps q_mark / k_mark / v_mark (one byte per element of
  * q, k_cache, v_cache) are set to 1 for every element the loops read; with
@@ -146,7 +159,7 @@ int oracle_decode_f64_traced(int B, int h_q, int h_kv, int d_k, int d_v,
     if (B < 0 || h_q < 1 || h_kv < 1 || h_q % h_kv || d_k < 1 || d_v < 1 || cap < 1)
         return -1;
     if (!elem_bytes(q_dtype) || !elem_bytes(kv_dtype)) return -1;
-    if (kv_dtype == ORACLE_FP8_E4M3FN && !kv_scales) return -1;
+    if (scaled(kv_dtype) && !kv_scales) return -1;
     for (int b = 0; b < B; ++b)
         if (lens[b] < 1 || lens[b] > cap) return -3;
     const int g = h_q / h_kv;
@@ -160,7 +173,7 @@ int oracle_decode_f64_traced(int B, int h_q, int h_kv, int d_k, int d_v,
         const int n = lens[b];
         const size_t slot = (size_t)b * h_kv + kvh;
         double ks = 1.0, vs = 1.0;
-        if (kv_dtype == ORACLE_FP8_E4M3FN) {
+        if (scaled(kv_dtype)) {
             ks = (double)kv_scales[slot * 2 + 0];
             vs = (double)kv_scales[slot * 2 + 1];
         }

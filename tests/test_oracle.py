@@ -68,14 +68,14 @@ def _widen(x: torch.Tensor, scales=None, which=None) -> np.ndarray:
 
 
 @pytest.mark.parametrize("seed", range(6))
-@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8", "int8"])
 def test_oracle_vs_decimal_brute_force(seed, kv):
     """Tiny random cases (GQA, ragged n <= 8, d <= 4) against 50-digit arithmetic."""
     rng = np.random.default_rng(100 * seed + len(kv))
     h_kv = int(rng.integers(1, 3))
     g = int(rng.integers(1, 3))
     B, d, cap = 2, int(rng.integers(1, 5)), 8
-    w = workloads.Workload("tiny", B, h_kv * g, h_kv, d, cap, "bf16" if kv == "fp8" else kv, kv,
+    w = workloads.Workload("tiny", B, h_kv * g, h_kv, d, cap, "bf16" if kv in workloads.SCALED else kv, kv,
                            ("uniform", 1, cap), 0, 1000 + seed, 0.5 + seed / 7)
     c = workloads.generate(w, poison=False)
     got = oracle.decode_f64(c["q"], c["k_cache"], c["v_cache"], c["lens_final"], w.scale,
@@ -91,7 +91,7 @@ def test_oracle_vs_decimal_brute_force(seed, kv):
 # ---------------------------------------------------------------- SDPA (the page's ground truth)
 @pytest.mark.parametrize("name,h_q,h_kv,d,kv", [
     ("mha", 4, 4, 64, "bf16"), ("gqa4", 8, 2, 128, "bf16"), ("mqa", 8, 1, 64, "f32"),
-    ("fp8", 8, 2, 128, "fp8")])
+    ("fp8", 8, 2, 128, "fp8"), ("int8", 8, 1, 128, "int8")])
 def test_oracle_vs_torch_sdpa_fp64(name, h_q, h_kv, d, kv):
     """torch SDPA in fp64 on the CPU, per sequence, with (B, H, S, D) wrapping and
     GQA by repeat_interleave (page "MoA-Structured Decode Attention", SDPA as ground truth)."""
@@ -248,13 +248,13 @@ def test_append_is_bit_exact_and_touches_only_its_rows():
     assert np.array_equal(kc, exp_k) and np.array_equal(vc, exp_v)
 
 
-@pytest.mark.parametrize("h_q,h_kv,kv", [(1, 1, "f32"), (8, 2, "bf16"), (4, 1, "fp8")])
+@pytest.mark.parametrize("h_q,h_kv,kv", [(1, 1, "f32"), (8, 2, "bf16"), (4, 1, "fp8"), (1, 1, "int8")])
 def test_traffic_formula_by_counting_reads(h_q, h_kv, kv):
     """I6 (page "MoA-Structured Decode Attention", §2 memory traffic
     (d_k + n d_k + n d_v + d_v) x bytes; §6 traffic falls by h_q / h_kv): the distinct
     elements the oracle's loops read are exactly q, and the first n rows of K and V of
     each selected group, once."""
-    w = workloads.Workload("tr", 2, h_q, h_kv, 8, 30, "bf16" if kv == "fp8" else kv, kv,
+    w = workloads.Workload("tr", 2, h_q, h_kv, 8, 30, "bf16" if kv in workloads.SCALED else kv, kv,
                            ("uniform", 1, 30), 0, 3, 0.3)
     c = workloads.generate(w)
     out, (qm, km, vm) = oracle.decode_f64(c["q"], c["k_cache"], c["v_cache"], c["lens_final"],
@@ -283,6 +283,16 @@ def test_fp8_e4m3fn_decoder_all_codes():
     ok = ~np.isnan(ref)
     assert np.array_equal(got[ok], ref[ok])
     assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_int8_decoder_all_codes():
+    """The oracle's int8 decoder is the two's-complement value of the byte, for all 256 codes
+    (torch's integer cast as the independent check)."""
+    codes = torch.arange(-128, 128, dtype=torch.int32).to(torch.int8)
+    ref = codes.to(torch.float64).numpy()
+    got = np.array([oracle.int8_to_f64(c) for c in range(-128, 128)])
+    assert np.array_equal(got, ref)
+    assert got[0] == -128.0 and got[-1] == 127.0 and got[128] == 0.0
 
 
 def test_bf16_decoder_all_codes():

@@ -2,8 +2,8 @@
 
 Each case plants one mistake in a private copy of ``oracle/oracle.c`` (a
 dropped term, a wrong sign, index or group map, a transposed operand, a
-doubled scale, a wrong dequantisation scale, a decoder off by one, a missing
-length update), builds it with gcc in a temporary directory, routes the
+doubled scale, a wrong dequantisation scale, a decoder off by one, int8
+codes read as unsigned bytes, a missing length update), builds it with gcc in a temporary directory, routes the
 oracle wrapper to it and runs the pin tests of ``test_oracle.py``. At least
 one pin must fail for every mutant; the unmutated copy must pass them all.
 Everything runs on the CPU.
@@ -27,6 +27,8 @@ MUTANTS = {
                                    "for (int l = 1; l < n; ++l) acc += a[l] * V"),
     "v_uses_k_scale": ("load_elem(v_cache, kv_dtype, idx) * vs;", "load_elem(v_cache, kv_dtype, idx) * ks;"),
     "fp8_bias_8": ("v = ldexp(1.0 + mant / 8.0, expo - 7);", "v = ldexp(1.0 + mant / 8.0, expo - 8);"),
+    "int8_read_unsigned": ("case ORACLE_INT8: return oracle_int8_to_f64(((const int8_t *)base)[idx]);",
+                           "case ORACLE_INT8: return (double)((const uint8_t *)base)[idx];"),
     "append_no_len_update": ("lens[b] += 1;", "lens[b] += 0;"),
     "append_wrong_row": ("(slot * cap + (size_t)lens[b]) * d_k * eb", "(slot * cap + (size_t)lens[b] / 2) * d_k * eb"),
     # a rewrite that changes nothing: the control that must pass every pin
@@ -39,6 +41,7 @@ PINS = [
     ("closed_form", lambda gd: pins.test_worked_example_closed_form(gd)),
     ("brute_f32", lambda gd: [pins.test_oracle_vs_decimal_brute_force(s, "f32") for s in range(6)]),
     ("brute_fp8", lambda gd: [pins.test_oracle_vs_decimal_brute_force(s, "fp8") for s in range(3)]),
+    ("brute_int8", lambda gd: [pins.test_oracle_vs_decimal_brute_force(s, "int8") for s in range(3)]),
     ("sdpa_gqa", lambda gd: pins.test_oracle_vs_torch_sdpa_fp64("gqa4", 8, 2, 128, "bf16")),
     ("special_cases", lambda gd: pins.test_special_cases_reduce_to_rows_or_mean()),
     ("fp8_codes", lambda gd: pins.test_fp8_e4m3fn_decoder_all_codes()),

@@ -14,12 +14,15 @@ Values are then rounded to the storage type: bf16 with round-to-nearest-even
 (``Tensor.to``); fp8 e4m3fn per (sequence, KV head, K or V) slot with scale
 amax / 448 over the slot's rows (scale 1 when amax is 0), codes
 clamp(x / scale, -448, 448) rounded to nearest even. The clamp matters: an
-unclamped cast sends values above 448 to NaN.
+unclamped cast sends values above 448 to NaN. int8 is the symmetric 8-bit
+counterpart with the same slots: scale amax / 127, codes
+clamp(round-to-nearest-even(x / scale), -127, 127).
 
 Of the L_b drawn rows, the first ``L_b - steps`` are in the cache at the
 start and the rest are the rows that ``steps`` successive appends add. Rows
 of the cache at or after the current length are filled with NaN ("poison"),
-so any read past a sequence's end shows up in the output.
+so any read past a sequence's end shows up in the output (int8 has no NaN:
+its poison is the largest code, 127, which shifts the output instead).
 
 Workloads follow the decode-attention shapes the pages discuss: the
 single-head worked setting of page "MoA-Structured Decode Attention", the
@@ -36,6 +39,7 @@ from dataclasses import dataclass
 import torch
 
 FP8_MAX = 448.0
+INT8_MAX = 127.0
 
 
 @dataclass(frozen=True)
@@ -47,7 +51,7 @@ class Workload:
     d: int
     cap: int            # cache rows per (sequence, KV head)
     q_dtype: str        # "f32" | "bf16"
-    kv_dtype: str       # "f32" | "bf16" | "fp8"
+    kv_dtype: str       # "f32" | "bf16" | "fp8" | "int8"
     lens: tuple         # ("const", L) or ("uniform", lo, hi) inclusive: final attended lengths
     steps: int          # appends performed (the last `steps` drawn rows of each sequence)
     seed: int
@@ -81,12 +85,17 @@ WORKLOADS = {
     # GQA 64q/8kv (Llama-2-70B shape), fp8 e4m3fn KV with per-slot scales
     "gqa8_fp8": Workload("gqa8_fp8", 32, 64, 8, 128, 16384, "bf16", "fp8",
                          ("const", 16384), 0, 5, _inv_sqrt(128)),
+    # the same shape with symmetric int8 KV and per-slot scales
+    "gqa8_int8": Workload("gqa8_int8", 32, 64, 8, 128, 16384, "bf16", "int8",
+                          ("const", 16384), 0, 6, _inv_sqrt(128)),
 }
 
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
-ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn,
+               "int8": torch.int8}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}
 POISON_BITS = {"f32": (torch.int32, 0x7FC00000), "bf16": (torch.int16, 0x7FC0),
-               "fp8": (torch.uint8, 0x7F)}
+               "fp8": (torch.uint8, 0x7F), "int8": (torch.int8, 127)}
+SCALED = ("fp8", "int8")  # cache types whose values are code x per-slot scale
 
 
 def _poisoned(shape, kind: str) -> torch.Tensor:
@@ -99,6 +108,14 @@ def quantize_e4m3fn(x: torch.Tensor):
     amax = x.abs().amax(dim=(1, 2))
     scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax)).to(torch.float32)
     codes = (x / scale[:, None, None]).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    return codes, scale
+
+
+def quantize_int8(x: torch.Tensor):
+    """Per-slot symmetric int8 codes and scale for x [h_kv, L, d] (fp32)."""
+    amax = x.abs().amax(dim=(1, 2))
+    scale = torch.where(amax > 0, amax / INT8_MAX, torch.ones_like(amax)).to(torch.float32)
+    codes = torch.round(x / scale[:, None, None]).clamp(-INT8_MAX, INT8_MAX).to(torch.int8)
     return codes, scale
 
 
@@ -120,7 +137,7 @@ def generate(w: Workload, seed: int | None = None, poison: bool = True) -> dict:
       lens_final [B] int32                   rows after `steps` appends
       k_new      [steps, B, h_kv, d]         rows appended at step t
       v_new      [steps, B, h_kv, d]
-      kv_scales  [B, h_kv, 2] fp32 (K, V)    fp8 only, else None
+      kv_scales  [B, h_kv, 2] fp32 (K, V)    fp8 / int8 only, else None
       scale      float (fp32 value)
     """
     gen = torch.Generator(device="cpu")
@@ -137,15 +154,16 @@ def generate(w: Workload, seed: int | None = None, poison: bool = True) -> dict:
         k_cache, v_cache = torch.zeros(shape, dtype=kv_t), torch.zeros(shape, dtype=kv_t)
     k_new = torch.zeros((w.steps, w.B, w.h_kv, w.d), dtype=kv_t)
     v_new = torch.zeros((w.steps, w.B, w.h_kv, w.d), dtype=kv_t)
-    kv_scales = torch.ones((w.B, w.h_kv, 2), dtype=torch.float32) if w.kv_dtype == "fp8" else None
+    kv_scales = torch.ones((w.B, w.h_kv, 2), dtype=torch.float32) if w.kv_dtype in SCALED else None
+    quantize = quantize_e4m3fn if w.kv_dtype == "fp8" else quantize_int8
     lens_init = lens - w.steps
     for b in range(w.B):
         L = int(lens[b])
         k = torch.randn(w.h_kv, L, w.d, generator=gen, dtype=torch.float32)
         v = torch.randn(w.h_kv, L, w.d, generator=gen, dtype=torch.float32)
-        if w.kv_dtype == "fp8":
-            k, ks = quantize_e4m3fn(k)
-            v, vs = quantize_e4m3fn(v)
+        if w.kv_dtype in SCALED:
+            k, ks = quantize(k)
+            v, vs = quantize(v)
             kv_scales[b, :, 0], kv_scales[b, :, 1] = ks, vs
         else:
             k, v = k.to(kv_t), v.to(kv_t)
