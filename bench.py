@@ -50,7 +50,7 @@ def parse_args():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="gqa8_bf16",
-                   help="single_head_f32 | mha_bf16 | gqa8_bf16 | mqa_bf16 | gqa8_fp8")
+                   help="single_head_f32 | mha_bf16 | gqa8_bf16 | mqa_bf16 | gqa8_fp8 | gqa8_int8")
     p.add_argument("--const-len", type=int, default=0,
                    help="override: every sequence this long (the 8K/16K/32K sweep)")
     p.add_argument("--block-rows", type=int, default=0, help="rows per split (0 = library choice)")
@@ -87,7 +87,7 @@ def profiled_traffic(workload: str):
 
 def split_kernel_name(w) -> str:
     """The split kernel the library launches for this workload: query groups that are a
-    multiple of 4 over a bf16 / fp8 cache run on the matrix cores."""
+    multiple of 4 over a bf16 / fp8 / int8 cache run on the matrix cores."""
     mfma = w.kv_dtype != "f32" and (w.h_q // w.h_kv) % 4 == 0
     return "split_kv_attn_mfma_kernel" if mfma else "split_kv_attn_kernel"
 

@@ -11,7 +11,7 @@ binding's functions fails.
 
 Layouts (the same as the C ABI):
   q [B, h_q, d] ; k_cache, v_cache [B, h_kv, cap, d] ; lens [B] int32 ;
-  k_new, v_new [B, h_kv, d] ; kv_scales [B, h_kv, 2] fp32 (fp8 only) ;
+  k_new, v_new [B, h_kv, d] ; kv_scales [B, h_kv, 2] fp32 (fp8 / int8 only) ;
   out [B, h_q, d] fp32.
 """
 from __future__ import annotations
@@ -23,20 +23,22 @@ from dataclasses import dataclass
 
 import torch
 
-from ._lib import DA_BF16, DA_F32, DA_FP8_E4M3FN, lib, library_path  # noqa: F401
+from ._lib import DA_BF16, DA_F32, DA_FP8_E4M3FN, DA_INT8, lib, library_path  # noqa: F401
 
 __all__ = [
     "Desc", "DecodeAttnError", "Workspace", "da_workspace_size", "da_plan", "da_workspace_init",
     "kv_append", "decode_attn_run", "decode_attn_partial", "decode_attn_combine",
     "decode_attn_append_run", "decode_attn_append_partial", "decode_attn_append_combine",
     "da_read_device_error", "da_status_string", "da_last_error", "library_path",
-    "DA_F32", "DA_BF16", "DA_FP8_E4M3FN", "DEV_ERR_APPEND_FULL", "DEV_ERR_LEN_RANGE",
+    "DA_F32", "DA_BF16", "DA_FP8_E4M3FN", "DA_INT8", "DEV_ERR_APPEND_FULL", "DEV_ERR_LEN_RANGE",
 ]
 
 DEV_ERR_APPEND_FULL = 1
 DEV_ERR_LEN_RANGE = 2
 
-_TORCH_CODE = {torch.float32: DA_F32, torch.bfloat16: DA_BF16, torch.float8_e4m3fn: DA_FP8_E4M3FN}
+_TORCH_CODE = {torch.float32: DA_F32, torch.bfloat16: DA_BF16, torch.float8_e4m3fn: DA_FP8_E4M3FN,
+               torch.int8: DA_INT8}
+_SCALED = (torch.float8_e4m3fn, torch.int8)  # caches of codes with per-slot scales
 
 
 class DecodeAttnError(RuntimeError):
@@ -169,7 +171,7 @@ def _attn_args(desc: Desc, q, k_cache, v_cache, lens, kv_scales):
     kc = _dev(k_cache, "k_cache", _cache_shapes(desc), desc.kv_dtype, dev)
     vc = _dev(v_cache, "v_cache", _cache_shapes(desc), desc.kv_dtype, dev)
     ln = _dev(lens, "lens", (desc.batch,), torch.int32, dev)
-    if desc.kv_dtype == torch.float8_e4m3fn:
+    if desc.kv_dtype in _SCALED:
         sc = _dev(kv_scales, "kv_scales", (desc.batch, desc.h_kv, 2), torch.float32, dev)
     else:
         sc = ctypes.c_void_p(None)

@@ -10,7 +10,7 @@ import os
 
 import torch  # noqa: F401  (load order: torch's HIP runtime first)
 
-DA_F32, DA_BF16, DA_FP8_E4M3FN = 0, 1, 2
+DA_F32, DA_BF16, DA_FP8_E4M3FN, DA_INT8 = 0, 1, 2, 3
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libdecode_attn.so")

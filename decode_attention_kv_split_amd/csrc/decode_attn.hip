@@ -56,6 +56,10 @@ template <int KV> struct Kv;
 template <> struct Kv<DA_F32> { static constexpr int kEsz = 4, kEpl = 4; using Vec = uint4; };
 template <> struct Kv<DA_BF16> { static constexpr int kEsz = 2, kEpl = 8; using Vec = uint4; };
 template <> struct Kv<DA_FP8_E4M3FN> { static constexpr int kEsz = 1, kEpl = 8; using Vec = uint2; };
+template <> struct Kv<DA_INT8> { static constexpr int kEsz = 1, kEpl = 8; using Vec = uint2; };
+
+// 8-bit caches hold codes; an element's value is code * its slot's scale.
+constexpr bool kv_scaled(int kv) { return kv == DA_FP8_E4M3FN || kv == DA_INT8; }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -69,6 +73,9 @@ __device__ __forceinline__ float e4m3fn_to_f32(uint32_t c) {
     return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
 }
 
+// int8 byte i of w -> fp32 (one v_cvt_f32_i32 with a sign-extended byte operand)
+__device__ __forceinline__ float i8_to_f32(uint32_t w, int i) { return (float)(int8_t)(w >> (8 * i)); }
+
 // Widen one lane's load into kEpl floats.
 template <int KV>
 __device__ __forceinline__ void widen(const typename Kv<KV>::Vec &v, float *f) {
@@ -79,6 +86,10 @@ __device__ __forceinline__ void widen(const typename Kv<KV>::Vec &v, float *f) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(w[i]); f[2 * i + 1] = bf16_hi(w[i]); }
+    } else if constexpr (KV == DA_INT8) {
+        const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = i8_to_f32(w[i / 4], i % 4);
     } else {
         const uint32_t w[2] = {v.x, v.y};
 #pragma unroll
@@ -241,7 +252,7 @@ __device__ void sequence_prefix(const int32_t *__restrict__ lens, const Partitio
 struct SplitArgs {
     const void *q, *kc, *vc;
     const int32_t *lens;
-    const float *kv_scales;   // [B, h_kv, 2] for fp8 caches, else unused
+    const float *kv_scales;   // [B, h_kv, 2] for fp8 / int8 caches, else unused
     float *part_ml, *part_o;  // per segment: [GT][2] (max, sum) and [GT][D] output rows
     float *out;               // decode_attn_run: output rows of units one workgroup covers
     int h_q, cap;
@@ -282,7 +293,7 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const char *>(a.vc) + slot * slot_bytes, r1 * ROWB);
     const uint32_t lane_off = grp * ROWB + sub * (uint32_t)sizeof(Vec);
     float vscale = 1.f, sc = a.qk_scale;
-    if constexpr (KV == DA_FP8_E4M3FN) {
+    if constexpr (kv_scaled(KV)) {
         sc *= a.kv_scales[slot * 2 + 0];
         vscale = a.kv_scales[slot * 2 + 1];
     }
@@ -478,11 +489,23 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
+// Two int8 codes (bytes 2*HI, 2*HI+1 of w) -> two bf16 packed in a word: each code is an
+// integer of at most 8 significant bits, so its fp32 value has zero low halves and the high
+// halves are the exact bf16 values.
+template <bool HI>
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w) {
+    const float lo = i8_to_f32(w, 2 * HI), hi = i8_to_f32(w, 2 * HI + 1);
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
 // Eight elements (one lane's load) as bf16x8.
 template <int KV>
 __device__ __forceinline__ uint4 to_bf16x8(const typename std::conditional<KV == DA_BF16, uint4, uint2>::type &v) {
     if constexpr (KV == DA_BF16) {
         return v;
+    } else if constexpr (KV == DA_INT8) {
+        return uint4{i8x2_to_bf16x2<false>(v.x), i8x2_to_bf16x2<true>(v.x), i8x2_to_bf16x2<false>(v.y),
+                     i8x2_to_bf16x2<true>(v.y)};
     } else {
         return uint4{fp8x2_to_bf16x2<false>(v.x), fp8x2_to_bf16x2<true>(v.x), fp8x2_to_bf16x2<false>(v.y),
                      fp8x2_to_bf16x2<true>(v.y)};
@@ -715,7 +738,7 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
     auto tile_row = [&](int t) { return t < nfull ? r0 + t * STEP + wq * TR : t < ntiles ? ts : r1; };
     auto tile_end = [&](int t) { return t < nfull ? r1 : te; };
     float vscale = 1.f, sc = a.qk_scale;
-    if constexpr (KV == DA_FP8_E4M3FN) {
+    if constexpr (kv_scaled(KV)) {
         sc *= a.kv_scales[slot * 2 + 0];
         vscale = a.kv_scales[slot * 2 + 1];
     }
@@ -774,7 +797,7 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
 
 // Matrix-core segment with workgroup-wide LDS stages filled by DMA (buffer_load ... lds), so
 // that no registers hold K or V in flight and 64 KiB per CU are outstanding.
-//   * A stage holds RS rows of K and V (16 KiB each: 64 bf16 or 128 fp8 rows of d = 128),
+//   * A stage holds RS rows of K and V (16 KiB each: 64 bf16 or 128 8-bit rows of d = 128),
 //     every 16-row tile chunk-major: 16-byte chunk c of row r at byte (c*16 + r)*16. One DMA
 //     instruction fills 1 KiB in lane order (lane i: chunk 4q + i/16, row i%16), so the K
 //     A operand of k block kb is one contiguous KiB and the V transpose reads of a d block a
@@ -782,15 +805,16 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
 //     arrays); all 256 threads fill each, and barriers mark a stage filled / consumed.
 //   * Each wave owns one 16-head tile (its own q operand, running max, sums and O) and a
 //     share of the stage's P.V blocks: 16-row blocks for bf16 (Step III by
-//     v_mfma_f32_16x16x16_bf16, V read by ds_read_b64_tr_b16), 32-row blocks for fp8 (Step III
-//     by v_mfma_f32_16x16x32_bf16 with P's 8 rows per lane taken from the block's two score
-//     tiles, V read as fp8 by ds_read_b64_tr_b8 and widened in registers). Step I always
-//     uses v_mfma_f32_16x16x32_bf16 (fp8 K widened to bf16 after its LDS read).
+//     v_mfma_f32_16x16x16_bf16, V read by ds_read_b64_tr_b16), 32-row blocks for 8-bit codes
+//     (fp8 or int8; Step III by v_mfma_f32_16x16x32_bf16 with P's 8 rows per lane taken from
+//     the block's two score tiles, V read as codes by ds_read_b64_tr_b8 and widened to bf16 in
+//     registers, exactly). Step I always uses v_mfma_f32_16x16x32_bf16 (8-bit K widened to bf16
+//     after its LDS read).
 //   * At the end the waves holding the same head tile merge through LDS.
 template <int KV, int D, int GT>
 __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
                                                       size_t k, bool direct) {
-    static_assert(KV == DA_BF16 || KV == DA_FP8_E4M3FN, "matrix-core flavour takes bf16 or fp8 caches");
+    static_assert(KV == DA_BF16 || Kv<KV>::kEsz == 1, "matrix-core flavour takes bf16 or 8-bit caches");
     constexpr int HT = (GT + 15) / 16;
     constexpr int KB = D / 32, NB = D / 16;
     constexpr int ESZ = Kv<KV>::kEsz;
@@ -823,7 +847,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const char *>(a.kc) + slot * slot_bytes, r1 * ROWB);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const char *>(a.vc) + slot * slot_bytes, r1 * ROWB);
     float vscale = 1.f, sc = a.qk_scale;
-    if constexpr (KV == DA_FP8_E4M3FN) {
+    if constexpr (kv_scaled(KV)) {
         sc *= a.kv_scales[slot * 2 + 0];
         vscale = a.kv_scales[slot * 2 + 1];
     }
@@ -1184,7 +1208,8 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a
     });
 }
 
-// Matrix-core flavour (GT in {4, 8, 16, 32}; bf16 or fp8 caches).
+// Matrix-core flavour (GT in {4, 8, 16, 32}; bf16, fp8 or int8 caches): bf16 streams through
+// the register ring, 8-bit caches through the LDS stages.
 // Register targets: GT = 32 keeps all of the register file (one wave per SIMD); smaller
 // groups are held to 256 registers so that two waves fit per SIMD.
 template <int GT>
@@ -1197,7 +1222,7 @@ constexpr int kMfmaRing = 2;
 template <int KV, int D, int GT, bool DIRECT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MfmaWaves<GT>::kMin)))
 void split_kv_attn_mfma_kernel(const SplitArgs a) {
-    if constexpr (KV == DA_FP8_E4M3FN) {
+    if constexpr (Kv<KV>::kEsz == 1) {
         walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole) {
             attend_segment_staged<KV, D, GT>(a, b, kvh, h0, r0, r1, k, DIRECT && whole);
         });
@@ -1336,7 +1361,9 @@ int fail(int code, const char *fmt, ...) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int elem_size(int dt) { return dt == DA_F32 ? 4 : dt == DA_BF16 ? 2 : dt == DA_FP8_E4M3FN ? 1 : 0; }
+int elem_size(int dt) {
+    return dt == DA_F32 ? 4 : dt == DA_BF16 ? 2 : (dt == DA_FP8_E4M3FN || dt == DA_INT8) ? 1 : 0;
+}
 
 int validate(const da_desc *d) {
     if (!d) return fail(DA_ERR_INVALID_ARG, "desc is NULL");
@@ -1355,7 +1382,8 @@ int validate(const da_desc *d) {
                     d->d_k, d->d_v);
     const bool ok = (d->q_dtype == DA_F32 && d->kv_dtype == DA_F32) ||
                     (d->q_dtype == DA_BF16 && d->kv_dtype == DA_BF16) ||
-                    (d->q_dtype == DA_BF16 && d->kv_dtype == DA_FP8_E4M3FN);
+                    (d->q_dtype == DA_BF16 && d->kv_dtype == DA_FP8_E4M3FN) ||
+                    (d->q_dtype == DA_BF16 && d->kv_dtype == DA_INT8);
     if (!ok) return fail(DA_ERR_UNSUPPORTED, "dtype pair (q %d, kv %d) is not built", d->q_dtype, d->kv_dtype);
     return DA_OK;
 }
@@ -1370,10 +1398,10 @@ struct Plan {
 };
 
 // Flavour and query heads per workgroup: groups that are a multiple of 4 query heads over a
-// bf16 / fp8 cache run on the matrix cores with 4, 8, 16 or 32 heads per workgroup (fewer than
-// 16 heads pad the 16-wide head tile with zero queries: the matrix cores still take the
-// arithmetic off the vector ALUs, measured equal or faster at g = 4); everything else runs on
-// the vector ALUs with 4, 2 or 1.
+// bf16 / fp8 / int8 cache run on the matrix cores with 4, 8, 16 or 32 heads per workgroup
+// (fewer than 16 heads pad the 16-wide head tile with zero queries: the matrix cores still
+// take the arithmetic off the vector ALUs, measured equal or faster at g = 4); everything
+// else runs on the vector ALUs with 4, 2 or 1.
 bool use_mfma(const da_desc *d) { return d->kv_dtype != DA_F32 && (d->h_q / d->h_kv) % 4 == 0; }
 int heads_per_block(const da_desc *d) {
     const int g = d->h_q / d->h_kv;
@@ -1433,6 +1461,7 @@ const void *split_kernel_ptr(int gt, bool mfma) {
 const void *split_kernel_ptr(int kv, int d, int gt, bool mfma) {
     if (kv == DA_F32) return d == 64 ? split_kernel_ptr<DA_F32, 64>(gt, false) : split_kernel_ptr<DA_F32, 128>(gt, false);
     if (kv == DA_BF16) return d == 64 ? split_kernel_ptr<DA_BF16, 64>(gt, mfma) : split_kernel_ptr<DA_BF16, 128>(gt, mfma);
+    if (kv == DA_INT8) return d == 64 ? split_kernel_ptr<DA_INT8, 64>(gt, mfma) : split_kernel_ptr<DA_INT8, 128>(gt, mfma);
     return d == 64 ? split_kernel_ptr<DA_FP8_E4M3FN, 64>(gt, mfma) : split_kernel_ptr<DA_FP8_E4M3FN, 128>(gt, mfma);
 }
 
@@ -1494,6 +1523,9 @@ void launch_split(int kv, int d, int gt, bool mfma, dim3 grid, hipStream_t st, c
         if (kv == DA_BF16) {
             if (d == 64) launch_split_mfma_gt<DA_BF16, 64, DIRECT>(gt, grid, st, args);
             else launch_split_mfma_gt<DA_BF16, 128, DIRECT>(gt, grid, st, args);
+        } else if (kv == DA_INT8) {
+            if (d == 64) launch_split_mfma_gt<DA_INT8, 64, DIRECT>(gt, grid, st, args);
+            else launch_split_mfma_gt<DA_INT8, 128, DIRECT>(gt, grid, st, args);
         } else {
             if (d == 64) launch_split_mfma_gt<DA_FP8_E4M3FN, 64, DIRECT>(gt, grid, st, args);
             else launch_split_mfma_gt<DA_FP8_E4M3FN, 128, DIRECT>(gt, grid, st, args);
@@ -1506,6 +1538,9 @@ void launch_split(int kv, int d, int gt, bool mfma, dim3 grid, hipStream_t st, c
     } else if (kv == DA_BF16) {
         if (d == 64) launch_split_gt<DA_BF16, 64, DIRECT>(gt, grid, st, args);
         else launch_split_gt<DA_BF16, 128, DIRECT>(gt, grid, st, args);
+    } else if (kv == DA_INT8) {
+        if (d == 64) launch_split_gt<DA_INT8, 64, DIRECT>(gt, grid, st, args);
+        else launch_split_gt<DA_INT8, 128, DIRECT>(gt, grid, st, args);
     } else {
         if (d == 64) launch_split_gt<DA_FP8_E4M3FN, 64, DIRECT>(gt, grid, st, args);
         else launch_split_gt<DA_FP8_E4M3FN, 128, DIRECT>(gt, grid, st, args);
@@ -1537,8 +1572,8 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     const bool append = k_new || v_new;
     if (append && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)))
         return fail(DA_ERR_INVALID_ARG, "%s: k_new and v_new must both be 16-byte aligned device pointers", who);
-    if (desc->kv_dtype == DA_FP8_E4M3FN && !kv_scales)
-        return fail(DA_ERR_INVALID_ARG, "%s: an fp8 cache needs kv_scales", who);
+    if ((desc->kv_dtype == DA_FP8_E4M3FN || desc->kv_dtype == DA_INT8) && !kv_scales)
+        return fail(DA_ERR_INVALID_ARG, "%s: an 8-bit (fp8 / int8) cache needs kv_scales", who);
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace) ||
         (out && !aligned16(out)))
         return fail(DA_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", who);

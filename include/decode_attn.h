@@ -16,9 +16,11 @@
  *                                       element (b,kvh,l,j) at ((b*h_kv+kvh)*cap+l)*d_k+j
  *   v_cache  [batch, h_kv, cap, d_v]    element type desc->kv_dtype
  *   lens     [batch] int32              rows currently in each sequence (device memory)
- *   kv_scales[batch, h_kv, 2] fp32      (K scale, V scale) per slot; fp8 caches only
+ *   kv_scales[batch, h_kv, 2] fp32      (K scale, V scale) per slot; 8-bit caches only
  *   out      [batch, h_q, d_v] fp32
- * For an fp8 cache the value of an element is decode_e4m3fn(code) * its slot's scale.
+ * For an fp8 cache the value of an element is decode_e4m3fn(code) * its slot's scale; for
+ * an int8 cache it is the two's-complement code * its slot's scale (the decode-attention
+ * roofline page: 8-bit KV, fp8 or int8, halves the bytes each step reads).
  *
  * Memory and threads: the caller owns every buffer (all pointers are device pointers unless
  * stated otherwise). The library never allocates or frees device memory and keeps no
@@ -56,12 +58,12 @@ extern "C" {
                                     lens[b] unchanged */
 #define DA_DEV_ERR_LEN_RANGE 2   /* decode: lens[b] outside [1, max_len]; out[b] zeroed */
 
-typedef enum { DA_F32 = 0, DA_BF16 = 1, DA_FP8_E4M3FN = 2 } da_dtype;
+typedef enum { DA_F32 = 0, DA_BF16 = 1, DA_FP8_E4M3FN = 2, DA_INT8 = 3 } da_dtype;
 
 /*
  * Problem descriptor. Supported: d_k == d_v in {64, 128}; (q_dtype, kv_dtype) in
- * {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN)}; any h_q that is a multiple of h_kv;
- * batch <= 1024. scale is the factor of Step I (1/sqrt(d_k) in the page's setting), applied
+ * {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN), (BF16, INT8)}; any h_q that is a
+ * multiple of h_kv; batch <= 1024. scale is the factor of Step I (1/sqrt(d_k) in the page's setting), applied
  * once. Work partition: the cache rows of all (sequence, KV head) pairs, taken in order,
  * are cut into equal contiguous shares, one per workgroup. block_rows = 0 lets the library
  * use one share per workgroup that fits on the device at once; block_rows > 0 asks for
@@ -107,8 +109,8 @@ int da_workspace_init(void *workspace, size_t ws_bytes, void *stream);
  * KV-cache accumulation (page "MoA-Structured Decode Attention", §5): for every sequence b
  * and KV head kvh, copies row k_new[b,kvh,:] (shape [batch, h_kv, d_k], kv_dtype) into row
  * lens[b] of k_cache and v_new[b,kvh,:] into row lens[b] of v_cache, then sets
- * lens[b] += 1. Bit copies: every other byte of the caches is unchanged. fp8 rows must
- * already be quantised with their slot's scale. A sequence with lens[b] outside [0, cap) is
+ * lens[b] += 1. Bit copies: every other byte of the caches is unchanged. 8-bit rows
+ * must already be quantised with their slot's scale. A sequence with lens[b] outside [0, cap) is
  * skipped and raises DA_DEV_ERR_APPEND_FULL in the workspace (which may be NULL when the
  * caller does not want the error word; the row is still skipped).
  */
@@ -119,10 +121,10 @@ int kv_append(const da_desc *desc, void *k_cache, void *v_cache, int32_t *lens,
  * Decode attention for every (b, h) over rows [0, lens[b]) (page "MoA-Structured Decode
  * Attention", §2 Steps I-III, §6 group selection). max_len is a host-side upper bound on
  * every lens[b] (1 <= max_len <= cap) that sizes the work partition. kv_scales is required
- * for an fp8 cache and ignored otherwise. out is fp32 [batch, h_q, d_v]. Two kernels: the
- * split kernel (a (sequence, KV head) whose rows one workgroup covers is written to out
- * directly, the others leave per-segment partial results) and the log-sum-exp combine of
- * the rest. The result equals decode_attn_partial followed by decode_attn_combine.
+ * for an fp8 or int8 cache and ignored otherwise. out is fp32 [batch, h_q, d_v]. Two
+ * kernels: the split kernel (a (sequence, KV head) whose rows one workgroup covers is
+ * written to out directly, the others leave per-segment partial results) and the
+ * log-sum-exp combine of the rest. The result equals decode_attn_partial followed by decode_attn_combine.
  */
 int decode_attn_run(const da_desc *desc, const void *q, const void *k_cache,
                     const void *v_cache, const int32_t *lens, int32_t max_len,
@@ -156,7 +158,7 @@ int decode_attn_combine(const da_desc *desc, const int32_t *lens, int32_t max_le
  * stores that row into the cache before reading it. The combine kernel then sets
  * lens[b] += 1 for the appended sequences. max_len bounds the lengths after the append
  * (lens[b] + 1 <= max_len <= cap). k_cache, v_cache and lens are written; k_new and v_new
- * are [batch, h_kv, d] rows in the cache's type, fp8 rows quantised with their slot's scale.
+ * are [batch, h_kv, d] rows in the cache's type, 8-bit rows quantised with their slot's scale.
  * The workspace's error word must be the one the caller reads (it is not optional here).
  */
 int decode_attn_append_run(const da_desc *desc, const void *q, void *k_cache, void *v_cache,

@@ -6,6 +6,8 @@ Tolerances (fixed per KV element type; see the parity tests):
   bf16 cache: |gpu - oracle| <= 2e-3 elementwise absolute
   fp8  cache: |gpu - oracle| <= 3e-2 elementwise absolute, the oracle run on the same
               dequantised values (code * slot scale)
+  int8 cache: as fp8 (the codes widen to bf16 exactly, as e4m3fn codes do, and the rest of
+              the arithmetic is the same)
 """
 from __future__ import annotations
 
@@ -18,7 +20,7 @@ import decode_attention_kv_split_amd as da
 import oracle
 import workloads
 
-TOL = {"f32": ("rel", 1e-5), "bf16": ("abs", 2e-3), "fp8": ("abs", 3e-2)}
+TOL = {"f32": ("rel", 1e-5), "bf16": ("abs", 2e-3), "fp8": ("abs", 3e-2), "int8": ("abs", 3e-2)}
 
 
 def log(msg: str) -> None:

@@ -157,3 +157,14 @@ def test_python_binding_marshalling_errors():
                            torch.zeros(1, 4, 64), torch.zeros(16, dtype=torch.uint8))
     with pytest.raises(da.DecodeAttnError):
         da.da_workspace_size(da.Desc(1, 3, 2, 64, 128, torch.bfloat16, torch.bfloat16), 10)
+
+
+def test_int8_cache_is_built_and_needs_scales(lib):
+    """(bf16 q, int8 cache) is a supported pair on both flavours; like fp8 it needs kv_scales."""
+    for h_q in (8, 6):  # g = 4: matrix cores; g = 3: vector ALUs
+        d = _desc(h_q=h_q, kv_dtype=3)
+        rc, n = _ws_size(lib, d, 1000)
+        assert rc == 0 and n > 0
+        assert lib.decode_attn_run(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1000, None, FAKE, FAKE, n, None) == -1
+        assert b"kv_scales" in lib.da_last_error()
+    assert _ws_size(lib, _desc(q_dtype=0, kv_dtype=3), 100)[0] == -2  # fp32 q over int8: not built

@@ -3,8 +3,8 @@
 It must give exactly what kv_append followed by decode_attn_run gives: the same output
 bits, the same cache bytes, the same lengths and the same error word (the two paths run the
 same arithmetic on the same bytes; only where the appended row is read from differs). The
-cases cover every kernel flavour, a new row read by two workgroups (two head tiles per KV
-head), 64-byte fp8 rows (a cache line shared by two rows), a full sequence whose append is
+cases cover every kernel flavour and cache type, a new row read by two workgroups (two head
+tiles per KV head), 64-byte 8-bit rows (a cache line shared by two rows), a full sequence whose append is
 skipped, an empty sequence that the append makes one row long, and small workgroup shares
 (many segments). The output is also checked against the CPU oracle.
 """
@@ -19,12 +19,12 @@ from tests.gpu_case import check_close, log
 
 pytestmark = pytest.mark.gpu
 
-TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "int8": torch.int8}
 
 
 def make_case(kv, d, h_q, h_kv, lens, cap, seed):
     """Seeded caches filled at every row (no poison: a full sequence attends over all of cap),
-    new rows, q, and fp8 slot scales."""
+    new rows, q, and slot scales for 8-bit caches."""
     gen = torch.Generator().manual_seed(seed)
     B = len(lens)
     qd = torch.float32 if kv == "f32" else torch.bfloat16
@@ -34,6 +34,12 @@ def make_case(kv, d, h_q, h_kv, lens, cap, seed):
             c = torch.randint(0, 254, shape, generator=gen, dtype=torch.int32)
             c = torch.where(c >= 127, c + 1, c)
             return c.to(torch.uint8).view(torch.float8_e4m3fn)
+        kc, vc = codes((B, h_kv, cap, d)), codes((B, h_kv, cap, d))
+        kn, vn = codes((B, h_kv, d)), codes((B, h_kv, d))
+        scales = (torch.rand(B, h_kv, 2, generator=gen) * 0.02 + 0.002).to(torch.float32)
+    elif kv == "int8":
+        def codes(shape):  # every code, -128 included
+            return torch.randint(-128, 128, shape, generator=gen, dtype=torch.int32).to(torch.int8)
         kc, vc = codes((B, h_kv, cap, d)), codes((B, h_kv, cap, d))
         kn, vn = codes((B, h_kv, d)), codes((B, h_kv, d))
         scales = (torch.rand(B, h_kv, 2, generator=gen) * 0.02 + 0.002).to(torch.float32)
@@ -80,6 +86,8 @@ CASES = [
     ("f32", 64, 3, 1, [1000, 17, 1499]),                  # fp32, g = 3
     ("fp8", 128, 8, 1, [1200, 33, 0, 1499]),              # fp8, LDS-staged segment
     ("fp8", 64, 16, 2, [640, 1, 1500, 1023]),             # 64-byte rows: two rows per cache line
+    ("int8", 128, 8, 1, [1200, 33, 0, 1499]),             # int8, LDS-staged segment
+    ("int8", 64, 6, 2, [640, 1, 1500, 1023]),             # int8 on the vector ALUs (g = 3)
 ]
 
 

@@ -69,6 +69,10 @@ CASES = [
     ("fp8", 128, 16, 2, ("uniform", 1, 1500), 256),
     ("fp8", 128, 8, 8, ("uniform", 1, 1500), 0),
     ("fp8", 64, 8, 1, ("uniform", 1, 1500), 512),
+    ("int8", 128, 16, 2, ("uniform", 1, 1500), 256),
+    ("int8", 128, 8, 8, ("uniform", 1, 1500), 0),
+    ("int8", 64, 8, 1, ("uniform", 1, 1500), 512),
+    ("int8", 128, 64, 2, ("uniform", 1, 1500), 0),
 ]
 
 
@@ -82,11 +86,11 @@ def test_parity_small(kv, d, h_q, h_kv, lens, chunk):
     check_close(out, oracle_out(w, c), kv)
 
 
-@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8", "int8"])
 def test_parity_tile_and_split_boundaries(kv):
     """Lengths at 1, tile edges and split edges (+-1); f32/bf16 append their last row first."""
     edges = [1, 2, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1023]
-    steps = 0 if kv == "fp8" else 1
+    steps = 0 if kv in workloads.SCALED else 1
     w = W(kv_dtype=kv, B=len(edges), h_q=4, h_kv=2, d=128, cap=1024, steps=steps,
           lens=("const", 1024), seed=5)
     c = workloads.generate(w)
@@ -163,6 +167,22 @@ def test_fp8_decoding_of_every_finite_code():
     assert err == 0
     expect = np.array([oracle.e4m3fn_to_f64(x) for x in codes]).reshape(2, 1, 128)
     assert np.array_equal(out.cpu().double().numpy(), expect)
+
+
+def test_int8_decoding_of_every_code():
+    """The in-register int8 decode: with one row per sequence out = code * v_scale, checked
+    for all 256 codes against the oracle's decoder (v_scale = 1, exact), on both flavours
+    (one query head per KV head: vector ALUs; four: matrix cores through the LDS stages)."""
+    codes = list(range(-128, 128))
+    for h_q in (1, 4):
+        w = W(B=2, h_q=h_q, h_kv=1, d=128, cap=64, kv_dtype="int8", lens=("const", 1))
+        c = workloads.generate(w)
+        c["v_cache"][:, 0, 0] = torch.tensor(codes, dtype=torch.int8).reshape(2, 128)
+        c["kv_scales"][:] = 1.0
+        out, _, _, err = run_gpu(w, c, max_len=1)
+        assert err == 0
+        expect = np.array([oracle.int8_to_f64(x) for x in codes]).reshape(2, 1, 128)
+        assert np.array_equal(out.cpu().double().numpy(), np.repeat(expect, h_q, axis=1)), f"h_q={h_q}"
 
 
 def test_gqa_equals_mha_on_broadcast_cache():
@@ -269,7 +289,7 @@ def test_device_errors_are_flagged_and_work_skipped():
 
 
 # ------------------------------------------------------------------ full-size workloads
-FULL = ["mha_bf16", "gqa8_bf16", "mqa_bf16", "gqa8_fp8"]
+FULL = ["mha_bf16", "gqa8_bf16", "mqa_bf16", "gqa8_fp8", "gqa8_int8"]
 
 
 @pytest.mark.parametrize("name", FULL)
