@@ -121,6 +121,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
 }
 
+// The same resource as four words, for inline assembly.
+__device__ __forceinline__ u32x4_t rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) & 0xFFFFu,
+                   (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kRsrcWord3};
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)p);
+}
+
+// One 1 KiB LDS DMA: lane i's 16 bytes at byte voff of the resource land at LDS byte
+// lds + 16 i, non-temporal. It is written as inline assembly because the compiler cannot
+// tell which LDS bytes a DMA writes: with the builtin it waits for every DMA in flight
+// (vmcnt(0)) before each LDS read, which serialises the stages. The caller orders DMA and
+// reads with explicit vmcnt waits and barriers instead. The compiler does not look inside
+// the assembly for hazards, so it keeps the wait states itself: five before (a vector
+// instruction that wrote one of the resource's scalar registers), one between the write of
+// M0 and the DMA that reads it.
+__device__ __forceinline__ void lds_dma16(u32x4_t rsrc, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+
 template <typename Vec>
 __device__ __forceinline__ Vec buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     if constexpr (sizeof(Vec) == 16) {
@@ -797,12 +825,20 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
 
 // Matrix-core segment with workgroup-wide LDS stages filled by DMA (buffer_load ... lds), so
 // that no registers hold K or V in flight and 64 KiB per CU are outstanding.
-//   * A stage holds RS rows of K and V (16 KiB each: 64 bf16 or 128 8-bit rows of d = 128),
-//     every 16-row tile chunk-major: 16-byte chunk c of row r at byte (c*16 + r)*16. One DMA
-//     instruction fills 1 KiB in lane order (lane i: chunk 4q + i/16, row i%16), so the K
-//     A operand of k block kb is one contiguous KiB and the V transpose reads of a d block a
-//     contiguous 512 bytes: neither read has bank conflicts. Two stages alternate (separate
-//     arrays); all 256 threads fill each, and barriers mark a stage filled / consumed.
+//   * A stage holds RS rows of K and V (16 KiB each: 64 bf16 or 128 8-bit rows of d = 128).
+//     One DMA instruction fills 1 KiB in lane order. Two layouts:
+//       - 128-byte rows (8-bit codes, d = 128): "pieces" of 8 whole rows, so that every DMA
+//         instruction reads 8 whole 128-byte lines (half-line reads spread over 16 rows
+//         stream 14 % slower, measured). Chunk c of row r of piece m sits at byte
+//         m*1024 + ((c ^ key(m))*8 + r)*16, with the swizzle key of piece_key: the K
+//         operand reads (16 rows of one chunk) and the V transpose reads (8 rows of pieces
+//         m and m+2) then fall on distinct banks.
+//       - otherwise every 16-row tile chunk-major: 16-byte chunk c of row r at byte
+//         (c*16 + r)*16 (lane i of DMA q: chunk 4q + i/16, row i%16; for 64-byte rows that
+//         is 16 whole rows), so the K A operand of k block kb is one contiguous KiB and the
+//         V transpose reads of a d block a contiguous 512 bytes.
+//     Two stages alternate (separate arrays); all 256 threads fill each; explicit vmcnt waits
+//     and barriers mark a stage filled / consumed.
 //   * Each wave owns one 16-head tile (its own q operand, running max, sums and O) and a
 //     share of the stage's P.V blocks: 16-row blocks for bf16 (Step III by
 //     v_mfma_f32_16x16x16_bf16, V read by ds_read_b64_tr_b16), 32-row blocks for 8-bit codes
@@ -811,6 +847,11 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
 //     registers, exactly). Step I always uses v_mfma_f32_16x16x32_bf16 (8-bit K widened to bf16
 //     after its LDS read).
 //   * At the end the waves holding the same head tile merge through LDS.
+// Swizzle key of the piece (8 rows of 128 bytes) at index m of a stage: flips the parity of
+// every chunk index in pieces whose Gray code is odd, so that pieces 2t / 2t+1 (one K tile)
+// and m / m+2 (the rows one V transpose read gathers) use opposite halves of the banks.
+__device__ __forceinline__ int piece_key(int m) { return (m ^ (m >> 1)) & 1; }
+
 template <int KV, int D, int GT>
 __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
                                                       size_t k, bool direct) {
@@ -828,6 +869,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     constexpr int IPW = NBLK / WPH;            // blocks per wave per stage
     constexpr int DPW = HALF / 1024 / kWaves;  // K (and V) DMA instructions per wave per stage
     constexpr int VM_STAGE = 2 * DPW;          // DMA ops of one stage per wave
+    constexpr bool kLines = ROWB == 128;       // 8-bit codes, d = 128: whole-line DMA layout
     static_assert(NBLK % WPH == 0 && (HALF / 1024) % kWaves == 0, "stage split");
     const int h_q = a.h_q;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -839,13 +881,12 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     __shared__ __align__(16) char s_b[2 * HALF];
     __shared__ __align__(16) float s_c[kWaves][16];
     __shared__ float s_mm[kWaves][16], s_ll[kWaves][16];
-    typedef __attribute__((address_space(3))) void lds_void;
     typedef __attribute__((address_space(3))) char lds_char;
 
     const size_t slot = (size_t)b * a.pt.h_kv + kvh;
     const size_t slot_bytes = (size_t)a.cap * ROWB;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const char *>(a.kc) + slot * slot_bytes, r1 * ROWB);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const char *>(a.vc) + slot * slot_bytes, r1 * ROWB);
+    const u32x4_t krs = rsrc_words(static_cast<const char *>(a.kc) + slot * slot_bytes, r1 * ROWB);
+    const u32x4_t vrs = rsrc_words(static_cast<const char *>(a.vc) + slot * slot_bytes, r1 * ROWB);
     float vscale = 1.f, sc = a.qk_scale;
     if constexpr (kv_scaled(KV)) {
         sc *= a.kv_scales[slot * 2 + 0];
@@ -877,16 +918,20 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     }
     __syncthreads();
 
-    auto issue = [&](char *st, int sb) {
+    const uint32_t lds_a = lds_addr(s_a), lds_b = lds_addr(s_b);
+    auto issue = [&](uint32_t st, int sb) {
 #pragma unroll
         for (int j = 0; j < DPW; ++j) {
-            const int x = wave * DPW + j;  // DMA slot of the stage: tile x / (TILE/1024), part x % ...
-            const int t = x / (TILE / 1024), qq = x % (TILE / 1024);
-            const uint32_t off = (sb + 16 * t + lr) * ROWB + (4 * qq + lg) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(st + t * TILE + qq * 1024), 16, off, 0, 0,
-                                                     kLoadNonTemporal);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(st + HALF + t * TILE + qq * 1024), 16, off, 0,
-                                                     0, kLoadNonTemporal);
+            const int x = wave * DPW + j;  // the stage's x-th KiB
+            uint32_t off;
+            if constexpr (kLines) {  // piece x: rows 8x .. 8x+7, lane i -> row i % 8, chunk (i / 8) ^ key
+                off = (sb + 8 * x + lane % 8) * ROWB + (((lane / 8) ^ piece_key(x)) * 16);
+            } else {  // tile x / (TILE/1024), part x % (TILE/1024)
+                const int t = x / (TILE / 1024), qq = x % (TILE / 1024);
+                off = (sb + 16 * t + lr) * ROWB + (4 * qq + lg) * 16;
+            }
+            lds_dma16(krs, off, st + x * 1024);
+            lds_dma16(vrs, off, st + HALF + x * 1024);
         }
     };
 
@@ -922,13 +967,19 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
 
     // Step I for the 16-row tile at byte `kt` of the stage's K half: lane l gets the scores of
     // rows 4*(l/16)+i for head l%16.
-    auto scores = [&](const char *kt) {
+    auto scores = [&](const char *kt, int t) {
         f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+        // line layout: this lane's row lr of the tile is row lr % 8 of piece 2t + lr / 8, and its
+        // chunk 2 kb + lg / 2 sits at ((2 kb + lg / 2) ^ key) * 8 + lr % 8
+        const char *kl = kt + (lr / 8) * 1024 + (lr % 8) * 16 + 8 * (lg % 2) +
+                         (((lg / 2) ^ piece_key(2 * t + lr / 8)) << 7);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             uint4 raw;
             if constexpr (KV == DA_BF16) {
                 raw = *reinterpret_cast<const uint4 *>(kt + kb * 1024 + lane * 16);
+            } else if constexpr (kLines) {
+                raw = to_bf16x8<KV>(*reinterpret_cast<const uint2 *>(kl + kb * 256));
             } else {
                 const uint2 v = *reinterpret_cast<const uint2 *>(kt + ((kb * 2 + lg / 2) * 16 + lr) * 16 + 8 * (lg % 2));
                 raw = to_bf16x8<KV>(v);
@@ -944,7 +995,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
             const int blk = wb + j * WPH;  // P.V block of the stage
             const int rb = sb + blk * PVR; // its first cache row
             if constexpr (KV == DA_BF16) {
-                const f32x4_t sacc = scores(st + blk * TILE);
+                const f32x4_t sacc = scores(st + blk * TILE, 0);
                 float x[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) x[i] = (rb + 4 * lg + i < r1) ? sacc[i] * sc : -INFINITY;
@@ -962,8 +1013,8 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                 }
             } else {
                 // rows of lane group g: 4g+e (tile 0) and 16+4g+e (tile 1), e < 4
-                const f32x4_t s0 = scores(st + (2 * blk) * TILE);
-                const f32x4_t s1 = scores(st + (2 * blk + 1) * TILE);
+                const f32x4_t s0 = scores(st + (2 * blk) * TILE, 0);
+                const f32x4_t s1 = scores(st + (2 * blk + 1) * TILE, 1);
                 float x[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -976,11 +1027,14 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                 // 16*nb + 8*(s%2) .. +8; the transpose read hands lane l the 8 rows of column l%16.
                 const int e = lr / 2;
                 const int rr = e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4;
-                const char *vt = st + HALF + (2 * blk + rr / 16) * TILE + (rr % 16) * 16 + 8 * (lr % 2);
+                const int vkey = piece_key(rr / 8);
+                const char *vt = kLines ? st + HALF + (4 * blk + rr / 8) * 1024 + (rr % 8) * 16 + 8 * (lr % 2)
+                                        : st + HALF + (2 * blk + rr / 16) * TILE + (rr % 16) * 16 + 8 * (lr % 2);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
+                    const int voff = kLines ? (nb ^ vkey) << 7 : nb * 256;
                     const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (__attribute__((address_space(3))) i32x2_t *)(lds_char *)(vt + nb * 256));
+                        (__attribute__((address_space(3))) i32x2_t *)(lds_char *)(vt + voff));
                     const uint4 w = to_bf16x8<KV>(uint2{(uint32_t)t[0], (uint32_t)t[1]});
                     const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, w);
                     o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, bv, o[nb], 0, 0, 0);
@@ -993,20 +1047,20 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     // Stages alternate between s_a and s_b; before reading a stage each wave waits for its own
     // DMA into it (the other stage's may stay outstanding), then a barrier covers the others.
     const int nst = (r1 - r0 + RS - 1) / RS;
-    issue(s_a, r0);
-    issue(s_b, r0 + RS);
+    issue(lds_a, r0);
+    issue(lds_b, r0 + RS);
     for (int st = 0; st < nst; st += 2) {
         __builtin_amdgcn_s_waitcnt(vmcnt_only(VM_STAGE));
         __syncthreads();
         process(s_a, r0 + st * RS);
         __syncthreads();
-        issue(s_a, r0 + (st + 2) * RS);  // past the end this fetches nothing
+        issue(lds_a, r0 + (st + 2) * RS);  // past the end this fetches nothing
         if (st + 1 < nst) {
             __builtin_amdgcn_s_waitcnt(vmcnt_only(VM_STAGE));
             __syncthreads();
             process(s_b, r0 + (st + 1) * RS);
             __syncthreads();
-            issue(s_b, r0 + (st + 3) * RS);
+            issue(lds_b, r0 + (st + 3) * RS);
         }
     }
     __builtin_amdgcn_s_waitcnt(0);  // no DMA into the stages is outstanding past this point
