@@ -24,6 +24,8 @@ Prints ONE JSON line:
                 the HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, read
                 from the profiles/ summary when it was taken on the current kernel source
   cpu_baseline= the fp64 CPU oracle on the same inputs, full step, host cores
+  stream_ceiling = the read rate of a plain streaming read (da_stream_read over 2 GiB), and
+                value and roofline.achieved as percentages of it
 """
 from __future__ import annotations
 
@@ -58,6 +60,7 @@ def parse_args():
     p.add_argument("--graph", action="store_true",
                    help="also time the step replayed from a captured HIP graph (one step per cache copy)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ceiling", action="store_true", help="skip the measured streaming-read ceiling")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle timing budget")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device copy (FETCH_SIZE / WRITE_SIZE scale factor)")
@@ -90,6 +93,29 @@ def split_kernel_name(w) -> str:
     multiple of 4 over a bf16 / fp8 / int8 cache run on the matrix cores."""
     mfma = w.kv_dtype != "f32" and (w.h_q // w.h_kv) % 4 == 0
     return "split_kv_attn_mfma_kernel" if mfma else "split_kv_attn_kernel"
+
+
+def stream_ceiling(dev, reps: int = 10) -> dict:
+    """The measured read ceiling: da_stream_read (a plain streaming read, no arithmetic) over a
+    2 GiB buffer, 8x the last-level cache, timed with HIP events."""
+    import torch
+    import decode_attention_kv_split_amd as da
+    n = 2 << 30
+    buf = torch.zeros(n, dtype=torch.uint8, device=dev)
+    sink = torch.empty(512, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        da.da_stream_read(buf, sink)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream(dev)
+    a.record(stream)
+    for _ in range(reps):
+        da.da_stream_read(buf, sink)
+    b.record(stream)
+    torch.cuda.synchronize()
+    gbs = n * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del buf
+    return {"GBs": round(gbs, 1), "bytes": n, "reps": reps,
+            "kernel": "stream_read_kernel (16-byte non-temporal buffer loads, 512 workgroups)"}
 
 
 def copy_calibration():
@@ -282,6 +308,11 @@ def main() -> int:
     }
     if graph is not None:
         result["graph_replay"] = graph
+    if not args.no_ceiling:
+        ceil = stream_ceiling(dev)
+        ceil["value_pct_of_ceiling"] = round(100 * value / ceil["GBs"], 2)
+        ceil["achieved_pct_of_ceiling"] = round(100 * achieved / ceil["GBs"], 2)
+        result["stream_ceiling"] = ceil
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, kv_bytes0)
     print(json.dumps(result), flush=True)

@@ -29,7 +29,7 @@ __all__ = [
     "Desc", "DecodeAttnError", "Workspace", "da_workspace_size", "da_plan", "da_workspace_init",
     "kv_append", "decode_attn_run", "decode_attn_partial", "decode_attn_combine",
     "decode_attn_append_run", "decode_attn_append_partial", "decode_attn_append_combine",
-    "da_read_device_error", "da_status_string", "da_last_error", "library_path",
+    "da_read_device_error", "da_stream_read", "da_status_string", "da_last_error", "library_path",
     "DA_F32", "DA_BF16", "DA_FP8_E4M3FN", "DA_INT8", "DEV_ERR_APPEND_FULL", "DEV_ERR_LEN_RANGE",
 ]
 
@@ -245,6 +245,18 @@ def decode_attn_append_combine(desc: Desc, lens, max_len: int, out, workspace) -
     cd = desc.c()
     _check(lib().decode_attn_append_combine(ctypes.byref(cd), ln, int(max_len), op, wp, wn, _stream(out)),
            "decode_attn_append_combine")
+
+
+def da_stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Measurement helper: one plain streaming read of buf (contiguous, on the GPU) into sink
+    (512 fp32 values)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    if not sink.is_cuda or sink.dtype != torch.float32 or sink.numel() < 512:
+        raise ValueError("sink must be a GPU fp32 tensor of at least 512 values")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().da_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                _stream(buf)), "da_stream_read")
 
 
 def da_read_device_error(workspace) -> int:

@@ -186,6 +186,33 @@ __global__ void workspace_init_kernel(int32_t *ws, size_t n) {
         ws[i] = 0;
 }
 
+// Plain streaming read for the measured bandwidth ceiling: workgroup w reads its contiguous
+// chunk of the buffer with 16-byte non-temporal buffer loads, kStreamUnroll in flight per lane,
+// and folds the words into one value per workgroup (so that no load can be dropped).
+constexpr int kStreamWorkgroups = 512;
+constexpr int kStreamUnroll = 8;
+__global__ __launch_bounds__(256) void stream_read_kernel(const char *__restrict__ buf, size_t bytes,
+                                                          uint32_t chunk, float *__restrict__ sink) {
+    const size_t base = (size_t)blockIdx.x * chunk;
+    const uint32_t mine = base >= bytes ? 0u : (uint32_t)(bytes - base < chunk ? bytes - base : chunk);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(buf + base, mine);
+    uint32_t acc = 0;
+    for (uint32_t off = threadIdx.x * 16u; off < mine; off += 256u * 16u * kStreamUnroll) {
+        u32x4_t v[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u)
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + u * 256u * 16u), 0, kLoadNonTemporal);
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    __shared__ uint32_t s_acc[kBlock / kWave];
+#pragma unroll
+    for (int o = 1; o < kWave; o *= 2) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+    if (threadIdx.x % kWave == 0) s_acc[threadIdx.x / kWave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = (float)(s_acc[0] ^ s_acc[1] ^ s_acc[2] ^ s_acc[3]);
+}
+
 // One workgroup per sequence: copy the h_kv new K rows and V rows into row lens[b] in
 // 16-byte pieces, then (after every thread has read lens[b]) advance lens[b].
 __global__ __launch_bounds__(256) void kv_append_kernel(
@@ -1803,6 +1830,18 @@ int decode_attn_append_run(const da_desc *desc, const void *q, void *k_cache, vo
                              ws_bytes, stream, "decode_attn_append_run");
     if (rc) return rc;
     return run_combine(desc, lens, max_len, out, workspace, ws_bytes, stream, 1, true, "decode_attn_append_run");
+}
+
+int da_stream_read(const void *buf, size_t bytes, float *sink, void *stream) {
+    if (!buf || !sink) return fail(DA_ERR_INVALID_ARG, "da_stream_read: NULL pointer");
+    if (!aligned16(buf) || bytes % 16 || bytes == 0)
+        return fail(DA_ERR_INVALID_ARG, "da_stream_read: buf must be 16-byte aligned and bytes a positive multiple of 16");
+    const size_t step = 256u * 16u * kStreamUnroll;
+    const size_t chunk = (bytes / kStreamWorkgroups + step - 1) / step * step;
+    if (chunk > 0x7FFFFFFFull) return fail(DA_ERR_INVALID_ARG, "da_stream_read: more than 1 TiB");
+    hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamWorkgroups), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const char *>(buf), bytes, (uint32_t)chunk, sink);
+    return launch_status("da_stream_read");
 }
 
 int da_read_device_error(const void *workspace, void *stream, int32_t *code) {

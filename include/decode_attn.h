@@ -184,6 +184,16 @@ int decode_attn_append_partial(const da_desc *desc, const void *q, void *k_cache
 int decode_attn_append_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
                                void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * Measurement helper, not part of the attention path: a plain streaming read of `bytes` bytes
+ * at buf (16-byte aligned, bytes a positive multiple of 16) by 512 workgroups, each reading a
+ * contiguous chunk with 16-byte non-temporal loads. sink is a device buffer of at least 512
+ * floats that receives one data-dependent value per workgroup. Timing it gives the read
+ * bandwidth the part sustains for a pure stream, the ceiling against which the split kernel's
+ * rate is compared.
+ */
+int da_stream_read(const void *buf, size_t bytes, float *sink, void *stream);
+
 /* Waits for the stream, then copies the error word into *code (host). For tests and tools. */
 int da_read_device_error(const void *workspace, void *stream, int32_t *code);
 

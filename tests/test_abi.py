@@ -168,3 +168,10 @@ def test_int8_cache_is_built_and_needs_scales(lib):
         assert lib.decode_attn_run(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1000, None, FAKE, FAKE, n, None) == -1
         assert b"kv_scales" in lib.da_last_error()
     assert _ws_size(lib, _desc(q_dtype=0, kv_dtype=3), 100)[0] == -2  # fp32 q over int8: not built
+
+
+def test_stream_read_rejects_bad_sizes(lib):
+    assert lib.da_stream_read(FAKE, 1000, FAKE, None) == -1          # not a multiple of 16
+    assert lib.da_stream_read(ctypes.c_void_p(0x10008), 1024, FAKE, None) == -1  # misaligned
+    assert lib.da_stream_read(FAKE, 0, FAKE, None) == -1
+    assert lib.da_stream_read(None, 1024, FAKE, None) == -1

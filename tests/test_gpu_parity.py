@@ -308,3 +308,22 @@ def test_full_size_workload_sampled(name):
     for b in samples:
         log(f"case full {name}: oracle b={b} L={int(c['lens_final'][b])}")
         check_close(out[b:b + 1], oracle_out(w, c, batch_index=b), w.kv_dtype, f"{name} b={b}")
+
+
+def test_stream_read_reads_every_byte_once():
+    """da_stream_read (the measured-ceiling helper): workgroup w folds the 32-bit words of its
+    chunk by XOR; every byte of the buffer lands in exactly one workgroup's value."""
+    n = (3 << 20) + 4096  # not a multiple of the per-workgroup chunk
+    g = torch.Generator().manual_seed(11)
+    host = torch.randint(0, 256, (n,), generator=g, dtype=torch.int32).to(torch.uint8)
+    sink = torch.full((512,), -1.0, device="cuda")
+    da.da_stream_read(host.cuda(), sink)
+    torch.cuda.synchronize()
+    step = 256 * 16 * 8
+    chunk = -(-(n // 512) // step) * step
+    words = host.numpy().view(np.uint32)
+    expect = []
+    for w in range(512):
+        part = words[w * chunk // 4:min((w + 1) * chunk, n) // 4]
+        expect.append(float(np.bitwise_xor.reduce(part)) if part.size else 0.0)
+    assert np.array_equal(sink.cpu().numpy(), np.array(expect, dtype=np.float32))
