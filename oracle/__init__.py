@@ -53,6 +53,8 @@ def _open(path: str):
     lib.oracle_head_f64.restype = I
     lib.oracle_decode_f64_traced.argtypes = [I] * 8 + [F] + [P] * 6 + [I] + [P] * 3
     lib.oracle_decode_f64_traced.restype = I
+    lib.oracle_decode_multi_f64.argtypes = [I] * 9 + [F] + [P] * 6 + [I]
+    lib.oracle_decode_multi_f64.restype = I
     lib.oracle_kv_append.argtypes = [I] * 6 + [P] * 5
     lib.oracle_kv_append.restype = I
     return lib
@@ -170,6 +172,27 @@ def decode_f64(q, k_cache, v_cache, lens, scale: float, kv_scales=None,
     if rc:
         raise ValueError(f"oracle_decode_f64 failed ({rc})")
     return (out, (qm, km, vm)) if marks else out
+
+
+def decode_multi_f64(q, k_cache, v_cache, lens, scale: float, kv_scales=None, nthreads: int = 0):
+    """Multi-query causal decode in fp64: q [B, T, h_q, d_k]; query t of sequence b attends
+    over its first lens[b] - T + 1 + t rows (lens[b] >= T). Returns out [B, T, h_q, d_v]."""
+    q, k_cache, v_cache, lens, kv_scales = map(_np, (q, k_cache, v_cache, lens, kv_scales))
+    q, k_cache, v_cache = (np.ascontiguousarray(a) for a in (q, k_cache, v_cache))
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    B, T, h_q, d_k = q.shape
+    _, h_kv, cap, _ = k_cache.shape
+    d_v = v_cache.shape[3]
+    if kv_scales is not None:
+        kv_scales = np.ascontiguousarray(kv_scales, dtype=np.float32)
+    out = np.zeros((B, T, h_q, d_v), dtype=np.float64)
+    rc = _load().oracle_decode_multi_f64(
+        B, T, h_q, h_kv, d_k, d_v, cap, _dtype_code(q), _dtype_code(k_cache),
+        float(np.float32(scale)), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens),
+        _ptr(kv_scales), _ptr(out), int(nthreads))
+    if rc:
+        raise ValueError(f"oracle_decode_multi_f64 failed ({rc})")
+    return out
 
 
 def kv_append(k_cache, v_cache, lens, k_new, v_new):

@@ -41,3 +41,37 @@ def decode(q, k_cache, v_cache, lens, scale):
             rows.append(attend_one(q[b][h], k_cache[b][kvh][:n], v_cache[b][kvh][:n], scale))
         out.append(rows)
     return out
+
+
+def decode_multi(q, k_cache, v_cache, lens, scale):
+    """Multi-query causal decode as masked attention over the whole cache (the forward form
+    with a mask, page "Phase 3, Section 6: StoryLM-0 head-parallel attention", §3: softmax of
+    scale * scores + mask over the key axis): q [B][T][h_q][d_k], caches [B][h_kv][cap][d],
+    lens [B]. Query t of sequence b sits at position lens[b] - T + t; the mask is 0 for key
+    rows at or before that position and minus infinity after it (up to lens[b])."""
+    out = []
+    with localcontext() as ctx:
+        ctx.prec = 50
+        sc = Decimal(float(scale))
+        minus_inf = Decimal("-Infinity")
+        for b in range(len(q)):
+            T, h_q, h_kv = len(q[b]), len(q[b][0]), len(k_cache[b])
+            g = h_q // h_kv
+            L = int(lens[b])
+            per_t = []
+            for t in range(T):
+                pos = L - T + t
+                rows = []
+                for h in range(h_q):
+                    K, V = k_cache[b][h // g][:L], v_cache[b][h // g][:L]
+                    qd = [Decimal(float(x)) for x in q[b][t][h]]
+                    s = [sc * sum(qd[j] * Decimal(float(K[l][j])) for j in range(len(qd)))
+                         + (Decimal(0) if l <= pos else minus_inf) for l in range(L)]
+                    m = max(s)
+                    e = [(x - m).exp() for x in s]
+                    Z = sum(e)
+                    rows.append([sum(e[l] / Z * Decimal(float(V[l][d])) for l in range(L))
+                                 for d in range(len(V[0]))])
+                per_t.append(rows)
+            out.append(per_t)
+    return out

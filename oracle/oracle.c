@@ -221,6 +221,68 @@ int oracle_decode_f64(int B, int h_q, int h_kv, int d_k, int d_v, int cap,
 }
 
 /*
+ * Multi-query causal decode (several query rows per sequence, as in speculative decoding
+ * or a chunked prefill). Page "MoA-Structured Decode Attention", introduction: the decode
+ * DNF is the forward DNF with the query-row index fixed to the current step; here it takes
+ * the last T positions of each sequence instead of one. Page "Phase 3, Section 6:
+ * StoryLM-0 head-parallel attention", §3: T query rows, softmax over the key axis of the
+ * scaled scores plus a mask. The mask is causal: query t of sequence b sits at position
+ * lens[b] - T + t, and its own row and every earlier row are visible, so it attends over
+ * the first n = lens[b] - T + 1 + t rows with Steps I-III unchanged (T = 1 is
+ * oracle_decode_f64).
+ *   q   [B, T, h_q, d_k]   out [B, T, h_q, d_v] double   lens[b] >= T
+ * Everything else as oracle_decode_f64.
+ */
+int oracle_decode_multi_f64(int B, int T, int h_q, int h_kv, int d_k, int d_v, int cap,
+                            int q_dtype, int kv_dtype, float scale, const void *q,
+                            const void *k_cache, const void *v_cache,
+                            const int32_t *lens, const float *kv_scales, double *out,
+                            int nthreads) {
+    if (B < 0 || T < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv || d_k < 1 || d_v < 1 || cap < 1)
+        return -1;
+    if (!elem_bytes(q_dtype) || !elem_bytes(kv_dtype)) return -1;
+    if (scaled(kv_dtype) && !kv_scales) return -1;
+    for (int b = 0; b < B; ++b)
+        if (lens[b] < T || lens[b] > cap) return -3;
+    const int g = h_q / h_kv;
+    const int nthr = nthreads > 0 ? nthreads : omp_get_max_threads();
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthr) reduction(min : status)
+    for (long bth = 0; bth < (long)B * T * h_q; ++bth) {
+        const int b = (int)(bth / ((long)T * h_q));
+        const int t = (int)(bth / h_q % T), h = (int)(bth % h_q);
+        const int kvh = h / g; /* its KV group */
+        const int n = lens[b] - T + 1 + t; /* causal: rows 0 .. lens[b] - T + t */
+        const size_t slot = (size_t)b * h_kv + kvh;
+        double ks = 1.0, vs = 1.0;
+        if (scaled(kv_dtype)) {
+            ks = (double)kv_scales[slot * 2 + 0];
+            vs = (double)kv_scales[slot * 2 + 1];
+        }
+        double *qd = (double *)malloc(sizeof(double) * (size_t)d_k);
+        double *Kd = (double *)malloc(sizeof(double) * (size_t)n * d_k);
+        double *Vd = (double *)malloc(sizeof(double) * (size_t)n * d_v);
+        if (!qd || !Kd || !Vd) {
+            free(qd); free(Kd); free(Vd);
+            status = -2;
+            continue;
+        }
+        for (int j = 0; j < d_k; ++j) qd[j] = load_elem(q, q_dtype, (size_t)bth * d_k + j);
+        for (int l = 0; l < n; ++l) {
+            for (int j = 0; j < d_k; ++j)
+                Kd[(size_t)l * d_k + j] = load_elem(k_cache, kv_dtype, (slot * cap + l) * d_k + j) * ks;
+            for (int d = 0; d < d_v; ++d)
+                Vd[(size_t)l * d_v + d] = load_elem(v_cache, kv_dtype, (slot * cap + l) * d_v + d) * vs;
+        }
+        int rc = oracle_head_f64(n, d_k, d_v, (double)scale, qd, Kd, Vd, NULL,
+                                 NULL, NULL, NULL, NULL, out + (size_t)bth * d_v);
+        if (rc < status) status = rc;
+        free(qd); free(Kd); free(Vd);
+    }
+    return status;
+}
+
+/*
  * KV-cache accumulation: for every sequence b and KV head kvh, copy row
  * k_new[b][kvh] into k_cache at row lens[b] (and v_new into v_cache), then
  * lens[b] += 1. Byte copies; every other byte of the caches is unchanged.

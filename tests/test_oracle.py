@@ -319,3 +319,79 @@ def test_thread_count_does_not_change_bits():
     a = oracle.decode_f64(c["q"], c["k_cache"], c["v_cache"], c["lens_final"], w.scale, nthreads=1)
     b = oracle.decode_f64(c["q"], c["k_cache"], c["v_cache"], c["lens_final"], w.scale, nthreads=4)
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- multi-query causal decode
+def _mq_case(seed, kv, T, h_q, h_kv, d, cap, lens=None):
+    w = workloads.Workload("mq", 3, h_q, h_kv, d, cap, "bf16" if kv in workloads.SCALED else kv, kv,
+                           lens or ("uniform", T, cap), 0, seed, 0.7, nq=T)
+    c = workloads.generate(w, poison=True)
+    if T == 1:
+        c["q"] = c["q"][:, None]  # [B, 1, h_q, d]
+    return w, c
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8", "int8"])
+def test_multi_query_vs_masked_brute_force(seed, kv):
+    """Multi-query causal decode against 50-digit masked attention over the whole cache
+    (scores + 0 / minus-infinity mask, the forward form of page "Phase 3, Section 6:
+    StoryLM-0 head-parallel attention", §3): tiny GQA cases, T = 1..3, ragged lengths >= T."""
+    rng = np.random.default_rng(700 + 10 * seed + len(kv))
+    T = int(rng.integers(1, 4))
+    h_kv = int(rng.integers(1, 3))
+    w, c = _mq_case(900 + seed, kv, T, h_kv * int(rng.integers(1, 3)), h_kv, int(rng.integers(1, 5)), 7)
+    got = oracle.decode_multi_f64(c["q"], c["k_cache"], c["v_cache"], c["lens_final"], w.scale,
+                                  kv_scales=c["kv_scales"])
+    sc = c["kv_scales"]
+    ref = brute.decode_multi(_widen(c["q"]).tolist(), _widen(c["k_cache"], sc, 0).tolist(),
+                             _widen(c["v_cache"], sc, 1).tolist(), c["lens_final"].tolist(),
+                             float(np.float32(w.scale)))
+    np.testing.assert_allclose(got, np.array(ref, dtype=np.float64), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("T,h_q,h_kv,d,kv", [
+    (4, 32, 8, 128, "bf16"), (2, 8, 1, 64, "f32"), (8, 4, 4, 64, "bf16"), (3, 16, 2, 128, "fp8"),
+    (5, 8, 2, 128, "int8")])
+def test_multi_query_vs_torch_sdpa_with_causal_mask(T, h_q, h_kv, d, kv):
+    """torch SDPA in fp64 on the CPU with an explicit boolean mask: query t of a sequence of
+    L rows sees key rows 0 .. L - T + t (its own position and before). GQA by repeat_interleave."""
+    w, c = _mq_case(31 + T, kv, T, h_q, h_kv, d, 300)
+    got = oracle.decode_multi_f64(c["q"], c["k_cache"], c["v_cache"], c["lens_final"], w.scale,
+                                  kv_scales=c["kv_scales"])
+    sc = c["kv_scales"]
+    K = torch.from_numpy(_widen(c["k_cache"], sc, 0))
+    V = torch.from_numpy(_widen(c["v_cache"], sc, 1))
+    q = c["q"].to(torch.float64)
+    for b in range(w.B):
+        L = int(c["lens_final"][b])
+        kb = K[b, :, :L].repeat_interleave(w.g, dim=0)[None]
+        vb = V[b, :, :L].repeat_interleave(w.g, dim=0)[None]
+        mask = torch.arange(L)[None, :] <= (L - T + torch.arange(T))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[b].transpose(0, 1)[None], kb, vb, attn_mask=mask, scale=float(np.float32(w.scale)))
+        np.testing.assert_allclose(got[b], ref[0].transpose(0, 1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_multi_query_reduces_to_single_query_decode():
+    """T = 1 is the single-query decode, and query t of T is the single-query decode of the
+    sequence cut after its own row (lens - T + 1 + t rows): bitwise, in fp64."""
+    w, c = _mq_case(5, "bf16", 1, 8, 2, 64, 200)
+    one = oracle.decode_multi_f64(c["q"], c["k_cache"], c["v_cache"], c["lens_final"], w.scale)
+    ref = oracle.decode_f64(c["q"][:, 0], c["k_cache"], c["v_cache"], c["lens_final"], w.scale)
+    assert np.array_equal(one[:, 0], ref)
+    T = 4
+    w, c = _mq_case(6, "bf16", T, 8, 2, 64, 200)
+    allq = oracle.decode_multi_f64(c["q"], c["k_cache"], c["v_cache"], c["lens_final"], w.scale)
+    for t in range(T):
+        ref = oracle.decode_f64(c["q"][:, t].contiguous(), c["k_cache"], c["v_cache"],
+                                c["lens_final"] - T + 1 + t, w.scale)
+        assert np.array_equal(allq[:, t], ref)
+
+
+def test_multi_query_needs_T_rows():
+    w, c = _mq_case(7, "f32", 3, 2, 1, 8, 20)
+    lens = c["lens_final"].clone()
+    lens[1] = 2
+    with pytest.raises(ValueError):
+        oracle.decode_multi_f64(c["q"], c["k_cache"], c["v_cache"], lens, w.scale)

@@ -3,7 +3,8 @@
 Each case plants one mistake in a private copy of ``oracle/oracle.c`` (a
 dropped term, a wrong sign, index or group map, a transposed operand, a
 doubled scale, a wrong dequantisation scale, a decoder off by one, int8
-codes read as unsigned bytes, a missing length update), builds it with gcc in a temporary directory, routes the
+codes read as unsigned bytes, a causal bound off by one, query rows taken in
+the wrong order, a missing length update), builds it with gcc in a temporary directory, routes the
 oracle wrapper to it and runs the pin tests of ``test_oracle.py``. At least
 one pin must fail for every mutant; the unmutated copy must pass them all.
 Everything runs on the CPU.
@@ -19,7 +20,8 @@ from tests import test_oracle as pins
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
 MUTANTS = {
-    "group_map_modulo": ("const int kvh = h / g;", "const int kvh = h % h_kv;"),
+    "group_map_modulo": ("const int kvh = h / g; /* the KV group this query head selects */",
+                         "const int kvh = h % h_kv;"),
     "transposed_K": ("acc += q[j] * K[(size_t)l * d_k + j];", "acc += q[j] * K[(size_t)j * n + l];"),
     "scale_twice": ("s[l] = scale * acc;", "s[l] = scale * scale * acc;"),
     "exp_sign": ("e[l] = exp(s[l] - m);\n        Z +=", "e[l] = exp(m - s[l]);\n        Z +="),
@@ -29,6 +31,9 @@ MUTANTS = {
     "fp8_bias_8": ("v = ldexp(1.0 + mant / 8.0, expo - 7);", "v = ldexp(1.0 + mant / 8.0, expo - 8);"),
     "int8_read_unsigned": ("case ORACLE_INT8: return oracle_int8_to_f64(((const int8_t *)base)[idx]);",
                            "case ORACLE_INT8: return (double)((const uint8_t *)base)[idx];"),
+    "causal_bound_off_by_one": ("const int n = lens[b] - T + 1 + t;", "const int n = lens[b] - T + t + (t > 0);"),
+    "query_index_swapped": ("const int t = (int)(bth / h_q % T), h = (int)(bth % h_q);",
+                            "const int t = (int)(bth % T), h = (int)(bth / T % h_q);"),
     "append_no_len_update": ("lens[b] += 1;", "lens[b] += 0;"),
     "append_wrong_row": ("(slot * cap + (size_t)lens[b]) * d_k * eb", "(slot * cap + (size_t)lens[b] / 2) * d_k * eb"),
     # a rewrite that changes nothing: the control that must pass every pin
@@ -45,6 +50,8 @@ PINS = [
     ("sdpa_gqa", lambda gd: pins.test_oracle_vs_torch_sdpa_fp64("gqa4", 8, 2, 128, "bf16")),
     ("special_cases", lambda gd: pins.test_special_cases_reduce_to_rows_or_mean()),
     ("fp8_codes", lambda gd: pins.test_fp8_e4m3fn_decoder_all_codes()),
+    ("mq_brute", lambda gd: [pins.test_multi_query_vs_masked_brute_force(s, "f32") for s in range(4)]),
+    ("mq_sdpa", lambda gd: pins.test_multi_query_vs_torch_sdpa_with_causal_mask(4, 32, 8, 128, "bf16")),
     ("append_layout", lambda gd: pins.test_append_layout_gamma_offsets(gd)),
     ("append_bits", lambda gd: pins.test_append_is_bit_exact_and_touches_only_its_rows()),
 ]

@@ -56,6 +56,7 @@ class Workload:
     steps: int          # appends performed (the last `steps` drawn rows of each sequence)
     seed: int
     scale: float        # softmax scale as fp32 (1/sqrt(d))
+    nq: int = 1         # query rows per sequence (> 1: multi-query causal decode)
 
     @property
     def g(self) -> int:
@@ -130,7 +131,7 @@ def generate(w: Workload, seed: int | None = None, poison: bool = True) -> dict:
     """Draw one workload's inputs on the CPU.
 
     Returns a dict of CPU tensors:
-      q          [B, h_q, d]                 q_dtype
+      q          [B, h_q, d]                 q_dtype ([B, nq, h_q, d] when nq > 1)
       k_cache    [B, h_kv, cap, d]           kv_dtype, rows < lens_init valid
       v_cache    [B, h_kv, cap, d]
       lens_init  [B] int32                   rows in the cache before the appends
@@ -143,9 +144,10 @@ def generate(w: Workload, seed: int | None = None, poison: bool = True) -> dict:
     gen = torch.Generator(device="cpu")
     gen.manual_seed(w.seed if seed is None else seed)
     lens = draw_lens(w, gen)
-    if int(lens.max()) > w.cap or int(lens.min()) < 1 + w.steps:
+    if int(lens.max()) > w.cap or int(lens.min()) < max(1 + w.steps, w.nq):
         raise ValueError("lengths do not fit the cache")
-    q = torch.randn(w.B, w.h_q, w.d, generator=gen, dtype=torch.float32).to(TORCH_DTYPE[w.q_dtype])
+    qshape = (w.B, w.h_q, w.d) if w.nq == 1 else (w.B, w.nq, w.h_q, w.d)
+    q = torch.randn(qshape, generator=gen, dtype=torch.float32).to(TORCH_DTYPE[w.q_dtype])
     shape = (w.B, w.h_kv, w.cap, w.d)
     kv_t = TORCH_DTYPE[w.kv_dtype]
     if poison:
