@@ -52,7 +52,7 @@ def parse_args():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="gqa8_bf16",
-                   help="single_head_f32 | mha_bf16 | gqa8_bf16 | mqa_bf16 | gqa8_fp8 | gqa8_int8")
+                   help="single_head_f32 | mha_bf16 | gqa8_bf16 | mqa_bf16 | gqa8_fp8 | gqa8_int8 | gqa8_mq4_bf16")
     p.add_argument("--const-len", type=int, default=0,
                    help="override: every sequence this long (the 8K/16K/32K sweep)")
     p.add_argument("--block-rows", type=int, default=0, help="rows per split (0 = library choice)")
@@ -89,9 +89,10 @@ def profiled_traffic(workload: str):
 
 
 def split_kernel_name(w) -> str:
-    """The split kernel the library launches for this workload: query groups that are a
-    multiple of 4 over a bf16 / fp8 / int8 cache run on the matrix cores."""
-    mfma = w.kv_dtype != "f32" and (w.h_q // w.h_kv) % 4 == 0
+    """The split kernel the library launches for this workload: query groups (g heads times
+    the query rows per sequence) that are a multiple of 4 over a bf16 / fp8 / int8 cache run
+    on the matrix cores."""
+    mfma = w.kv_dtype != "f32" and (w.h_q // w.h_kv * w.nq) % 4 == 0
     return "split_kv_attn_mfma_kernel" if mfma else "split_kv_attn_kernel"
 
 
@@ -153,7 +154,7 @@ def main() -> int:
     lens_final = c["lens_final"]
     esz = workloads.ELEM_BYTES[w.kv_dtype]
     row_bytes = w.h_kv * 2 * w.d * esz  # K and V bytes of one row of every KV head
-    q_bytes = w.B * w.h_q * w.d * workloads.ELEM_BYTES[w.q_dtype]
+    q_bytes = w.B * w.nq * w.h_q * w.d * workloads.ELEM_BYTES[w.q_dtype]
     cache_bytes = 2 * c["k_cache"].numel() * esz
     appends = w.steps > 0
     # use u of a cache copy (u = step // R) attends over lens_init + 1 + u rows when appending
@@ -172,7 +173,7 @@ def main() -> int:
         return kv_bytes0 + (w.B * (i // R) * row_bytes if appends else 0)
 
     desc = da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, workloads.TORCH_DTYPE[w.q_dtype],
-                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, args.block_rows)
+                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, args.block_rows, w.nq)
     plan = da.da_plan(desc, max_len)
     q = c["q"].to(dev)
     scales = c["kv_scales"].to(dev) if c["kv_scales"] is not None else None
@@ -187,7 +188,7 @@ def main() -> int:
         vc = v0 if r == 0 else v0.clone()
         slots.append((kc, vc, lens_init.clone() if appends else lens_init))
     ws = da.Workspace(desc, max_len, device=dev)
-    out = torch.empty(w.B, w.h_q, w.d, dtype=torch.float32, device=dev)
+    out = torch.empty(desc.rows_shape(), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(i, ev=None):
@@ -284,7 +285,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": w.B, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
-            "cap": w.cap, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype,
+            "cap": w.cap, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype, "query_rows_per_seq": w.nq,
             "lens": (f"const {int(lens_final.max())}" if w.lens[0] == "const"
                      else f"uniform[{w.lens[1]},{w.lens[2]}] seed {w.seed}"),
             "sum_lens_first_step": int(lens_first.sum()), "max_len": max_len,
@@ -344,9 +345,9 @@ def cpu_baseline(w, budget_s: float, kv_bytes_full: int) -> dict:
         sl = slice(bs[0], bs[-1] + 1)
         sc = None if c["kv_scales"] is None else c["kv_scales"][sl].contiguous()
         t = time.perf_counter()
-        oracle.decode_f64(c["q"][sl].contiguous(), np.ascontiguousarray(kc[sl]),
-                          np.ascontiguousarray(vc[sl]), lens[sl], w.scale, kv_scales=sc,
-                          nthreads=nthreads)
+        fn = oracle.decode_multi_f64 if w.nq > 1 else oracle.decode_f64
+        fn(c["q"][sl].contiguous(), np.ascontiguousarray(kc[sl]), np.ascontiguousarray(vc[sl]),
+           lens[sl], w.scale, kv_scales=sc, nthreads=nthreads)
         return time.perf_counter() - t
 
     t_one = run([0])
@@ -361,7 +362,8 @@ def cpu_baseline(w, budget_s: float, kv_bytes_full: int) -> dict:
     full_step_s = elapsed * (kv_bytes_full / sample_bytes)
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
             "sample": f"first {k} of {w.B} sequences ({rows} rows x {w.h_kv} KV heads, all "
-                      f"{w.h_q} query heads), fp64, {elapsed:.2f} s",
+                      f"{w.h_q} query heads" + (f" x {w.nq} query rows" if w.nq > 1 else "") +
+                      f"), fp64, {elapsed:.2f} s",
             "us_per_full_step_est": round(full_step_s * 1e6, 1),
             "cpu": _cpu_model()}
 

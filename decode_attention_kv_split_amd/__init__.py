@@ -10,9 +10,10 @@ stream. There is no fallback: if the library is not built, importing the
 binding's functions fails.
 
 Layouts (the same as the C ABI):
-  q [B, h_q, d] ; k_cache, v_cache [B, h_kv, cap, d] ; lens [B] int32 ;
+  q [B, h_q, d] ([B, T, h_q, d] for T = n_queries > 1) ; k_cache, v_cache [B, h_kv, cap, d] ;
+  lens [B] int32 ;
   k_new, v_new [B, h_kv, d] ; kv_scales [B, h_kv, 2] fp32 (fp8 / int8 only) ;
-  out [B, h_q, d] fp32.
+  out [B, h_q, d] fp32 ([B, T, h_q, d] for T > 1).
 """
 from __future__ import annotations
 
@@ -51,7 +52,7 @@ class _CDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("cap", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("block_rows", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("block_rows", ctypes.c_int32), ("n_queries", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -66,12 +67,19 @@ class Desc:
     kv_dtype: torch.dtype
     scale: float | None = None  # default 1/sqrt(d)
     block_rows: int = 0         # rows per workgroup at max_len; 0: one resident wave, equal shares
+    n_queries: int = 1          # query rows per sequence (> 1: multi-query causal decode)
 
     def c(self) -> _CDesc:
         scale = 1.0 / math.sqrt(self.d) if self.scale is None else self.scale
         return _CDesc(self.batch, self.h_q, self.h_kv, self.d, self.d, self.cap,
                       _TORCH_CODE.get(self.q_dtype, -1), _TORCH_CODE.get(self.kv_dtype, -1),
-                      float(scale), self.block_rows)
+                      float(scale), self.block_rows, self.n_queries)
+
+    def rows_shape(self) -> tuple:
+        """Shape of q and out: [B, h_q, d], or [B, T, h_q, d] with T = n_queries > 1."""
+        if self.n_queries > 1:
+            return (self.batch, self.n_queries, self.h_q, self.d)
+        return (self.batch, self.h_q, self.d)
 
 
 def _check(status: int, where: str) -> None:
@@ -167,7 +175,7 @@ def kv_append(desc: Desc, k_cache, v_cache, lens, k_new, v_new, workspace=None) 
 
 def _attn_args(desc: Desc, q, k_cache, v_cache, lens, kv_scales):
     dev = q.device
-    qp = _dev(q, "q", (desc.batch, desc.h_q, desc.d), desc.q_dtype, dev)
+    qp = _dev(q, "q", desc.rows_shape(), desc.q_dtype, dev)
     kc = _dev(k_cache, "k_cache", _cache_shapes(desc), desc.kv_dtype, dev)
     vc = _dev(v_cache, "v_cache", _cache_shapes(desc), desc.kv_dtype, dev)
     ln = _dev(lens, "lens", (desc.batch,), torch.int32, dev)
@@ -179,9 +187,10 @@ def _attn_args(desc: Desc, q, k_cache, v_cache, lens, kv_scales):
 
 
 def decode_attn_run(desc: Desc, q, k_cache, v_cache, lens, max_len: int, kv_scales, out, workspace) -> None:
-    """out[b, h] = softmax(scale * K[b, h/g, :lens[b]] q[b, h]) V[b, h/g, :lens[b]]."""
+    """out[b, h] = softmax(scale * K[b, h/g, :lens[b]] q[b, h]) V[b, h/g, :lens[b]]; with
+    desc.n_queries = T > 1, out[b, t, h] attends over the first lens[b] - T + 1 + t rows."""
     qp, kc, vc, ln, sc = _attn_args(desc, q, k_cache, v_cache, lens, kv_scales)
-    op = _dev(out, "out", (desc.batch, desc.h_q, desc.d), torch.float32, q.device)
+    op = _dev(out, "out", desc.rows_shape(), torch.float32, q.device)
     wp, wn, _ = _ws(workspace)
     cd = desc.c()
     _check(lib().decode_attn_run(ctypes.byref(cd), qp, kc, vc, ln, int(max_len), sc, op, wp, wn, _stream(q)),
@@ -200,7 +209,7 @@ def decode_attn_partial(desc: Desc, q, k_cache, v_cache, lens, max_len: int, kv_
 def decode_attn_combine(desc: Desc, lens, max_len: int, out, workspace) -> None:
     """Second stage: merge the splits by log-sum-exp weights into out."""
     ln = _dev(lens, "lens", (desc.batch,), torch.int32)
-    op = _dev(out, "out", (desc.batch, desc.h_q, desc.d), torch.float32, lens.device)
+    op = _dev(out, "out", desc.rows_shape(), torch.float32, lens.device)
     wp, wn, _ = _ws(workspace)
     cd = desc.c()
     _check(lib().decode_attn_combine(ctypes.byref(cd), ln, int(max_len), op, wp, wn, _stream(out)),
@@ -219,7 +228,7 @@ def decode_attn_append_run(desc: Desc, q, k_cache, v_cache, lens, k_new, v_new, 
     """One decode step: append the new K/V rows, attend over lens + 1 rows, lens += 1."""
     qp, kc, vc, ln, sc = _attn_args(desc, q, k_cache, v_cache, lens, kv_scales)
     kn, vn = _append_args(desc, k_cache, k_new, v_new)
-    op = _dev(out, "out", (desc.batch, desc.h_q, desc.d), torch.float32, q.device)
+    op = _dev(out, "out", desc.rows_shape(), torch.float32, q.device)
     wp, wn, _ = _ws(workspace)
     cd = desc.c()
     _check(lib().decode_attn_append_run(ctypes.byref(cd), qp, kc, vc, ln, kn, vn, int(max_len), sc, op, wp, wn,
@@ -240,7 +249,7 @@ def decode_attn_append_partial(desc: Desc, q, k_cache, v_cache, lens, k_new, v_n
 def decode_attn_append_combine(desc: Desc, lens, max_len: int, out, workspace) -> None:
     """Second stage of the fused step: merge into out, then lens += 1 where appended."""
     ln = _dev(lens, "lens", (desc.batch,), torch.int32)
-    op = _dev(out, "out", (desc.batch, desc.h_q, desc.d), torch.float32, lens.device)
+    op = _dev(out, "out", desc.rows_shape(), torch.float32, lens.device)
     wp, wn, _ = _ws(workspace)
     cd = desc.c()
     _check(lib().decode_attn_append_combine(ctypes.byref(cd), ln, int(max_len), op, wp, wn, _stream(out)),

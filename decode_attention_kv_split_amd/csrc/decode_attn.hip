@@ -252,10 +252,12 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
 // unit u are w in [owner(P_u), owner(P_u + L - 1)], owner(x) = ((x + 1) * N - 1) / T,
 // skipping any with an empty range.
 constexpr int kMaxBatch = 1024;
+constexpr int kMaxQueries = 1024;  // query rows per sequence in one call
 
 struct Partition {
     int batch, h_kv, tiles, max_len, nwg;
     int append_cap;  // > 0: this pass first appends one row per (sequence, KV head); the cache capacity
+    int nq;          // query rows per sequence (> 1: multi-query causal decode)
 };
 
 // Rows a pass attends over for a sequence whose stored length is L: with an append in the
@@ -264,7 +266,11 @@ struct Partition {
 __device__ __forceinline__ int attended_len(int L, int append_cap) {
     return (append_cap > 0 && L >= 0 && L < append_cap) ? L + 1 : L;
 }
-__device__ __forceinline__ int64_t unit_rows(int L, int max_len) { return (L >= 1 && L <= max_len) ? L : 0; }
+// Rows of a sequence of length L in each of its units; 0 (no work, output zeroed and flagged)
+// unless 1 <= L <= max_len and L holds the nq query positions.
+__device__ __forceinline__ int64_t unit_rows(int L, int max_len, int nq) {
+    return (L >= 1 && L >= nq && L <= max_len) ? L : 0;
+}
 __device__ __forceinline__ int64_t wg_start(int64_t w, int64_t T, int64_t N) { return w * T / N; }
 __device__ __forceinline__ int64_t wg_owner(int64_t x, int64_t T, int64_t N) { return ((x + 1) * N - 1) / T; }
 
@@ -280,7 +286,7 @@ __device__ void sequence_prefix(const int32_t *__restrict__ lens, const Partitio
     for (int i = 0; i < kMaxBatch / kBlock; ++i) {
         const int bb = threadIdx.x * per + i;
         local[i] = sum;
-        if (i < per && bb < pt.batch) sum += unit_rows(attended_len(lens[bb], pt.append_cap), pt.max_len) * upb;
+        if (i < per && bb < pt.batch) sum += unit_rows(attended_len(lens[bb], pt.append_cap), pt.max_len, pt.nq) * upb;
     }
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     int64_t incl = sum;
@@ -321,13 +327,30 @@ struct SplitArgs {
     int row_bytes;
 };
 
+// The query rows of a (sequence b, KV head kvh) are its g heads at each of the nq query
+// positions, g * nq rows taken position-major (row r: position r / g, head kvh * g + r % g);
+// a head tile holds rows h0 - kvh * g .. of them. For head slot hh of the tile: `row` indexes
+// the [d] vectors of q and out ([B, nq, h_q, d]), t is the query's position among the nq,
+// and the query attends over rows [0, slen - nq + 1 + t) of a sequence of slen rows (causal:
+// its own row and every earlier one). With nq = 1 that is head h0 + hh over all slen rows.
+struct QRow {
+    size_t row;
+    int lim;
+};
+__device__ __forceinline__ QRow query_row(const SplitArgs &a, int b, int kvh, int h0, int hh, int slen) {
+    const int g = a.h_q / a.pt.h_kv;
+    const int fr = h0 - kvh * g + hh;
+    const int t = fr / g;
+    return {((size_t)b * a.pt.nq + t) * a.h_q + kvh * g + fr % g, slen - a.pt.nq + 1 + t};
+}
+
 // Steps I-III over rows [r0, r1) of one (sequence b, KV head kvh) for query heads
 // h0 .. h0+GT-1, by the whole workgroup. The result (max, sum of exponentials, unnormalised
 // output; base-2 domain, V scale applied) goes to segment slot k of the partial arrays, or
 // normalised straight to out when `direct` (the segment is the whole unit).
 template <int KV, int D, int GT>
 __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
-                                               size_t k, bool direct) {
+                                               size_t k, bool direct, int slen) {
     using T = Kv<KV>;
     using Vec = typename T::Vec;
     constexpr int EPL = T::kEpl;
@@ -335,7 +358,6 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
     constexpr int RPL = kWave / LPR;     // rows per wave load
     constexpr int TILE = kUnroll * RPL;  // rows per wave per iteration
     constexpr int STEP = TILE * kWaves;  // rows per workgroup per iteration
-    const int h_q = a.h_q;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int grp = lane / LPR, sub = lane % LPR;
 
@@ -354,12 +376,15 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
     }
 
     // This lane's slice of q for the GT heads: fp32 values, or packed bf16 pairs for the
-    // bf16 dot instruction.
+    // bf16 dot instruction; each head's end of rows (the segment's, or the causal bound).
     float qf[GT][EPL];
     uint32_t qp[GT][EPL / 2];
+    int rend[GT];
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
-        const size_t qoff = ((size_t)b * h_q + h0 + h) * D + sub * EPL;
+        const QRow qr = query_row(a, b, kvh, h0, h, slen);
+        rend[h] = min(r1, qr.lim);
+        const size_t qoff = qr.row * D + sub * EPL;
         if constexpr (KV == DA_F32) {
             const float4 x = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.q) + qoff);
             qf[h][0] = x.x; qf[h][1] = x.y; qf[h][2] = x.z; qf[h][3] = x.w;
@@ -390,7 +415,7 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
         float s[GT][kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const bool valid = tbase + u * RPL + grp < r1;
+            const int row = tbase + u * RPL + grp;
             float kf[EPL];
             if constexpr (KV != DA_BF16) widen<KV>(kt[u], kf);
 #pragma unroll
@@ -408,7 +433,7 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
                     for (int e = 0; e < EPL; ++e) acc = fmaf(kf[e], qf[h][e], acc);
                 }
                 acc = group_sum<LPR>(acc) * sc;
-                s[h][u] = valid ? acc : -INFINITY;
+                s[h][u] = row < rend[h] ? acc : -INFINITY;
             }
         }
         // s becomes p = 2^(s - m_new); l and o are rescaled to the new running max.
@@ -512,7 +537,7 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
             O = fmaf(s_o[w][h][d], f, O);
         }
         if (direct) {
-            a.out[((size_t)b * h_q + h0 + h) * D + d] = O * vscale / Ls;
+            a.out[query_row(a, b, kvh, h0, h, slen).row * D + d] = O * vscale / Ls;
         } else {
             a.part_o[(k * GT + h) * D + d] = O * vscale;
             if (d == 0) { a.part_ml[(k * GT + h) * 2 + 0] = M; a.part_ml[(k * GT + h) * 2 + 1] = Ls; }
@@ -592,9 +617,10 @@ struct MfmaAttn {
     f32x4_t o[HT][NB];
     float sc;
     int lane, lr, lg, wave;
+    int lim[HT];  // end of the rows this lane's head (ht*16 + l%16) may see (causal bound)
 
     // q^T as the B operand of Step I: lane l holds q[head ht*16 + l%16][kb*32 + 8*(l/16) ..+8].
-    __device__ __forceinline__ void init(const SplitArgs &a, int b, int h0, float score_scale) {
+    __device__ __forceinline__ void init(const SplitArgs &a, int b, int kvh, int h0, int slen, float score_scale) {
         lane = threadIdx.x % kWave;
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
         lr = lane % 16;
@@ -603,12 +629,14 @@ struct MfmaAttn {
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             const int head = ht * 16 + lr;
+            const QRow qr = query_row(a, b, kvh, h0, head < GT ? head : 0, slen);
+            lim[ht] = qr.lim;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 uint4 x = {0u, 0u, 0u, 0u};
                 if (head < GT)
-                    x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) +
-                                                          ((size_t)b * a.h_q + h0 + head) * D + kb * 32 + 8 * lg);
+                    x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qr.row * D + kb * 32 +
+                                                          8 * lg);
                 qb[ht][kb] = __builtin_bit_cast(bf16x8_t, x);
             }
             m[ht] = kNegBig;
@@ -618,7 +646,8 @@ struct MfmaAttn {
         }
     }
 
-    // One tile of rows tb .. tb+15 (rows at or past r1 masked): ka = the K rows as A operands;
+    // One tile of rows tb .. tb+15 (rows at or past r1, or past a head's causal bound, masked):
+    // ka = the K rows as A operands;
     // vaddr(nb) = this lane's LDS address for the transpose read of d block nb.
     template <class VAddr>
     __device__ __forceinline__ void tile(const bf16x8_t (&ka)[KB], VAddr &&vaddr, int tb, int r1, float *s_c) {
@@ -631,8 +660,9 @@ struct MfmaAttn {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qb[ht][kb], sacc, 0, 0, 0);
             float x[4];
+            const int rend = min(r1, lim[ht]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * lg + i < r1) ? sacc[i] * sc : -INFINITY;
+            for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * lg + i < rend) ? sacc[i] * sc : -INFINITY;
             float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -679,8 +709,8 @@ struct MfmaAttn {
 
     // Merge the four waves pairwise through LDS ((0,2), (1,3), then (0,1)) and write the
     // segment's result: s_oo holds 2 * HT*16 * D floats, s_mm / s_ll kWaves * HT*16 each.
-    __device__ __forceinline__ void finish(const SplitArgs &a, int b, int h0, size_t k, bool direct, float vscale,
-                                           float *s_oo, float *s_mm, float *s_ll) {
+    __device__ __forceinline__ void finish(const SplitArgs &a, int b, int kvh, int h0, int slen, size_t k, bool direct,
+                                           float vscale, float *s_oo, float *s_mm, float *s_ll) {
         constexpr int HP = HT * 16;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {  // the lane groups share each head's max: sums add
@@ -732,7 +762,7 @@ struct MfmaAttn {
                     const int head = ht * 16 + 4 * lg + i;
                     if (head >= GT) continue;
                     const float M = s_mm[head], Ls = s_ll[head];
-                    const size_t row = (size_t)b * a.h_q + h0 + head;
+                    const size_t row = query_row(a, b, kvh, h0, head, slen).row;
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
                         const float v = o[ht][nb][i] * vscale;
@@ -756,7 +786,7 @@ struct MfmaAttn {
 // row-major in the wave's LDS tile for the transpose read.
 template <int KV, int D, int GT, int NBUF>
 __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
-                                                    size_t k, bool direct) {
+                                                    size_t k, bool direct, int slen) {
     static_assert(KV == DA_BF16 || KV == DA_FP8_E4M3FN, "MFMA flavour takes bf16 or fp8 caches");
     using LVec = typename std::conditional<KV == DA_BF16, uint4, uint2>::type;  // 8 elements
     using A = MfmaAttn<D, GT>;
@@ -798,7 +828,7 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
         vscale = a.kv_scales[slot * 2 + 1];
     }
     A at;
-    at.init(a, b, h0, sc);
+    at.init(a, b, kvh, h0, slen, sc);
     const int lane = at.lane, wave = at.wave, lr = at.lr, lg = at.lg;
     const int vrow = lane / VL, vcol = (lane % VL) * 8;
 
@@ -847,7 +877,7 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
             }
         }
     }
-    at.finish(a, b, h0, k, direct, vscale, s_oo, s_mm, s_ll);
+    at.finish(a, b, kvh, h0, slen, k, direct, vscale, s_oo, s_mm, s_ll);
 }
 
 // Matrix-core segment with workgroup-wide LDS stages filled by DMA (buffer_load ... lds), so
@@ -881,7 +911,7 @@ __device__ __forceinline__ int piece_key(int m) { return (m ^ (m >> 1)) & 1; }
 
 template <int KV, int D, int GT>
 __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
-                                                      size_t k, bool direct) {
+                                                      size_t k, bool direct, int slen) {
     static_assert(KV == DA_BF16 || Kv<KV>::kEsz == 1, "matrix-core flavour takes bf16 or 8-bit caches");
     constexpr int HT = (GT + 15) / 16;
     constexpr int KB = D / 32, NB = D / 16;
@@ -898,7 +928,6 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     constexpr int VM_STAGE = 2 * DPW;          // DMA ops of one stage per wave
     constexpr bool kLines = ROWB == 128;       // 8-bit codes, d = 128: whole-line DMA layout
     static_assert(NBLK % WPH == 0 && (HALF / 1024) % kWaves == 0, "stage split");
-    const int h_q = a.h_q;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int lr = lane % 16, lg = lane / 16;
     const int ht = wave % HT;  // this wave's head tile
@@ -919,16 +948,19 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
         sc *= a.kv_scales[slot * 2 + 0];
         vscale = a.kv_scales[slot * 2 + 1];
     }
-    // q^T of this wave's 16 heads as the B operand of Step I (zero past GT)
+    // q^T of this wave's 16 heads as the B operand of Step I (zero past GT), and the end of
+    // the rows this lane's head may see (the segment's, or the causal bound)
     bf16x8_t qb[KB];
+    int rend;
     {
         const int head = ht * 16 + lr;
+        const QRow qr = query_row(a, b, kvh, h0, head < GT ? head : 0, slen);
+        rend = min(r1, qr.lim);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             uint4 x = {0u, 0u, 0u, 0u};
             if (head < GT)
-                x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) +
-                                                      ((size_t)b * h_q + h0 + head) * D + kb * 32 + 8 * lg);
+                x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qr.row * D + kb * 32 + 8 * lg);
             qb[kb] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
@@ -1025,7 +1057,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                 const f32x4_t sacc = scores(st + blk * TILE, 0);
                 float x[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = (rb + 4 * lg + i < r1) ? sacc[i] * sc : -INFINITY;
+                for (int i = 0; i < 4; ++i) x[i] = (rb + 4 * lg + i < rend) ? sacc[i] * sc : -INFINITY;
                 bf16x4_t phi, plo;
                 softmax(x, phi, plo, 4);
                 const char *vt = st + HALF + blk * TILE;
@@ -1045,8 +1077,8 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                 float x[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    x[i] = (rb + 4 * lg + i < r1) ? s0[i] * sc : -INFINITY;
-                    x[4 + i] = (rb + 16 + 4 * lg + i < r1) ? s1[i] * sc : -INFINITY;
+                    x[i] = (rb + 4 * lg + i < rend) ? s0[i] * sc : -INFINITY;
+                    x[4 + i] = (rb + 16 + 4 * lg + i < rend) ? s1[i] * sc : -INFINITY;
                 }
                 bf16x8_t phi, plo;
                 softmax(x, phi, plo, 8);
@@ -1134,7 +1166,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
             const int hd = ht * 16 + 4 * lg + i;
             if (hd >= GT) continue;
             const float M = s_mm[wave][4 * lg + i], Ls = s_ll[wave][4 * lg + i];
-            const size_t row = (size_t)b * h_q + h0 + hd;
+            const size_t row = query_row(a, b, kvh, h0, hd, slen).row;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const float v = o[nb][i] * vscale;
@@ -1275,7 +1307,7 @@ __device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn 
             // another workgroup on this CU may hold, stale, in the vector L1: drop it
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
-        seg(wk.sb, wk.kvh, wk.h0, wk.r0, wk.r1, wk.k, wk.whole);
+        seg(wk.sb, wk.kvh, wk.h0, wk.r0, wk.r1, wk.k, wk.whole, wk.slen);
     }
 }
 
@@ -1284,8 +1316,8 @@ __device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn 
 // every segment leaves a partial result.
 template <int KV, int D, int GT, bool DIRECT>
 __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a) {
-    walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole) {
-        attend_segment<KV, D, GT>(a, b, kvh, h0, r0, r1, k, DIRECT && whole);
+    walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole, int slen) {
+        attend_segment<KV, D, GT>(a, b, kvh, h0, r0, r1, k, DIRECT && whole, slen);
     });
 }
 
@@ -1304,12 +1336,12 @@ template <int KV, int D, int GT, bool DIRECT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MfmaWaves<GT>::kMin)))
 void split_kv_attn_mfma_kernel(const SplitArgs a) {
     if constexpr (Kv<KV>::kEsz == 1) {
-        walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole) {
-            attend_segment_staged<KV, D, GT>(a, b, kvh, h0, r0, r1, k, DIRECT && whole);
+        walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole, int slen) {
+            attend_segment_staged<KV, D, GT>(a, b, kvh, h0, r0, r1, k, DIRECT && whole, slen);
         });
     } else {
-        walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole) {
-            attend_segment_mfma<KV, D, GT, kMfmaRing>(a, b, kvh, h0, r0, r1, k, DIRECT && whole);
+        walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole, int slen) {
+            attend_segment_mfma<KV, D, GT, kMfmaRing>(a, b, kvh, h0, r0, r1, k, DIRECT && whole, slen);
         });
     }
 }
@@ -1324,12 +1356,12 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     const float *__restrict__ part_o, float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt,
     Partition pt, int skip_single) {
     constexpr int SG = kCombineBlock / (D / 4);  // segment groups working side by side
-    const int bh = blockIdx.x;
-    const int b = bh / h_q, h = bh % h_q;
+    const int bh = blockIdx.x;  // output row ((b * nq) + query position tq) * h_q + head h
+    const int b = bh / (h_q * pt.nq), tq = bh / h_q % pt.nq, h = bh % h_q;
     const int L = attended_len(lens[b], pt.append_cap);
     if (lens_upd && h == 0 && threadIdx.x == 0) lens_upd[b] = L;
     float *dst = out + (size_t)bh * D;
-    if (L < 1 || L > pt.max_len) {
+    if (unit_rows(L, pt.max_len, pt.nq) == 0) {
         for (int d = threadIdx.x; d < D; d += kCombineBlock) dst[d] = 0.f;
         if (threadIdx.x == 0) atomicOr(err, DA_DEV_ERR_LEN_RANGE);
         return;
@@ -1339,7 +1371,7 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     const int64_t upb = (int64_t)pt.h_kv * pt.tiles;
     int64_t before = 0, total = 0;
     for (int bb = threadIdx.x; bb < pt.batch; bb += kCombineBlock) {
-        const int64_t r = unit_rows(attended_len(lens[bb], pt.append_cap), pt.max_len) * upb;
+        const int64_t r = unit_rows(attended_len(lens[bb], pt.append_cap), pt.max_len, pt.nq) * upb;
         total += r;
         if (bb < b) before += r;
     }
@@ -1357,7 +1389,8 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
 #pragma unroll
     for (int w = 0; w < kCombineBlock / kWave; ++w) { before += s_red[0][w]; total += s_red[1][w]; }
 
-    const int g = h_q / pt.h_kv, kvh = h / g, t = (h % g) / gt, hh = h % gt;
+    // the query's row among its group's g * nq rows, its head tile and slot
+    const int g = h_q / pt.h_kv, kvh = h / g, fr = tq * g + h % g, t = fr / gt, hh = fr % gt;
     const int64_t ul = (int64_t)kvh * pt.tiles + t;
     const int64_t u = b * upb + ul;
     const int64_t P = before + ul * L, N = pt.nwg;
@@ -1466,8 +1499,14 @@ int validate(const da_desc *d) {
                     (d->q_dtype == DA_BF16 && d->kv_dtype == DA_FP8_E4M3FN) ||
                     (d->q_dtype == DA_BF16 && d->kv_dtype == DA_INT8);
     if (!ok) return fail(DA_ERR_UNSUPPORTED, "dtype pair (q %d, kv %d) is not built", d->q_dtype, d->kv_dtype);
+    if (d->n_queries < 0 || d->n_queries > kMaxQueries)
+        return fail(DA_ERR_INVALID_ARG, "n_queries must be in [0, %d] (got %d)", kMaxQueries, d->n_queries);
     return DA_OK;
 }
+
+// Query rows per sequence (0 and 1 both mean single-query decode), and per KV group.
+int n_queries(const da_desc *d) { return d->n_queries > 1 ? d->n_queries : 1; }
+int group_rows(const da_desc *d) { return d->h_q / d->h_kv * n_queries(d); }
 
 // Workspace layout: [error word, padded to 256 B][segment (max, sum) pairs,
 // (N + units) * GT * 2 fp32][segment output rows, (N + units) * GT * d_v fp32], each section
@@ -1483,9 +1522,9 @@ struct Plan {
 // (fewer than 16 heads pad the 16-wide head tile with zero queries: the matrix cores still
 // take the arithmetic off the vector ALUs, measured equal or faster at g = 4); everything
 // else runs on the vector ALUs with 4, 2 or 1.
-bool use_mfma(const da_desc *d) { return d->kv_dtype != DA_F32 && (d->h_q / d->h_kv) % 4 == 0; }
+bool use_mfma(const da_desc *d) { return d->kv_dtype != DA_F32 && group_rows(d) % 4 == 0; }
 int heads_per_block(const da_desc *d) {
-    const int g = d->h_q / d->h_kv;
+    const int g = group_rows(d);
     if (use_mfma(d)) return g % 32 == 0 ? 32 : g % 16 == 0 ? 16 : g % 8 == 0 ? 8 : 4;
     return g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
 }
@@ -1553,7 +1592,7 @@ int make_plan(const da_desc *d, int max_len, Plan *p) {
         return fail(DA_ERR_INVALID_ARG, "max_len (%d) must be in [1, cap = %d]", max_len, d->cap);
     p->mfma = use_mfma(d);
     p->gt = heads_per_block(d);
-    p->tiles = d->h_q / d->h_kv / p->gt;
+    p->tiles = group_rows(d) / p->gt;
     const int64_t units = (int64_t)d->batch * d->h_kv * p->tiles;
     const int64_t rows_max = units * max_len;  // rows of all units at max_len
     int64_t nwg;
@@ -1636,6 +1675,7 @@ Partition partition_of(const da_desc *desc, const Plan &p, int max_len, bool app
     pt.max_len = max_len;
     pt.nwg = p.nwg;
     pt.append_cap = append ? desc->cap : 0;
+    pt.nq = n_queries(desc);
     return pt;
 }
 
@@ -1651,6 +1691,9 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     if (!q || !k_cache || !v_cache || !lens || !workspace)
         return fail(DA_ERR_INVALID_ARG, "%s: a buffer pointer is NULL", who);
     const bool append = k_new || v_new;
+    if (append && n_queries(desc) > 1)
+        return fail(DA_ERR_UNSUPPORTED, "%s: the fused append takes one query per sequence (n_queries %d)", who,
+                    desc->n_queries);
     if (append && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)))
         return fail(DA_ERR_INVALID_ARG, "%s: k_new and v_new must both be 16-byte aligned device pointers", who);
     if ((desc->kv_dtype == DA_FP8_E4M3FN || desc->kv_dtype == DA_INT8) && !kv_scales)
@@ -1701,7 +1744,10 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
     const float *ml = reinterpret_cast<const float *>(ws + p.ml_off);
     const float *po = reinterpret_cast<const float *>(ws + p.o_off);
     int32_t *err = reinterpret_cast<int32_t *>(ws);
-    const dim3 grid(desc->batch * desc->h_q);
+    if (append && n_queries(desc) > 1)
+        return fail(DA_ERR_UNSUPPORTED, "%s: the fused append takes one query per sequence (n_queries %d)", who,
+                    desc->n_queries);
+    const dim3 grid(desc->batch * n_queries(desc) * desc->h_q);
     const Partition pt = partition_of(desc, p, max_len, append);
     // appending: stored lengths from the split kernel's copy, new lengths written to lens
     const int32_t *lsrc = append ? reinterpret_cast<const int32_t *>(ws + p.lens_off) : lens;

@@ -11,13 +11,14 @@
  * cache at its row-major offset (same page, §5 KV-cache accumulation).
  *
  * Layouts (all row-major, contiguous; the same page's §4 gamma offsets lifted to rank 4):
- *   q        [batch, h_q, d_k]          element type desc->q_dtype
+ *   q        [batch, h_q, d_k]          element type desc->q_dtype ([batch, T, h_q, d_k] for
+ *                                       T = desc->n_queries > 1 query rows per sequence)
  *   k_cache  [batch, h_kv, cap, d_k]    element type desc->kv_dtype;
  *                                       element (b,kvh,l,j) at ((b*h_kv+kvh)*cap+l)*d_k+j
  *   v_cache  [batch, h_kv, cap, d_v]    element type desc->kv_dtype
  *   lens     [batch] int32              rows currently in each sequence (device memory)
  *   kv_scales[batch, h_kv, 2] fp32      (K scale, V scale) per slot; 8-bit caches only
- *   out      [batch, h_q, d_v] fp32
+ *   out      [batch, h_q, d_v] fp32     ([batch, T, h_q, d_v] for T > 1)
  * For an fp8 cache the value of an element is decode_e4m3fn(code) * its slot's scale; for
  * an int8 cache it is the two's-complement code * its slot's scale (the decode-attention
  * roofline page: 8-bit KV, fp8 or int8, halves the bytes each step reads).
@@ -56,18 +57,30 @@ extern "C" {
 /* Device-side error bits, ORed into the workspace's error word. */
 #define DA_DEV_ERR_APPEND_FULL 1 /* kv_append: lens[b] outside [0, cap); row b not written,
                                     lens[b] unchanged */
-#define DA_DEV_ERR_LEN_RANGE 2   /* decode: lens[b] outside [1, max_len]; out[b] zeroed */
+#define DA_DEV_ERR_LEN_RANGE 2   /* decode: lens[b] outside [max(1, n_queries), max_len]; out[b] zeroed */
 
 typedef enum { DA_F32 = 0, DA_BF16 = 1, DA_FP8_E4M3FN = 2, DA_INT8 = 3 } da_dtype;
 
 /*
  * Problem descriptor. Supported: d_k == d_v in {64, 128}; (q_dtype, kv_dtype) in
  * {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN), (BF16, INT8)}; any h_q that is a
- * multiple of h_kv; batch <= 1024. scale is the factor of Step I (1/sqrt(d_k) in the page's setting), applied
- * once. Work partition: the cache rows of all (sequence, KV head) pairs, taken in order,
- * are cut into equal contiguous shares, one per workgroup. block_rows = 0 lets the library
- * use one share per workgroup that fits on the device at once; block_rows > 0 asks for
- * shares of about block_rows rows at max_len instead.
+ * multiple of h_kv; batch <= 1024. scale is the factor of Step I (1/sqrt(d_k) in the page's
+ * setting), applied once. Work partition: the cache rows of all (sequence, KV head) pairs,
+ * taken in order, are cut into equal contiguous shares, one per workgroup. block_rows = 0
+ * lets the library use one share per workgroup that fits on the device at once;
+ * block_rows > 0 asks for shares of about block_rows rows at max_len instead.
+ *
+ * n_queries (T; 0 or 1: single-query decode, at most 1024) is the number of query rows per
+ * sequence, for speculative decoding or a chunked prefill: q and out are then
+ * [batch, T, h_q, d], and query t of sequence b, at position lens[b] - T + t, attends over
+ * rows [0, lens[b] - T + 1 + t) of the cache (causal: its own row and every earlier one; the
+ * T newest rows are the queries' own keys, already in the cache). Page "MoA-Structured Decode
+ * Attention", introduction (the decode form is the forward form with the query-row index
+ * fixed to the current step; here it spans the last T steps) and page "Phase 3, Section 6:
+ * StoryLM-0 head-parallel attention", §3 (softmax over the key axis of the scaled scores
+ * plus a mask, T query rows). Each K and V row is still read once for all g * T query rows
+ * of its group. lens[b] must be at least T (else the device error DA_DEV_ERR_LEN_RANGE).
+ * The fused-append entry points take T = 1 only.
  */
 typedef struct {
     int32_t batch;
@@ -80,6 +93,7 @@ typedef struct {
     int32_t kv_dtype; /* da_dtype */
     float scale;
     int32_t block_rows;
+    int32_t n_queries; /* query rows per sequence; 0 or 1 = single-query decode */
 } da_desc;
 
 /*

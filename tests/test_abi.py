@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def _desc(**kw):
     base = dict(batch=2, h_q=8, h_kv=2, d_k=128, d_v=128, cap=1024, q_dtype=1, kv_dtype=1,
-                scale=0.088, block_rows=0)
+                scale=0.088, block_rows=0, n_queries=0)
     base.update(kw)
     return da._CDesc(**base)
 
@@ -68,6 +68,8 @@ def _ws_size(lib, desc, max_len):
     (dict(block_rows=-1), 100, -1),            # negative workgroup share
     (dict(batch=1025), 100, -2),               # more sequences than one call takes
     (dict(scale=float("nan")), 100, -1),
+    (dict(n_queries=-1), 100, -1),             # negative query rows
+    (dict(n_queries=1025), 100, -1),           # more query rows per sequence than one call takes
 ])
 def test_invalid_descriptors_are_rejected(lib, kw, max_len, code):
     rc, _ = _ws_size(lib, _desc(**kw), max_len)
@@ -175,3 +177,21 @@ def test_stream_read_rejects_bad_sizes(lib):
     assert lib.da_stream_read(ctypes.c_void_p(0x10008), 1024, FAKE, None) == -1  # misaligned
     assert lib.da_stream_read(FAKE, 0, FAKE, None) == -1
     assert lib.da_stream_read(None, 1024, FAKE, None) == -1
+
+
+def test_multi_query_plan_and_limits(lib):
+    """T query rows per sequence multiply the rows of each KV group: g * T picks the flavour and
+    the head tile (g = 2, T = 2 -> 4 rows on the matrix cores; g = 1, T = 3 -> vector ALUs), the
+    workspace grows with the units, and the fused append refuses T > 1."""
+    assert _plan(lib, _desc(h_q=4, h_kv=2, n_queries=2), 100)[2] == 4
+    assert _plan(lib, _desc(h_q=2, h_kv=2, n_queries=3), 100)[2] == 1
+    assert _plan(lib, _desc(h_q=32, h_kv=8, n_queries=4), 100)[2] == 16
+    assert _plan(lib, _desc(h_q=32, h_kv=1, n_queries=8), 100)[2] == 32
+    one = _ws_size(lib, _desc(h_q=32, h_kv=8), 1000)[1]
+    four = _ws_size(lib, _desc(h_q=32, h_kv=8, n_queries=4), 1000)[1]
+    assert four > one > 0
+    d = _desc(n_queries=2)
+    rc, n = _ws_size(lib, d, 100)
+    assert lib.decode_attn_append_run(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, None, FAKE, FAKE,
+                                      n, None) == -2
+    assert lib.decode_attn_append_combine(ctypes.byref(d), FAKE, 100, FAKE, FAKE, n, None) == -2

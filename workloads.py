@@ -89,6 +89,10 @@ WORKLOADS = {
     # the same shape with symmetric int8 KV and per-slot scales
     "gqa8_int8": Workload("gqa8_int8", 32, 64, 8, 128, 16384, "bf16", "int8",
                           ("const", 16384), 0, 6, _inv_sqrt(128)),
+    # the GQA shape verifying 4 speculative tokens per sequence: 4 query rows, causal over the
+    # 4 newest rows (already in the cache)
+    "gqa8_mq4_bf16": Workload("gqa8_mq4_bf16", 16, 32, 8, 128, 32768, "bf16", "bf16",
+                              ("uniform", 512, 32768), 0, 7, _inv_sqrt(128), nq=4),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn,
