@@ -78,9 +78,10 @@ typedef enum { DA_F32 = 0, DA_BF16 = 1, DA_FP8_E4M3FN = 2, DA_INT8 = 3 } da_dtyp
  * Attention", introduction (the decode form is the forward form with the query-row index
  * fixed to the current step; here it spans the last T steps) and page "Phase 3, Section 6:
  * StoryLM-0 head-parallel attention", §3 (softmax over the key axis of the scaled scores
- * plus a mask, T query rows). Each K and V row is still read once for all g * T query rows
- * of its group. lens[b] must be at least T (else the device error DA_DEV_ERR_LEN_RANGE).
- * The fused-append entry points take T = 1 only.
+ * plus a mask, T query rows). The g * T query rows of a KV group share each K and V row
+ * read: it is read once per head tile of up to 32 of them, i.e. once when g * T <= 32.
+ * lens[b] must be at least T (else the device error DA_DEV_ERR_LEN_RANGE). The fused-append
+ * entry points take T = 1 only.
  */
 typedef struct {
     int32_t batch;

@@ -46,6 +46,8 @@ CASES = [
     ("fp8", 128, 16, 2, 4, 0),       # fp8, LDS stages, 32-row tiles (two head tiles)
     ("int8", 128, 8, 1, 2, 37),      # int8, LDS stages, 16-row tiles, many segments
     ("int8", 64, 12, 4, 5, 0),       # int8 d = 64, g*T = 15: vector ALUs
+    ("bf16", 128, 8, 2, 64, 0),      # a 64-row prefill chunk: g*T = 256, eight 32-row tiles per KV head
+    ("fp8", 128, 4, 4, 40, 500),     # fp8 chunk of 40 rows, MHA: g*T = 40 -> 8-row tiles
 ]
 
 
