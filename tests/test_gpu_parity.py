@@ -327,3 +327,15 @@ def test_stream_read_reads_every_byte_once():
         part = words[w * chunk // 4:min((w + 1) * chunk, n) // 4]
         expect.append(float(np.bitwise_xor.reduce(part)) if part.size else 0.0)
     assert np.array_equal(sink.cpu().numpy(), np.array(expect, dtype=np.float32))
+
+
+def test_largest_batch_and_short_sequences():
+    """The largest batch one call takes (1024 sequences, the prefix over lengths spread over
+    every thread of the workgroup), with ragged lengths from 1 row up, on both flavours."""
+    for h_q in (8, 2):  # g = 4: matrix cores; g = 1: vector ALUs
+        w = W(B=1024, h_q=h_q, h_kv=2, d=64, cap=96, lens=("uniform", 1, 96), seed=90 + h_q)
+        c = workloads.generate(w)
+        log(f"case batch 1024 h_q={h_q}")
+        out, _, _, err = run_gpu(w, c)
+        assert err == 0
+        check_close(out, oracle_out(w, c), "bf16", f"B=1024 h_q={h_q}")
