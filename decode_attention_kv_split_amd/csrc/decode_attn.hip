@@ -166,16 +166,38 @@ __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+// Exchanges between the four 16-lane rows of a wave by v_permlane16_swap / v_permlane32_swap
+// (vector ALU instructions, a few cycles) instead of ds_bpermute (a round trip through the LDS
+// unit). With both operands the same value x, the swap of rows leaves lane l holding x of
+// lanes l and l ^ 16 (one in each result), and the swap of halves x of lanes l and l ^ 32
+// (checked on the device for every lane).
+__device__ __forceinline__ float xor16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over each aligned group of LPR consecutive lanes; every lane gets its group's sum.
 // quad_perm [1,0,3,2] and [2,3,0,1] sum a quad; row_half_mirror pairs quads inside
-// 8 lanes; row_mirror pairs halves inside a 16-lane row; 32 needs a cross-row swizzle.
+// 8 lanes; row_mirror pairs halves inside a 16-lane row; 32 adds the neighbouring row.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float x) {
     if constexpr (LPR >= 2) x += dpp<0xB1>(x);
     if constexpr (LPR >= 4) x += dpp<0x4E>(x);
     if constexpr (LPR >= 8) x += dpp<0x141>(x);
     if constexpr (LPR >= 16) x += dpp<0x140>(x);
-    if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
+    if constexpr (LPR >= 32) x = xor16_sum(x);
     return x;
 }
 
@@ -664,8 +686,7 @@ struct MfmaAttn {
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * lg + i < rend) ? sacc[i] * sc : -INFINITY;
             float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            tmax = xor32_max(xor16_max(tmax));
             const float mn = fmaxf(m[ht], tmax);
             corr[ht] = __builtin_amdgcn_exp2f(m[ht] - mn);
             grew |= mn > m[ht];
@@ -714,8 +735,7 @@ struct MfmaAttn {
         constexpr int HP = HT * 16;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {  // the lane groups share each head's max: sums add
-            lp[ht] += __shfl_xor(lp[ht], 16);
-            lp[ht] += __shfl_xor(lp[ht], 32);
+            lp[ht] = xor32_sum(xor16_sum(lp[ht]));
         }
         __syncthreads();  // every wave is done with the LDS the merge reuses
         if (lg == 0) {
@@ -999,8 +1019,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     auto softmax = [&](float *x, auto &phi, auto &plo, int nr) {
         float tmax = x[0];
         for (int i = 1; i < nr; ++i) tmax = fmaxf(tmax, x[i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = xor32_max(xor16_max(tmax));
         const float mn = fmaxf(m, tmax);
         const float corr = __builtin_amdgcn_exp2f(m - mn);
         const bool grew = mn > m;
@@ -1126,8 +1145,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
 
     // Merge: lane groups share each head's max (sums add); then waves holding the same head
     // tile merge through LDS and one wave per head tile writes.
-    lp += __shfl_xor(lp, 16);
-    lp += __shfl_xor(lp, 32);
+    lp = xor32_sum(xor16_sum(lp));
     __syncthreads();
     float *s_oo = reinterpret_cast<float *>(s_a);  // [2][16][D] floats, reusing stage a
     if (lg == 0) { s_mm[wave][lr] = m; s_ll[wave][lr] = lp; }
