@@ -621,11 +621,13 @@ __device__ __forceinline__ uint4 to_bf16x8(const typename std::conditional<KV ==
 //     heads is the B operand. The result gives lane l the scores of rows 4*(l/16)+i (i < 4)
 //     for head l%16.
 //   * Step II online on that layout: the tile max per head reduces over the 4 lane groups;
-//     O is rescaled (through a 16-float LDS transpose) only when some head's max grew.
-//   * Step III as O += P . V_tile with v_mfma_f32_16x16x16_bf16: the score layout above is
-//     exactly the A-operand layout of P; V, staged in LDS as bf16, is read back as the B
-//     operand with ds_read_b64_tr_b16. P is split into bf16 hi + lo parts (two MFMAs) so that
-//     P.V keeps ~16 bits of P's precision.
+//     O is rescaled only when some head's max grew.
+//   * Step III transposed, O^T += V_tile^T . P^T with v_mfma_f32_16x16x16_bf16: V, staged in
+//     LDS as bf16 and read back with ds_read_b64_tr_b16 (lane l: d column l%16, rows
+//     4*(l/16) ..), is the A operand, and the score layout above is exactly the B-operand
+//     layout of P^T. Lane l then holds d = 4*(l/16)+i of head l%16: the head's rescale factor
+//     is its own, with no exchange between lanes. P is split into bf16 hi + lo parts (two
+//     MFMAs) so that P.V keeps ~16 bits of P's precision.
 // GT = 4, 8, 16 or 32 heads (HT = 1 or 2 MFMA tiles of 16; heads past GT are zero padding).
 template <int D, int GT>
 struct MfmaAttn {
@@ -672,7 +674,7 @@ struct MfmaAttn {
     // ka = the K rows as A operands;
     // vaddr(nb) = this lane's LDS address for the transpose read of d block nb.
     template <class VAddr>
-    __device__ __forceinline__ void tile(const bf16x8_t (&ka)[KB], VAddr &&vaddr, int tb, int r1, float *s_c) {
+    __device__ __forceinline__ void tile(const bf16x8_t (&ka)[KB], VAddr &&vaddr, int tb, int r1) {
         bool grew = false;
         float corr[HT];
         bf16x4_t phi[HT], plo[HT];
@@ -702,34 +704,34 @@ struct MfmaAttn {
             }
         }
         if (__builtin_amdgcn_ballot_w64(grew)) {
-            // corr is held per head = l%16; O rows are heads 4*(l/16)+i: transpose via LDS
-            if (lg == 0) {
+            // O is held transposed (d rows 4*(l/16)+i of head l%16), so the head's factor is
+            // this lane's own
 #pragma unroll
-                for (int ht = 0; ht < HT; ++ht) s_c[ht * 16 + lr] = corr[ht];
-            }
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                const float4 c4 = *reinterpret_cast<const float4 *>(&s_c[ht * 16 + 4 * lg]);
+            for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    o[ht][nb][0] *= c4.x; o[ht][nb][1] *= c4.y; o[ht][nb][2] *= c4.z; o[ht][nb][3] *= c4.w;
+                    o[ht][nb][0] *= corr[ht]; o[ht][nb][1] *= corr[ht]; o[ht][nb][2] *= corr[ht]; o[ht][nb][3] *= corr[ht];
                 }
-            }
         }
+        // O^T += V_tile^T . P^T: the transposed V read (lane l: column l%16 of d block nb, rows
+        // 4*(l/16) ..) is the A operand of V^T, the score layout the B operand of P^T
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const i16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)vaddr(nb));
             const bf16x4_t bv = __builtin_bit_cast(bf16x4_t, t);
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
-                o[ht][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi[ht], bv, o[ht][nb], 0, 0, 0);
-                o[ht][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo[ht], bv, o[ht][nb], 0, 0, 0);
+                o[ht][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bv, phi[ht], o[ht][nb], 0, 0, 0);
+                o[ht][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bv, plo[ht], o[ht][nb], 0, 0, 0);
             }
         }
     }
 
     // Merge the four waves pairwise through LDS ((0,2), (1,3), then (0,1)) and write the
-    // segment's result: s_oo holds 2 * HT*16 * D floats, s_mm / s_ll kWaves * HT*16 each.
+    // segment's result: s_oo holds 2 * HT*16 rows of kRowO floats (one head's D outputs and a
+    // 16-byte pad, so that the 16 heads of a row-exchange land on distinct banks), s_mm / s_ll
+    // kWaves * HT*16 each.
+    static constexpr int kRowO = D + 4;
     __device__ __forceinline__ void finish(const SplitArgs &a, int b, int kvh, int h0, int slen, size_t k, bool direct,
                                            float vscale, float *s_oo, float *s_mm, float *s_ll) {
         constexpr int HP = HT * 16;
@@ -742,29 +744,36 @@ struct MfmaAttn {
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) { s_mm[wave * HP + ht * 16 + lr] = m[ht]; s_ll[wave * HP + ht * 16 + lr] = lp[ht]; }
         }
+        // O^T layout: lane l holds d = nb*16 + 4*(l/16) + i of head ht*16 + l%16
         auto put_o = [&](int slot) {
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) s_oo[(slot * HP + ht * 16 + 4 * lg + i) * D + nb * 16 + lr] = o[ht][nb][i];
+                    *reinterpret_cast<f32x4_t *>(&s_oo[(slot * HP + ht * 16 + lr) * kRowO + nb * 16 + 4 * lg]) = o[ht][nb];
         };
+        // The merged (max, sum) of each head also stay in registers (every lane of the head
+        // computes the same values): the lanes never read back what another lane of their own
+        // wave stored without a barrier in between.
+        float mres[HT], lres[HT];
         auto merge_o = [&](int slot, int other) {
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
+            for (int ht = 0; ht < HT; ++ht) {
+                const int head = ht * 16 + lr;
+                const float ms = s_mm[wave * HP + head], mo = s_mm[other * HP + head];
+                const float M = fmaxf(ms, mo);
+                const float fs = __builtin_amdgcn_exp2f(ms - M), fo = __builtin_amdgcn_exp2f(mo - M);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int head = ht * 16 + 4 * lg + i;
-                    const float ms = s_mm[wave * HP + head], mo = s_mm[other * HP + head];
-                    const float M = fmaxf(ms, mo);
-                    const float fs = __builtin_amdgcn_exp2f(ms - M), fo = __builtin_amdgcn_exp2f(mo - M);
+                for (int nb = 0; nb < NB; ++nb) {
+                    const f32x4_t x = *reinterpret_cast<const f32x4_t *>(&s_oo[(slot * HP + head) * kRowO + nb * 16 + 4 * lg]);
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        o[ht][nb][i] = fmaf(o[ht][nb][i], fs, s_oo[(slot * HP + head) * D + nb * 16 + lr] * fo);
-                    const float Ls = fmaf(s_ll[wave * HP + head], fs, s_ll[other * HP + head] * fo);
-                    if (lr == 0) { s_mm[wave * HP + head] = M; s_ll[wave * HP + head] = Ls; }
+                    for (int i = 0; i < 4; ++i) o[ht][nb][i] = fmaf(o[ht][nb][i], fs, x[i] * fo);
                 }
+                const float Ls = fmaf(s_ll[wave * HP + head], fs, s_ll[other * HP + head] * fo);
+                mres[ht] = M;
+                lres[ht] = Ls;
+                if (lg == 0) { s_mm[wave * HP + head] = M; s_ll[wave * HP + head] = Ls; }
+            }
         };
         __syncthreads();
         if (wave >= 2) put_o(wave - 2);
@@ -776,26 +785,24 @@ struct MfmaAttn {
         if (wave == 0) {
             merge_o(0, 1);
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
+            for (int ht = 0; ht < HT; ++ht) {
+                const int head = ht * 16 + lr;
+                if (head >= GT) continue;
+                const float M = mres[ht], Ls = lres[ht];
+                const size_t row = query_row(a, b, kvh, h0, head, slen).row;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int head = ht * 16 + 4 * lg + i;
-                    if (head >= GT) continue;
-                    const float M = s_mm[head], Ls = s_ll[head];
-                    const size_t row = query_row(a, b, kvh, h0, head, slen).row;
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        const float v = o[ht][nb][i] * vscale;
-                        if (direct)
-                            a.out[row * D + nb * 16 + lr] = v / Ls;
-                        else
-                            a.part_o[(k * GT + head) * D + nb * 16 + lr] = v;
-                    }
-                    if (!direct && lr == 0) {
-                        a.part_ml[(k * GT + head) * 2 + 0] = M;
-                        a.part_ml[(k * GT + head) * 2 + 1] = Ls;
-                    }
+                for (int nb = 0; nb < NB; ++nb) {
+                    const f32x4_t v = o[ht][nb] * vscale;
+                    if (direct)
+                        *reinterpret_cast<f32x4_t *>(&a.out[row * D + nb * 16 + 4 * lg]) = v / Ls;
+                    else
+                        *reinterpret_cast<f32x4_t *>(&a.part_o[(k * GT + head) * D + nb * 16 + 4 * lg]) = v;
                 }
+                if (!direct && lg == 0) {
+                    a.part_ml[(k * GT + head) * 2 + 0] = M;
+                    a.part_ml[(k * GT + head) * 2 + 1] = Ls;
+                }
+            }
         }
         __syncthreads();  // the LDS arrays are reused by the next segment
     }
@@ -853,8 +860,7 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
     const int vrow = lane / VL, vcol = (lane % VL) * 8;
 
     __shared__ __align__(16) uint16_t s_v[kWaves][TR * VROW];
-    __shared__ __align__(16) float s_c[kWaves][HP];
-    __shared__ __align__(16) float s_oo[2 * HP * D];
+    __shared__ __align__(16) float s_oo[2 * HP * A::kRowO];
     __shared__ float s_mm[kWaves * HP], s_ll[kWaves * HP];
 
     auto process = [&](const LVec (&kt)[KB], const LVec (&vt)[VLD], int t) {
@@ -867,7 +873,7 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
         at.tile(ka, [&](int nb) {
             return (__attribute__((address_space(3))) uint16_t *)&s_v[wave][0] +
                    (4 * lg + lr / 4) * VROW + nb * 16 + 4 * (lane % 4);
-        }, tile_row(t), tile_end(t), &s_c[wave][0]);
+        }, tile_row(t), tile_end(t));
     };
     // Software pipeline over a ring of NBUF register buffers: NBUF - 1 tiles of this wave are
     // in flight while one is computed. The ring is unrolled so every buffer index is static;
@@ -1155,6 +1161,9 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
 #pragma unroll
             for (int i = 0; i < 4; ++i) s_oo[(slot_ * 16 + 4 * lg + i) * D + nb * 16 + lr] = o[nb][i];
     };
+    // the merged (max, sum) of this lane's heads also stay in registers (no lane reads back
+    // what another lane of its own wave stored without a barrier in between)
+    float mres[4], lres[4];
     auto merge_o = [&](int slot_, int other) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1165,6 +1174,8 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) o[nb][i] = fmaf(o[nb][i], fs, s_oo[(slot_ * 16 + hd) * D + nb * 16 + lr] * fo);
             const float Ls = fmaf(s_ll[wave][hd], fs, s_ll[other][hd] * fo);
+            mres[i] = M;
+            lres[i] = Ls;
             if (lr == 0) { s_mm[wave][hd] = M; s_ll[wave][hd] = Ls; }
         }
     };
@@ -1183,7 +1194,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
         for (int i = 0; i < 4; ++i) {
             const int hd = ht * 16 + 4 * lg + i;
             if (hd >= GT) continue;
-            const float M = s_mm[wave][4 * lg + i], Ls = s_ll[wave][4 * lg + i];
+            const float M = mres[i], Ls = lres[i];
             const size_t row = query_row(a, b, kvh, h0, hd, slen).row;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
