@@ -73,6 +73,11 @@ CASES = [
     ("int8", 128, 8, 8, ("uniform", 1, 1500), 0),
     ("int8", 64, 8, 1, ("uniform", 1, 1500), 512),
     ("int8", 128, 64, 2, ("uniform", 1, 1500), 0),
+    # 16 heads per workgroup over short sequences: whole units written directly by one
+    # workgroup (the merged sums must reach every lane of a head)
+    ("bf16", 128, 32, 2, ("uniform", 1, 40), 0),
+    ("fp8", 128, 32, 2, ("uniform", 1, 40), 0),
+    ("bf16", 64, 64, 4, ("uniform", 1, 100), 0),
 ]
 
 
