@@ -928,7 +928,9 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
 //     (fp8 or int8; Step III by v_mfma_f32_16x16x32_bf16 with P's 8 rows per lane taken from
 //     the block's two score tiles, V read as codes by ds_read_b64_tr_b8 and widened to bf16 in
 //     registers, exactly). Step I always uses v_mfma_f32_16x16x32_bf16 (8-bit K widened to bf16
-//     after its LDS read).
+//     after its LDS read). Step III is computed transposed, O^T += V^T . P^T (the V read is the
+//     A operand, the score layout the B operand), so that each lane holds d rows of its own
+//     head and rescales them by that head's factor with no exchange.
 //   * At the end the waves holding the same head tile merge through LDS.
 // Swizzle key of the piece (8 rows of 128 bytes) at index m of a stage: flips the parity of
 // every chunk index in pieces whose Gray code is odd, so that pieces 2t / 2t+1 (one K tile)
@@ -961,7 +963,6 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
 
     __shared__ __align__(16) char s_a[2 * HALF];
     __shared__ __align__(16) char s_b[2 * HALF];
-    __shared__ __align__(16) float s_c[kWaves][16];
     __shared__ float s_mm[kWaves][16], s_ll[kWaves][16];
     typedef __attribute__((address_space(3))) char lds_char;
 
@@ -1039,12 +1040,10 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
         }
         lp = fmaf(lp, corr, ps);
         if (__builtin_amdgcn_ballot_w64(grew)) {
-            // corr is held per head = l%16; O rows are heads 4*(l/16)+i: transpose via LDS
-            if (lg == 0) s_c[wave][lr] = corr;
-            const float4 c4 = *reinterpret_cast<const float4 *>(&s_c[wave][4 * lg]);
+            // O is held transposed (d rows 4*(l/16)+i of head l%16): the factor is in-lane
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                o[nb][0] *= c4.x; o[nb][1] *= c4.y; o[nb][2] *= c4.z; o[nb][3] *= c4.w;
+                o[nb][0] *= corr; o[nb][1] *= corr; o[nb][2] *= corr; o[nb][3] *= corr;
             }
         }
     };
@@ -1092,8 +1091,8 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                     const i16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) i16x4_t *)(lds_char *)(vt + ((d0 / 8) * 16 + r) * 16 + (d0 % 8) * 2));
                     const bf16x4_t bv = __builtin_bit_cast(bf16x4_t, t);
-                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, o[nb], 0, 0, 0);
-                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, o[nb], 0, 0, 0);
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bv, phi, o[nb], 0, 0, 0);
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bv, plo, o[nb], 0, 0, 0);
                 }
             } else {
                 // rows of lane group g: 4g+e (tile 0) and 16+4g+e (tile 1), e < 4
@@ -1121,8 +1120,8 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                         (__attribute__((address_space(3))) i32x2_t *)(lds_char *)(vt + voff));
                     const uint4 w = to_bf16x8<KV>(uint2{(uint32_t)t[0], (uint32_t)t[1]});
                     const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, w);
-                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, bv, o[nb], 0, 0, 0);
-                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, bv, o[nb], 0, 0, 0);
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, phi, o[nb], 0, 0, 0);
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, plo, o[nb], 0, 0, 0);
                 }
             }
         }
@@ -1153,31 +1152,34 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     // tile merge through LDS and one wave per head tile writes.
     lp = xor32_sum(xor16_sum(lp));
     __syncthreads();
-    float *s_oo = reinterpret_cast<float *>(s_a);  // [2][16][D] floats, reusing stage a
+    // [2][16] rows of kRowO floats (a head's D outputs and a 16-byte pad: the 16 heads of a
+    // row exchange fall on distinct banks), reusing stage a
+    constexpr int kRowO = D + 4;
+    float *s_oo = reinterpret_cast<float *>(s_a);
     if (lg == 0) { s_mm[wave][lr] = m; s_ll[wave][lr] = lp; }
+    // O^T layout: lane l holds d = nb*16 + 4*(l/16) + i of head l%16
     auto put_o = [&](int slot_) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s_oo[(slot_ * 16 + 4 * lg + i) * D + nb * 16 + lr] = o[nb][i];
+            *reinterpret_cast<f32x4_t *>(&s_oo[(slot_ * 16 + lr) * kRowO + nb * 16 + 4 * lg]) = o[nb];
     };
-    // the merged (max, sum) of this lane's heads also stay in registers (no lane reads back
+    // the merged (max, sum) of this lane's head also stay in registers (no lane reads back
     // what another lane of its own wave stored without a barrier in between)
-    float mres[4], lres[4];
+    float mres = 0.f, lres = 0.f;
     auto merge_o = [&](int slot_, int other) {
+        const float ms = s_mm[wave][lr], mo = s_mm[other][lr];
+        const float M = fmaxf(ms, mo);
+        const float fs = __builtin_amdgcn_exp2f(ms - M), fo = __builtin_amdgcn_exp2f(mo - M);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hd = 4 * lg + i;
-            const float ms = s_mm[wave][hd], mo = s_mm[other][hd];
-            const float M = fmaxf(ms, mo);
-            const float fs = __builtin_amdgcn_exp2f(ms - M), fo = __builtin_amdgcn_exp2f(mo - M);
+        for (int nb = 0; nb < NB; ++nb) {
+            const f32x4_t x = *reinterpret_cast<const f32x4_t *>(&s_oo[(slot_ * 16 + lr) * kRowO + nb * 16 + 4 * lg]);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) o[nb][i] = fmaf(o[nb][i], fs, s_oo[(slot_ * 16 + hd) * D + nb * 16 + lr] * fo);
-            const float Ls = fmaf(s_ll[wave][hd], fs, s_ll[other][hd] * fo);
-            mres[i] = M;
-            lres[i] = Ls;
-            if (lr == 0) { s_mm[wave][hd] = M; s_ll[wave][hd] = Ls; }
+            for (int i = 0; i < 4; ++i) o[nb][i] = fmaf(o[nb][i], fs, x[i] * fo);
         }
+        const float Ls = fmaf(s_ll[wave][lr], fs, s_ll[other][lr] * fo);
+        mres = M;
+        lres = Ls;
+        if (lg == 0) { s_mm[wave][lr] = M; s_ll[wave][lr] = Ls; }
     };
     __syncthreads();
     if (wave >= 2) put_o(wave - 2);
@@ -1189,25 +1191,20 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
         __syncthreads();
         if (wave == 0) merge_o(0, 1);
     }
-    if (wave < HT) {  // wave ht now holds head tile ht
+    const int hd = ht * 16 + lr;
+    if (wave < HT && hd < GT) {  // wave ht now holds head tile ht
+        const size_t row = query_row(a, b, kvh, h0, hd, slen).row;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hd = ht * 16 + 4 * lg + i;
-            if (hd >= GT) continue;
-            const float M = mres[i], Ls = lres[i];
-            const size_t row = query_row(a, b, kvh, h0, hd, slen).row;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const float v = o[nb][i] * vscale;
-                if (direct)
-                    a.out[row * D + nb * 16 + lr] = v / Ls;
-                else
-                    a.part_o[(k * GT + hd) * D + nb * 16 + lr] = v;
-            }
-            if (!direct && lr == 0) {
-                a.part_ml[(k * GT + hd) * 2 + 0] = M;
-                a.part_ml[(k * GT + hd) * 2 + 1] = Ls;
-            }
+        for (int nb = 0; nb < NB; ++nb) {
+            const f32x4_t v = o[nb] * vscale;
+            if (direct)
+                *reinterpret_cast<f32x4_t *>(&a.out[row * D + nb * 16 + 4 * lg]) = v / lres;
+            else
+                *reinterpret_cast<f32x4_t *>(&a.part_o[(k * GT + hd) * D + nb * 16 + 4 * lg]) = v;
+        }
+        if (!direct && lg == 0) {
+            a.part_ml[(k * GT + hd) * 2 + 0] = mres;
+            a.part_ml[(k * GT + hd) * 2 + 1] = lres;
         }
     }
     __syncthreads();  // the LDS arrays are reused by the next segment
