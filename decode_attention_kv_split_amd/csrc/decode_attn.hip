@@ -46,6 +46,9 @@ constexpr int kUnroll = 4;  // row loads per lane per tile
 constexpr int kCombineBlock = 256;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kNegBig = -3.0e38f;  // finite "minus infinity" for running maxima
+// Matrix-core segments rescale their running sums only when a tile's max exceeds the
+// exponent reference by this much (base 2), so the exponentials stay below 2^8 = 256.
+constexpr float kLazyRescale = 8.f;
 constexpr size_t kHeaderBytes = 256;  // error word + padding at the workspace start
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -676,42 +679,47 @@ struct MfmaAttn {
     template <class VAddr>
     __device__ __forceinline__ void tile(const bf16x8_t (&ka)[KB], VAddr &&vaddr, int tb, int r1) {
         bool grew = false;
-        float corr[HT];
+        float x[HT][4], tmax[HT];
         bf16x4_t phi[HT], plo[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qb[ht][kb], sacc, 0, 0, 0);
-            float x[4];
             const int rend = min(r1, lim[ht]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * lg + i < rend) ? sacc[i] * sc : -INFINITY;
-            float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-            tmax = xor32_max(xor16_max(tmax));
-            const float mn = fmaxf(m[ht], tmax);
-            corr[ht] = __builtin_amdgcn_exp2f(m[ht] - mn);
-            grew |= mn > m[ht];
-            m[ht] = mn;
+            for (int i = 0; i < 4; ++i) x[ht][i] = (tb + 4 * lg + i < rend) ? sacc[i] * sc : -INFINITY;
+            tmax[ht] = xor32_max(xor16_max(fmaxf(fmaxf(x[ht][0], x[ht][1]), fmaxf(x[ht][2], x[ht][3]))));
+            grew |= tmax[ht] > m[ht] + kLazyRescale;
+        }
+        // Lazy rescaling: m is the reference the exponentials are taken against, not the exact
+        // running max; it moves (and O and the sums are rescaled) only when some head's tile
+        // max passes it by kLazyRescale, so p = 2^(s - m) stays below 2^kLazyRescale.
+        const bool rescale = __builtin_amdgcn_ballot_w64(grew);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            float corr = 1.f;
+            if (rescale) {
+                const float mn = fmaxf(m[ht], tmax[ht]);
+                corr = __builtin_amdgcn_exp2f(m[ht] - mn);
+                m[ht] = mn;
+            }
             float p[4], ps = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - mn); ps += p[i]; }
-            lp[ht] = fmaf(lp[ht], corr[ht], ps);
+            for (int i = 0; i < 4; ++i) { p[i] = __builtin_amdgcn_exp2f(x[ht][i] - m[ht]); ps += p[i]; }
+            lp[ht] = fmaf(lp[ht], corr, ps);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 phi[ht][i] = (__bf16)p[i];
                 plo[ht][i] = (__bf16)(p[i] - (float)phi[ht][i]);
             }
-        }
-        if (__builtin_amdgcn_ballot_w64(grew)) {
-            // O is held transposed (d rows 4*(l/16)+i of head l%16), so the head's factor is
-            // this lane's own
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
+            if (rescale) {
+                // O is held transposed (d rows 4*(l/16)+i of head l%16): the factor is in-lane
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    o[ht][nb][0] *= corr[ht]; o[ht][nb][1] *= corr[ht]; o[ht][nb][2] *= corr[ht]; o[ht][nb][3] *= corr[ht];
+                    o[ht][nb][0] *= corr; o[ht][nb][1] *= corr; o[ht][nb][2] *= corr; o[ht][nb][3] *= corr;
                 }
+            }
         }
         // O^T += V_tile^T . P^T: the transposed V read (lane l: column l%16 of d block nb, rows
         // 4*(l/16) ..) is the A operand of V^T, the score layout the B operand of P^T
@@ -1023,23 +1031,28 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
 
     // Online softmax over NR rows held 4 per 16-row score tile: x[] are the scaled, masked
     // scores; returns P split into bf16 hi / lo in the lane's row order and rescales O.
+    // (lazy rescaling as in MfmaAttn::tile: m moves only when a tile max passes it by
+    // kLazyRescale)
     auto softmax = [&](float *x, auto &phi, auto &plo, int nr) {
         float tmax = x[0];
         for (int i = 1; i < nr; ++i) tmax = fmaxf(tmax, x[i]);
         tmax = xor32_max(xor16_max(tmax));
-        const float mn = fmaxf(m, tmax);
-        const float corr = __builtin_amdgcn_exp2f(m - mn);
-        const bool grew = mn > m;
-        m = mn;
+        float corr = 1.f;
+        const bool rescale = __builtin_amdgcn_ballot_w64(tmax > m + kLazyRescale);
+        if (rescale) {
+            const float mn = fmaxf(m, tmax);
+            corr = __builtin_amdgcn_exp2f(m - mn);
+            m = mn;
+        }
         float ps = 0.f;
         for (int i = 0; i < nr; ++i) {
-            const float p = __builtin_amdgcn_exp2f(x[i] - mn);
+            const float p = __builtin_amdgcn_exp2f(x[i] - m);
             ps += p;
             phi[i] = (__bf16)p;
             plo[i] = (__bf16)(p - (float)phi[i]);
         }
         lp = fmaf(lp, corr, ps);
-        if (__builtin_amdgcn_ballot_w64(grew)) {
+        if (rescale) {
             // O is held transposed (d rows 4*(l/16)+i of head l%16): the factor is in-lane
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
