@@ -723,16 +723,22 @@ struct MfmaAttn {
         }
         // O^T += V_tile^T . P^T: the transposed V read (lane l: column l%16 of d block nb, rows
         // 4*(l/16) ..) is the A operand of V^T, the score layout the B operand of P^T
+        // all hi products first, then all lo ones: the two MFMAs into one accumulator are NB
+        // (or NB * HT) instructions apart instead of back to back
+        bf16x4_t bvs[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const i16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)vaddr(nb));
-            const bf16x4_t bv = __builtin_bit_cast(bf16x4_t, t);
+        for (int nb = 0; nb < NB; ++nb)
+            bvs[nb] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)vaddr(nb)));
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                o[ht][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bv, phi[ht], o[ht][nb], 0, 0, 0);
-                o[ht][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bv, plo[ht], o[ht][nb], 0, 0, 0);
-            }
-        }
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                o[ht][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bvs[nb], phi[ht], o[ht][nb], 0, 0, 0);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                o[ht][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bvs[nb], plo[ht], o[ht][nb], 0, 0, 0);
     }
 
     // Merge the four waves pairwise through LDS ((0,2), (1,3), then (0,1)) and write the
