@@ -1132,16 +1132,19 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                 const int vkey = piece_key(rr / 8);
                 const char *vt = kLines ? st + HALF + (4 * blk + rr / 8) * 1024 + (rr % 8) * 16 + 8 * (lr % 2)
                                         : st + HALF + (2 * blk + rr / 16) * TILE + (rr % 16) * 16 + 8 * (lr % 2);
+                // all hi products, then all lo ones (dependent MFMAs NB instructions apart)
+                bf16x8_t bvs[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     const int voff = kLines ? (nb ^ vkey) << 7 : nb * 256;
                     const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                         (__attribute__((address_space(3))) i32x2_t *)(lds_char *)(vt + voff));
-                    const uint4 w = to_bf16x8<KV>(uint2{(uint32_t)t[0], (uint32_t)t[1]});
-                    const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, w);
-                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, phi, o[nb], 0, 0, 0);
-                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, plo, o[nb], 0, 0, 0);
+                    bvs[nb] = __builtin_bit_cast(bf16x8_t, to_bf16x8<KV>(uint2{(uint32_t)t[0], (uint32_t)t[1]}));
                 }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bvs[nb], phi, o[nb], 0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bvs[nb], plo, o[nb], 0, 0, 0);
             }
         }
     };
