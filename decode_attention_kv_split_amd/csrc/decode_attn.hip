@@ -603,12 +603,11 @@ __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w) {
     return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
-// Eight elements (one lane's load) as bf16x8.
+// Eight 8-bit codes (fp8 or int8) as bf16x8, exactly.
 template <int KV>
-__device__ __forceinline__ uint4 to_bf16x8(const typename std::conditional<KV == DA_BF16, uint4, uint2>::type &v) {
-    if constexpr (KV == DA_BF16) {
-        return v;
-    } else if constexpr (KV == DA_INT8) {
+__device__ __forceinline__ uint4 to_bf16x8(const uint2 &v) {
+    static_assert(Kv<KV>::kEsz == 1, "8-bit codes");
+    if constexpr (KV == DA_INT8) {
         return uint4{i8x2_to_bf16x2<false>(v.x), i8x2_to_bf16x2<true>(v.x), i8x2_to_bf16x2<false>(v.y),
                      i8x2_to_bf16x2<true>(v.y)};
     } else {
@@ -822,14 +821,14 @@ struct MfmaAttn {
     }
 };
 
-// Matrix-core segment with the tiles staged through registers (bf16 or fp8 caches): K rows
-// are loaded straight into A-operand order and V rows are widened to bf16 and stored
-// row-major in the wave's LDS tile for the transpose read.
+// Matrix-core segment with the tiles staged through registers (bf16 caches): K rows are loaded
+// straight into A-operand order and V rows are stored row-major in the wave's LDS tile for the
+// transpose read.
 template <int KV, int D, int GT, int NBUF>
 __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
                                                     size_t k, bool direct, int slen) {
-    static_assert(KV == DA_BF16 || KV == DA_FP8_E4M3FN, "MFMA flavour takes bf16 or fp8 caches");
-    using LVec = typename std::conditional<KV == DA_BF16, uint4, uint2>::type;  // 8 elements
+    static_assert(KV == DA_BF16, "the register-ring segment takes bf16 caches");
+    using LVec = uint4;  // 8 elements
     using A = MfmaAttn<D, GT>;
     constexpr int KB = A::KB, HP = A::HT * 16;
     constexpr int ESZ = Kv<KV>::kEsz;
@@ -863,11 +862,7 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
     const int ntiles = nfull + (te > ts ? 1 : 0);
     auto tile_row = [&](int t) { return t < nfull ? r0 + t * STEP + wq * TR : t < ntiles ? ts : r1; };
     auto tile_end = [&](int t) { return t < nfull ? r1 : te; };
-    float vscale = 1.f, sc = a.qk_scale;
-    if constexpr (kv_scaled(KV)) {
-        sc *= a.kv_scales[slot * 2 + 0];
-        vscale = a.kv_scales[slot * 2 + 1];
-    }
+    const float vscale = 1.f, sc = a.qk_scale;
     A at;
     at.init(a, b, kvh, h0, slen, sc);
     const int lane = at.lane, wave = at.wave, lr = at.lr, lg = at.lg;
@@ -880,10 +875,10 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
     auto process = [&](const LVec (&kt)[KB], const LVec (&vt)[VLD], int t) {
 #pragma unroll
         for (int u = 0; u < VLD; ++u)
-            *reinterpret_cast<uint4 *>(&s_v[wave][(vrow + u * VRPI) * VROW + vcol]) = to_bf16x8<KV>(vt[u]);
+            *reinterpret_cast<uint4 *>(&s_v[wave][(vrow + u * VRPI) * VROW + vcol]) = vt[u];
         bf16x8_t ka[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) ka[kb] = __builtin_bit_cast(bf16x8_t, to_bf16x8<KV>(kt[kb]));
+        for (int kb = 0; kb < KB; ++kb) ka[kb] = __builtin_bit_cast(bf16x8_t, kt[kb]);
         at.tile(ka, [&](int nb) {
             return (__attribute__((address_space(3))) uint16_t *)&s_v[wave][0] +
                    (4 * lg + lr / 4) * VROW + nb * 16 + 4 * (lane % 4);
@@ -920,9 +915,10 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
     at.finish(a, b, kvh, h0, slen, k, direct, vscale, s_oo, s_mm, s_ll);
 }
 
-// Matrix-core segment with workgroup-wide LDS stages filled by DMA (buffer_load ... lds), so
-// that no registers hold K or V in flight and 64 KiB per CU are outstanding.
-//   * A stage holds RS rows of K and V (16 KiB each: 64 bf16 or 128 8-bit rows of d = 128).
+// Matrix-core segment for 8-bit codes (fp8, int8) with workgroup-wide LDS stages filled by DMA
+// (buffer_load ... lds), so that no registers hold K or V in flight and 64 KiB per CU are
+// outstanding.
+//   * A stage holds RS rows of K and V (16 KiB each: 128 rows of d = 128).
 //     One DMA instruction fills 1 KiB in lane order. Two layouts:
 //       - 128-byte rows (8-bit codes, d = 128): "pieces" of 8 whole rows, so that every DMA
 //         instruction reads 8 whole 128-byte lines (half-line reads spread over 16 rows
@@ -937,12 +933,10 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
 //     Two stages alternate (separate arrays); all 256 threads fill each; explicit vmcnt waits
 //     and barriers mark a stage filled / consumed.
 //   * Each wave owns one 16-head tile (its own q operand, running max, sums and O) and a
-//     share of the stage's P.V blocks: 16-row blocks for bf16 (Step III by
-//     v_mfma_f32_16x16x16_bf16, V read by ds_read_b64_tr_b16), 32-row blocks for 8-bit codes
-//     (fp8 or int8; Step III by v_mfma_f32_16x16x32_bf16 with P's 8 rows per lane taken from
-//     the block's two score tiles, V read as codes by ds_read_b64_tr_b8 and widened to bf16 in
-//     registers, exactly). Step I always uses v_mfma_f32_16x16x32_bf16 (8-bit K widened to bf16
-//     after its LDS read). Step III is computed transposed, O^T += V^T . P^T (the V read is the
+//     share of the stage's 32-row P.V blocks (Step III by v_mfma_f32_16x16x32_bf16 with P's 8
+//     rows per lane taken from the block's two score tiles, V read as codes by
+//     ds_read_b64_tr_b8 and widened to bf16 in registers, exactly). Step I uses
+//     v_mfma_f32_16x16x32_bf16 (K widened to bf16 after its LDS read). Step III is computed transposed, O^T += V^T . P^T (the V read is the
 //     A operand, the score layout the B operand), so that each lane holds d rows of its own
 //     head and rescales them by that head's factor with no exchange.
 //   * At the end the waves holding the same head tile merge through LDS.
@@ -954,7 +948,7 @@ __device__ __forceinline__ int piece_key(int m) { return (m ^ (m >> 1)) & 1; }
 template <int KV, int D, int GT>
 __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
                                                       size_t k, bool direct, int slen) {
-    static_assert(KV == DA_BF16 || Kv<KV>::kEsz == 1, "matrix-core flavour takes bf16 or 8-bit caches");
+    static_assert(Kv<KV>::kEsz == 1, "the LDS-staged segment takes 8-bit codes");
     constexpr int HT = (GT + 15) / 16;
     constexpr int KB = D / 32, NB = D / 16;
     constexpr int ESZ = Kv<KV>::kEsz;
@@ -962,7 +956,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     constexpr int TILE = 16 * ROWB;            // K (or V) bytes of a 16-row tile
     constexpr int HALF = 16384;                // K (or V) bytes per stage
     constexpr int RS = HALF / ROWB;            // rows per stage
-    constexpr int PVR = KV == DA_BF16 ? 16 : 32;  // rows per P.V block
+    constexpr int PVR = 32;                    // rows per P.V block
     constexpr int NBLK = RS / PVR;             // P.V blocks per stage
     constexpr int WPH = kWaves / HT;           // waves per head tile
     constexpr int IPW = NBLK / WPH;            // blocks per wave per stage
@@ -1078,9 +1072,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             uint4 raw;
-            if constexpr (KV == DA_BF16) {
-                raw = *reinterpret_cast<const uint4 *>(kt + kb * 1024 + lane * 16);
-            } else if constexpr (kLines) {
+            if constexpr (kLines) {
                 raw = to_bf16x8<KV>(*reinterpret_cast<const uint2 *>(kl + kb * 256));
             } else {
                 const uint2 v = *reinterpret_cast<const uint2 *>(kt + ((kb * 2 + lg / 2) * 16 + lr) * 16 + 8 * (lg % 2));
@@ -1096,24 +1088,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
         for (int j = 0; j < IPW; ++j) {
             const int blk = wb + j * WPH;  // P.V block of the stage
             const int rb = sb + blk * PVR; // its first cache row
-            if constexpr (KV == DA_BF16) {
-                const f32x4_t sacc = scores(st + blk * TILE, 0);
-                float x[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = (rb + 4 * lg + i < rend) ? sacc[i] * sc : -INFINITY;
-                bf16x4_t phi, plo;
-                softmax(x, phi, plo, 4);
-                const char *vt = st + HALF + blk * TILE;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const int r = 4 * lg + lr / 4, d0 = nb * 16 + 4 * (lane % 4);
-                    const i16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4_t *)(lds_char *)(vt + ((d0 / 8) * 16 + r) * 16 + (d0 % 8) * 2));
-                    const bf16x4_t bv = __builtin_bit_cast(bf16x4_t, t);
-                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bv, phi, o[nb], 0, 0, 0);
-                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bv, plo, o[nb], 0, 0, 0);
-                }
-            } else {
+            {
                 // rows of lane group g: 4g+e (tile 0) and 16+4g+e (tile 1), e < 4
                 const f32x4_t s0 = scores(st + (2 * blk) * TILE, 0);
                 const f32x4_t s1 = scores(st + (2 * blk + 1) * TILE, 1);
