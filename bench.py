@@ -32,7 +32,6 @@ Prints ONE JSON line:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -45,7 +44,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "achieved HBM GB/s (KV bytes/step ÷ time, % of peak) + µs/decode step"
-KERNEL_SRC = os.path.join(ROOT, "decode_attention_kv_split_amd", "csrc", "decode_attn.hip")
 
 
 def parse_args():
@@ -70,13 +68,14 @@ def parse_args():
 
 
 def source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 of the kernel source and its compiler flags (the device code measured)."""
+    from decode_attention_kv_split_amd.build import code_digest
+    return code_digest()
 
 
 def profiled_traffic(workload: str):
     """HBM bytes per split-kernel launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    was taken on the current kernel source and compiler flags; else None."""
     path = os.path.join(ROOT, "profiles", f"split_kv_attn__{workload}__pmc.txt")
     if not os.path.exists(path):
         return None

@@ -30,6 +30,15 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
          "-I", os.path.join(ROOT, "include")]
 
 
+def code_digest() -> str:
+    """sha256 of the kernel source and the compiler flags: it names the device code that a
+    measurement was taken on."""
+    import hashlib
+    with open(SRC, "rb") as f:
+        src = f.read()
+    return hashlib.sha256(src + b"\0" + " ".join(FLAGS).encode()).hexdigest()
+
+
 def build_library(verbose: bool = False) -> str:
     """Compile the HIP library (always recompiles) and return its path."""
     tmp = LIB + ".tmp%d" % os.getpid()
