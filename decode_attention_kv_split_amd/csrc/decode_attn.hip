@@ -49,7 +49,8 @@ constexpr float kNegBig = -3.0e38f;  // finite "minus infinity" for running maxi
 // Matrix-core segments rescale their running sums only when a tile's max exceeds the
 // exponent reference by this much (base 2), so the exponentials stay below 2^8 = 256.
 constexpr float kLazyRescale = 8.f;
-constexpr size_t kHeaderBytes = 256;  // error word + padding at the workspace start
+constexpr size_t kHeaderBytes = 256;  // error word, total rows (int64 at byte 8), padding
+constexpr size_t kTotalOff = 8;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -297,7 +298,6 @@ __device__ __forceinline__ int64_t unit_rows(int L, int max_len, int nq) {
     return (L >= 1 && L >= nq && L <= max_len) ? L : 0;
 }
 __device__ __forceinline__ int64_t wg_start(int64_t w, int64_t T, int64_t N) { return w * T / N; }
-__device__ __forceinline__ int64_t wg_owner(int64_t x, int64_t T, int64_t N) { return ((x + 1) * N - 1) / T; }
 
 // Exclusive prefix over sequences of their rows in all units, s_pre[0..batch]; s_pre[batch] = T.
 // Needs batch <= kMaxBatch and blockDim.x == kBlock.
@@ -350,6 +350,10 @@ struct SplitArgs {
     const void *k_new, *v_new;
     int32_t *lens_copy, *err;
     int row_bytes;
+    // for the combine: per unit, the workgroups holding its first and its last row, and the
+    // rows of all units (the partition's total)
+    int2 *unit_wg;
+    int64_t *rows_total;
 };
 
 // The query rows of a (sequence b, KV head kvh) are its g heads at each of the nq query
@@ -1299,13 +1303,16 @@ __device__ __forceinline__ SegWalk first_segment(const SplitArgs &a, int gt) {
         }
     }
     sequence_prefix(a.lens, a.pt, s_pre, s_wave);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.rows_total = s_pre[a.pt.batch];
     SegWalk wk;
     wk.start(a, gt, s_pre);
     return wk;
 }
 
 // Workgroup w walks its share of the rows and calls seg(b, kvh, h0, r0, r1, k, whole) once per
-// unit it crosses.
+// unit it crosses. The workgroup holding a unit's first row, and the one holding its last,
+// record themselves in the unit's entry of unit_wg, so that the combine finds the unit's
+// segments without redoing the partition.
 // With a fused append, a segment that ends at a unit's new last row first stores that row of
 // K and V into the cache itself; the barrier (a workgroup-scope release and acquire) makes the
 // stores visible to the loads of every wave of the workgroup. Only workgroups holding that
@@ -1329,6 +1336,11 @@ __device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn 
             // a row shorter than a cache line shares its line with the previous row, which
             // another workgroup on this CU may hold, stale, in the vector L1: drop it
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        if (threadIdx.x == 0) {
+            int32_t *uw = reinterpret_cast<int32_t *>(a.unit_wg + (wk.k - wk.w));
+            if (wk.r0 == 0) uw[0] = (int32_t)wk.w;
+            if (wk.r1 == wk.slen) uw[1] = (int32_t)wk.w;
         }
         seg(wk.sb, wk.kvh, wk.h0, wk.r0, wk.r1, wk.k, wk.whole, wk.slen);
     }
@@ -1369,116 +1381,107 @@ void split_kv_attn_mfma_kernel(const SplitArgs a) {
     }
 }
 
-// One workgroup per (sequence, query head): merge the segments of the head's unit by their
-// log-sum-exp weights. skip_single: a unit covered by one workgroup was already written.
+// Merges the segments of every query row by their log-sum-exp weights. Workgroup x takes rows
+// rw * (x % (gt / rw)) .. + rw - 1 of unit u = x / (gt / rw) (a unit's rows share its
+// segments), each row with kCombineBlock / rw threads: segment groups of D / 4 threads, one
+// float4 column each. skip_single: a unit covered by one workgroup was already written.
 // With a fused append (pt.append_cap > 0) the stored lengths come from the split kernel's
 // workspace copy, and the workgroup of head 0 writes each sequence's new length to lens_upd.
+// The unit's segments are those of workgroups unit_wg[u].x .. unit_wg[u].y (slot w + u), which
+// the split kernel recorded; only when the partition has fewer rows than workgroups can a
+// workgroup in between hold no rows (and no segment), which the share bounds then tell.
+// The length, that entry and the total are read together, then every segment once: each
+// segment group keeps a running maximum, and the groups merge at the end.
 template <int D>
 __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
-    const int32_t *__restrict__ lens, int32_t *__restrict__ lens_upd, const float *__restrict__ part_ml,
-    const float *__restrict__ part_o, float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt,
-    Partition pt, int skip_single) {
-    constexpr int SG = kCombineBlock / (D / 4);  // segment groups working side by side
-    const int bh = blockIdx.x;  // output row ((b * nq) + query position tq) * h_q + head h
-    const int b = bh / (h_q * pt.nq), tq = bh / h_q % pt.nq, h = bh % h_q;
+    const int32_t *__restrict__ lens, int32_t *__restrict__ lens_upd, const int2 *__restrict__ unit_wg,
+    const int64_t *__restrict__ rows_total, const float *__restrict__ part_ml, const float *__restrict__ part_o,
+    float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt, int rw, Partition pt, int skip_single) {
+    constexpr int C4 = D / 4;  // float4 columns of a row
+    constexpr int UN = 8;      // segments a group loads before using them
+    const int tpr = kCombineBlock / rw, sgr = tpr / C4;  // threads and segment groups per row
+    const int per_unit = gt / rw;
+    const int64_t u = blockIdx.x / per_unit;
+    const int hh = (blockIdx.x % per_unit) * rw + threadIdx.x / tpr;  // the thread's row in the unit
+    const int sg = threadIdx.x % tpr / C4, c4 = threadIdx.x % C4;
+    const int upb = pt.h_kv * pt.tiles, g = h_q / pt.h_kv;
+    const int b = (int)(u / upb), ul = (int)(u % upb), kvh = ul / pt.tiles;
+    // the row's query position and head: row hh of the tile is row fr of the group's g * nq
+    const int fr = (ul % pt.tiles) * gt + hh, tq = fr / g, h = kvh * g + fr % g;
+    float *dst = out + ((size_t)(b * pt.nq + tq) * h_q + h) * D;
     const int L = attended_len(lens[b], pt.append_cap);
-    if (lens_upd && h == 0 && threadIdx.x == 0) lens_upd[b] = L;
-    float *dst = out + (size_t)bh * D;
+    const int2 ww = unit_wg[u];
+    const int64_t total = *rows_total, N = pt.nwg;
+    if (lens_upd && ul == 0 && threadIdx.x == 0 && blockIdx.x % per_unit == 0) lens_upd[b] = L;
     if (unit_rows(L, pt.max_len, pt.nq) == 0) {
-        for (int d = threadIdx.x; d < D; d += kCombineBlock) dst[d] = 0.f;
+        if (sg == 0) reinterpret_cast<float4 *>(dst)[c4] = float4{0.f, 0.f, 0.f, 0.f};
         if (threadIdx.x == 0) atomicOr(err, DA_DEV_ERR_LEN_RANGE);
         return;
     }
-    // rows before this sequence, and in total
-    __shared__ int64_t s_red[2][kCombineBlock / kWave];
-    const int64_t upb = (int64_t)pt.h_kv * pt.tiles;
-    int64_t before = 0, total = 0;
-    for (int bb = threadIdx.x; bb < pt.batch; bb += kCombineBlock) {
-        const int64_t r = unit_rows(attended_len(lens[bb], pt.append_cap), pt.max_len, pt.nq) * upb;
-        total += r;
-        if (bb < b) before += r;
-    }
-#pragma unroll
-    for (int off = 1; off < kWave; off *= 2) {
-        before += __shfl_xor(before, off);
-        total += __shfl_xor(total, off);
-    }
-    if (threadIdx.x % kWave == 0) {
-        s_red[0][threadIdx.x / kWave] = before;
-        s_red[1][threadIdx.x / kWave] = total;
-    }
-    __syncthreads();
-    before = total = 0;
-#pragma unroll
-    for (int w = 0; w < kCombineBlock / kWave; ++w) { before += s_red[0][w]; total += s_red[1][w]; }
-
-    // the query's row among its group's g * nq rows, its head tile and slot
-    const int g = h_q / pt.h_kv, kvh = h / g, fr = tq * g + h % g, t = fr / gt, hh = fr % gt;
-    const int64_t ul = (int64_t)kvh * pt.tiles + t;
-    const int64_t u = b * upb + ul;
-    const int64_t P = before + ul * L, N = pt.nwg;
-    const int64_t wa = wg_owner(P, total, N), wb = wg_owner(P + L - 1, total, N);
+    const int wa = ww.x, wb = ww.y;
     if (skip_single && wa == wb) return;
+    const bool every_share_has_rows = total >= N;
 
-    __shared__ float red[kCombineBlock / kWave];
-    __shared__ float4 s_acc[SG][D / 4];
-    __shared__ float s_l[SG];
-    float M = kNegBig;
-    for (int64_t w = wa + threadIdx.x; w <= wb; w += kCombineBlock)
-        if (wg_start(w, total, N) < wg_start(w + 1, total, N)) M = fmaxf(M, part_ml[((w + u) * gt + hh) * 2]);
-#pragma unroll
-    for (int off = 1; off < kWave; off *= 2) M = fmaxf(M, __shfl_xor(M, off));
-    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = M;
-    __syncthreads();
-    M = red[0];
-#pragma unroll
-    for (int w = 1; w < kCombineBlock / kWave; ++w) M = fmaxf(M, red[w]);
-
-    // SG segment groups side by side, D/4 threads each holding 4 output columns; every
-    // iteration issues the loads of UN segments before using any of them.
-    constexpr int UN = 4;
-    const int c4 = threadIdx.x % (D / 4), sg = threadIdx.x / (D / 4);
+    __shared__ float4 s_acc[kCombineBlock / C4][C4];  // per (row, group)
+    __shared__ float s_m[kCombineBlock / C4], s_l[kCombineBlock / C4];
     float4 acc = {0.f, 0.f, 0.f, 0.f};
-    float ls = 0.f;
-    for (int64_t w0 = wa + sg; w0 <= wb; w0 += SG * UN) {
+    float mrun = kNegBig, ls = 0.f;  // an absent segment is (kNegBig, 0, 0): weight 0 or no effect
+    for (int w0 = wa + sg; w0 <= wb; w0 += sgr * UN) {
         float mj[UN], lj[UN];
         float4 oj[UN];
 #pragma unroll
         for (int j = 0; j < UN; ++j) {
-            const int64_t w = w0 + j * SG;
-            mj[j] = -INFINITY;  // an empty or absent segment weighs 0
+            const int w = w0 + j * sgr;
+            mj[j] = kNegBig;
             lj[j] = 0.f;
             oj[j] = float4{0.f, 0.f, 0.f, 0.f};
-            if (w <= wb && wg_start(w, total, N) < wg_start(w + 1, total, N)) {
+            if (w <= wb && (every_share_has_rows || wg_start(w, total, N) < wg_start(w + 1, total, N))) {
                 const size_t kk = (size_t)(w + u) * gt + hh;
                 mj[j] = part_ml[kk * 2];
                 lj[j] = part_ml[kk * 2 + 1];
                 oj[j] = reinterpret_cast<const float4 *>(part_o + kk * D)[c4];
             }
         }
+        float mx = mrun;
+#pragma unroll
+        for (int j = 0; j < UN; ++j) mx = fmaxf(mx, mj[j]);
+        const float r = __builtin_amdgcn_exp2f(mrun - mx);
+        ls *= r;
+        acc.x *= r;
+        acc.y *= r;
+        acc.z *= r;
+        acc.w *= r;
 #pragma unroll
         for (int j = 0; j < UN; ++j) {
-            const float f = __builtin_amdgcn_exp2f(mj[j] - M);
+            const float f = __builtin_amdgcn_exp2f(mj[j] - mx);
             ls = fmaf(lj[j], f, ls);
             acc.x = fmaf(oj[j].x, f, acc.x);
             acc.y = fmaf(oj[j].y, f, acc.y);
             acc.z = fmaf(oj[j].z, f, acc.z);
             acc.w = fmaf(oj[j].w, f, acc.w);
         }
+        mrun = mx;
     }
-    s_acc[sg][c4] = acc;
-    if (c4 == 0) s_l[sg] = ls;
+    const int grp = threadIdx.x / C4;  // (row, group) slot
+    s_acc[grp][c4] = acc;
+    if (c4 == 0) {
+        s_m[grp] = mrun;
+        s_l[grp] = ls;
+    }
     __syncthreads();
     if (sg == 0) {
-        float4 x = s_acc[0][c4];
-        float z = s_l[0];
-#pragma unroll
-        for (int i = 1; i < SG; ++i) {
-            x.x += s_acc[i][c4].x;
-            x.y += s_acc[i][c4].y;
-            x.z += s_acc[i][c4].z;
-            x.w += s_acc[i][c4].w;
-            z += s_l[i];
+        float M = s_m[grp];
+        for (int i = 1; i < sgr; ++i) M = fmaxf(M, s_m[grp + i]);
+        float4 x = {0.f, 0.f, 0.f, 0.f};
+        float z = 0.f;
+        for (int i = 0; i < sgr; ++i) {
+            const float f = __builtin_amdgcn_exp2f(s_m[grp + i] - M);
+            const float4 y = s_acc[grp + i][c4];
+            x.x = fmaf(y.x, f, x.x);
+            x.y = fmaf(y.y, f, x.y);
+            x.z = fmaf(y.z, f, x.z);
+            x.w = fmaf(y.w, f, x.w);
+            z = fmaf(s_l[grp + i], f, z);
         }
         reinterpret_cast<float4 *>(dst)[c4] = float4{x.x / z, x.y / z, x.z / z, x.w / z};
     }
@@ -1537,7 +1540,8 @@ int group_rows(const da_desc *d) { return d->h_q / d->h_kv * n_queries(d); }
 struct Plan {
     int gt, tiles, nwg;
     bool mfma;  // matrix-core flavour
-    size_t lens_off, ml_off, o_off, bytes;  // workspace: header, lengths copy, (max, sum), rows
+    // workspace: header, lengths copy, per-unit first / last workgroup, (max, sum), rows
+    size_t lens_off, unit_off, ml_off, o_off, bytes;
 };
 
 // Flavour and query heads per workgroup: groups that are a multiple of 4 query heads over a
@@ -1561,6 +1565,26 @@ constexpr int kFallbackResident = 512; // workgroups planned for when no device 
 // more shares than others and run up to 15 % slower; two 4-wave workgroups per CU stream
 // faster than three.
 constexpr int kBlocksPerCu = 2;
+// Compute units of the current device (256 when it cannot be queried).
+int cu_count() {
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    return cache[dev] = cus;
+}
+
 int resident_workgroups(const void *kernel) {
     static std::mutex mu;
     static std::map<std::pair<int, const void *>, int> cache;
@@ -1629,7 +1653,8 @@ int make_plan(const da_desc *d, int max_len, Plan *p) {
     const size_t segs = (size_t)p->nwg + units;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     p->lens_off = kHeaderBytes;
-    p->ml_off = p->lens_off + up((size_t)d->batch * sizeof(int32_t));
+    p->unit_off = p->lens_off + up((size_t)d->batch * sizeof(int32_t));
+    p->ml_off = p->unit_off + up((size_t)units * sizeof(int2));
     p->o_off = p->ml_off + up(segs * p->gt * 2 * sizeof(float));
     p->bytes = p->o_off + up(segs * p->gt * d->d_v * sizeof(float));
     return DA_OK;
@@ -1745,6 +1770,8 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     args.lens_copy = reinterpret_cast<int32_t *>(ws + p.lens_off);
     args.err = reinterpret_cast<int32_t *>(ws);
     args.row_bytes = desc->d_k * elem_size(desc->kv_dtype);
+    args.unit_wg = reinterpret_cast<int2 *>(ws + p.unit_off);
+    args.rows_total = reinterpret_cast<int64_t *>(ws + kTotalOff);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (out)
         launch_split<true>(desc->kv_dtype, desc->d_k, p.gt, p.mfma, dim3(p.nwg), st, args);
@@ -1765,23 +1792,38 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
         return fail(DA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", who, ws_bytes, p.bytes);
     char *ws = static_cast<char *>(workspace);
     const float *ml = reinterpret_cast<const float *>(ws + p.ml_off);
+    const int2 *uw = reinterpret_cast<const int2 *>(ws + p.unit_off);
+    const int64_t *tot = reinterpret_cast<const int64_t *>(ws + kTotalOff);
     const float *po = reinterpret_cast<const float *>(ws + p.o_off);
     int32_t *err = reinterpret_cast<int32_t *>(ws);
     if (append && n_queries(desc) > 1)
         return fail(DA_ERR_UNSUPPORTED, "%s: the fused append takes one query per sequence (n_queries %d)", who,
                     desc->n_queries);
-    const dim3 grid(desc->batch * n_queries(desc) * desc->h_q);
+    // rows of a unit per workgroup: more rows per workgroup spread the fixed cost (the length,
+    // the unit's entry, the merge) over more rows while at least two workgroups per CU remain
+    // and each segment group keeps at most one load batch (a unit has about nwg / units + 1
+    // segments); with 2048 rows over 256 CUs, 4 rows per workgroup took the combine from 6.5
+    // to 4.5 us, while fewer than two workgroups per CU were slower
+    const int64_t units = (int64_t)desc->batch * desc->h_kv * p.tiles;
+    const int groups = kCombineBlock / (desc->d_v / 4);  // segment groups of a workgroup
+    const int64_t segs = p.nwg / units + 1;
+    const int64_t min_wg = 2 * (int64_t)cu_count();
+    int rw = 1;
+    while (2 * rw <= groups && p.gt % (2 * rw) == 0 && 2 * rw * segs <= 8 * groups &&
+           units * (p.gt / (2 * rw)) >= min_wg)
+        rw *= 2;
+    const dim3 grid((unsigned)(units * (p.gt / rw)));
     const Partition pt = partition_of(desc, p, max_len, append);
     // appending: stored lengths from the split kernel's copy, new lengths written to lens
     const int32_t *lsrc = append ? reinterpret_cast<const int32_t *>(ws + p.lens_off) : lens;
     int32_t *lupd = append ? lens : nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (desc->d_v == 64)
-        hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, ml, po, out, err,
-                           desc->h_q, p.gt, pt, skip_single);
+        hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, tot, ml, po, out, err,
+                           desc->h_q, p.gt, rw, pt, skip_single);
     else
-        hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, ml, po, out, err,
-                           desc->h_q, p.gt, pt, skip_single);
+        hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, tot, ml, po, out, err,
+                           desc->h_q, p.gt, rw, pt, skip_single);
     return launch_status("lse_combine_kernel");
 }
 

@@ -101,7 +101,9 @@ typedef struct {
  * Bytes of device workspace decode_attn_run / kv_append need for this descriptor when no
  * sequence is longer than max_len (1 <= max_len <= cap). The workspace holds the sticky
  * error word and the per-split partial results (running max, sum of exponentials and
- * unnormalised output of each split; see decode_attn_partial). *bytes is written on the
+ * unnormalised output of each split; see decode_attn_partial), with the bookkeeping the
+ * combine needs to find them (the total row count and, per (sequence, KV head, head tile),
+ * the first and last workgroup holding its rows). *bytes is written on the
  * host. A workspace serves one call at a time: calls that overlap on the same workspace race.
  */
 int da_workspace_size(const da_desc *desc, int32_t max_len, size_t *bytes);
@@ -150,7 +152,8 @@ int decode_attn_run(const da_desc *desc, const void *q, const void *k_cache,
  * First stage of decode_attn_run: each workgroup reads its share of K and V rows once for
  * all query heads of the group and writes, per (sequence, KV head) segment of its share and
  * per query head, the running max (base-2 exponent domain), the sum of exponentials and the
- * unnormalised output row to the workspace.
+ * unnormalised output row to the workspace, and records which workgroups hold each
+ * (sequence, KV head, head tile)'s rows.
  */
 int decode_attn_partial(const da_desc *desc, const void *q, const void *k_cache,
                         const void *v_cache, const int32_t *lens, int32_t max_len,

@@ -129,6 +129,31 @@ def test_parity_uneven_workgroup_shares(block_rows):
     check_close(out, oracle_out(w, c), "bf16")
 
 
+@pytest.mark.parametrize("kv,h_q", [("bf16", 8), ("fp8", 8), ("bf16", 2), ("f32", 3)])
+def test_parity_more_workgroups_than_rows(kv, h_q):
+    """A partition with far fewer rows than workgroups (block_rows 1 at max_len 1000, a few
+    rows per sequence): most workgroups hold no rows, so a unit's segments sit on workgroups
+    hundreds apart with empty shares in between, which the combine must skip. Both the
+    one-call form and the two-stage form."""
+    w = W(B=3, h_q=h_q, h_kv=2 if h_q % 2 == 0 else 1, cap=1000, kv_dtype=kv, lens=("const", 5), seed=77)
+    c = workloads.generate(w)
+    c["lens_final"] = torch.tensor([3, 1, 5], dtype=torch.int32)
+    c["lens_init"] = c["lens_final"].clone()
+    log(f"case sparse partition {kv} h_q={h_q} h_kv={w.h_kv} lens={c['lens_final'].tolist()}")
+    out, g, lens, err = run_gpu(w, c, block_rows=1, max_len=1000)
+    assert err == 0
+    ref = oracle_out(w, c)
+    check_close(out, ref, kv, "one call")
+    desc = desc_of(w, 1)
+    assert da.da_plan(desc, 1000)["n_blocks"] > 1000
+    ws = da.Workspace(desc, 1000)
+    two = torch.empty_like(out)
+    da.decode_attn_partial(desc, g["q"], g["k_cache"], g["v_cache"], lens, 1000, g["kv_scales"], ws)
+    da.decode_attn_combine(desc, lens, 1000, two, ws)
+    assert da.da_read_device_error(ws) == 0
+    check_close(two, ref, kv, "two stages")
+
+
 def test_invalid_lengths_between_valid_ones():
     """Sequences with an out-of-range length hold no rows of the partition: their output
     is zeroed and flagged, and the sequences around them are unaffected."""
