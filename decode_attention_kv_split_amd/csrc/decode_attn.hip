@@ -49,8 +49,7 @@ constexpr float kNegBig = -3.0e38f;  // finite "minus infinity" for running maxi
 // Matrix-core segments rescale their running sums only when a tile's max exceeds the
 // exponent reference by this much (base 2), so the exponentials stay below 2^8 = 256.
 constexpr float kLazyRescale = 8.f;
-constexpr size_t kHeaderBytes = 256;  // error word, total rows (int64 at byte 8), padding
-constexpr size_t kTotalOff = 8;
+constexpr size_t kHeaderBytes = 256;  // error word + padding at the workspace start
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -350,10 +349,9 @@ struct SplitArgs {
     const void *k_new, *v_new;
     int32_t *lens_copy, *err;
     int row_bytes;
-    // for the combine: per unit, the workgroups holding its first and its last row, and the
-    // rows of all units (the partition's total)
+    // for the combine: per unit, the workgroups holding its first and its last row
     int2 *unit_wg;
-    int64_t *rows_total;
+    int dv;  // output row length (the partial rows' stride)
 };
 
 // The query rows of a (sequence b, KV head kvh) are its g heads at each of the nq query
@@ -1235,6 +1233,10 @@ struct SegWalk {
     size_t k;
     bool whole;
     bool new_row;  // this pass appended the unit's last row (row slen - 1)
+    // An empty share (only when there are fewer rows than workgroups) whose position lies
+    // strictly inside a unit: that unit's index (b * upb + ul), else -1. The combine reads
+    // every workgroup between the unit's first and last, so this one leaves an empty partial.
+    int64_t empty_unit;
 
     // Positions the walk on the workgroup's first segment; pre must hold the prefix.
     __device__ __forceinline__ void start(const SplitArgs &a, int gt_, const int64_t *s_pre) {
@@ -1252,7 +1254,8 @@ struct SegWalk {
         end = wg_start(w + 1, Tot, N);
         ord = -1;
         b = 0, L = 1, ul = 0, row = 0;
-        if (pos < end) {
+        empty_unit = -1;
+        if (pos < Tot) {
             // the sequence holding row `pos`: the last b with pre[b] <= pos (it has rows)
             int lo = 0, hi = pt.batch;  // invariant: pre[lo] <= pos < pre[hi]
             while (hi - lo > 1) {
@@ -1264,6 +1267,7 @@ struct SegWalk {
             const int64_t off = pos - uniform64(s_pre[b]);
             ul = (int)(off / L);  // unit within the sequence
             row = (int)(off % L);
+            if (pos == end && row > 0) empty_unit = (int64_t)b * upb + ul;
         }
         next();
     }
@@ -1303,7 +1307,6 @@ __device__ __forceinline__ SegWalk first_segment(const SplitArgs &a, int gt) {
         }
     }
     sequence_prefix(a.lens, a.pt, s_pre, s_wave);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *a.rows_total = s_pre[a.pt.batch];
     SegWalk wk;
     wk.start(a, gt, s_pre);
     return wk;
@@ -1319,7 +1322,13 @@ __device__ __forceinline__ SegWalk first_segment(const SplitArgs &a, int gt) {
 // row read it in this pass, and each of them writes it (the same bytes) before reading.
 template <class SegFn>
 __device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn &&seg) {
-    for (SegWalk wk = first_segment(a, gt); wk.has; wk.next()) {
+    SegWalk wk = first_segment(a, gt);
+    if (wk.empty_unit >= 0) {  // (max, sum, row) = (kNegBig, 0, 0): weighs nothing in the combine
+        const size_t kk = (size_t)wk.w + (size_t)wk.empty_unit;
+        for (int i = threadIdx.x; i < gt * 2; i += kBlock) a.part_ml[kk * gt * 2 + i] = (i % 2) ? 0.f : kNegBig;
+        for (int i = threadIdx.x; i < gt * a.dv; i += kBlock) a.part_o[kk * gt * a.dv + i] = 0.f;
+    }
+    for (; wk.has; wk.next()) {
         if (wk.new_row && wk.r1 == wk.slen) {
             const int n16 = a.row_bytes / 16;
             const size_t slot = (size_t)wk.sb * a.pt.h_kv + wk.kvh;
@@ -1388,14 +1397,13 @@ void split_kv_attn_mfma_kernel(const SplitArgs a) {
 // With a fused append (pt.append_cap > 0) the stored lengths come from the split kernel's
 // workspace copy, and the workgroup of head 0 writes each sequence's new length to lens_upd.
 // The unit's segments are those of workgroups unit_wg[u].x .. unit_wg[u].y (slot w + u), which
-// the split kernel recorded; only when the partition has fewer rows than workgroups can a
-// workgroup in between hold no rows (and no segment), which the share bounds then tell.
-// The length, that entry and the total are read together, then every segment once: each
-// segment group keeps a running maximum, and the groups merge at the end.
+// the split kernel recorded; every workgroup in between left a partial for the unit (an empty
+// one if its share holds no rows). The length and that entry are read together, then every
+// segment once: each segment group keeps a running maximum, and the groups merge at the end.
 template <int D>
 __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     const int32_t *__restrict__ lens, int32_t *__restrict__ lens_upd, const int2 *__restrict__ unit_wg,
-    const int64_t *__restrict__ rows_total, const float *__restrict__ part_ml, const float *__restrict__ part_o,
+    const float *__restrict__ part_ml, const float *__restrict__ part_o,
     float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt, int rw, Partition pt, int skip_single) {
     constexpr int C4 = D / 4;  // float4 columns of a row
     constexpr int UN = 8;      // segments a group loads before using them
@@ -1411,7 +1419,6 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     float *dst = out + ((size_t)(b * pt.nq + tq) * h_q + h) * D;
     const int L = attended_len(lens[b], pt.append_cap);
     const int2 ww = unit_wg[u];
-    const int64_t total = *rows_total, N = pt.nwg;
     if (lens_upd && ul == 0 && threadIdx.x == 0 && blockIdx.x % per_unit == 0) lens_upd[b] = L;
     if (unit_rows(L, pt.max_len, pt.nq) == 0) {
         if (sg == 0) reinterpret_cast<float4 *>(dst)[c4] = float4{0.f, 0.f, 0.f, 0.f};
@@ -1420,7 +1427,6 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     }
     const int wa = ww.x, wb = ww.y;
     if (skip_single && wa == wb) return;
-    const bool every_share_has_rows = total >= N;
 
     __shared__ float4 s_acc[kCombineBlock / C4][C4];  // per (row, group)
     __shared__ float s_m[kCombineBlock / C4], s_l[kCombineBlock / C4];
@@ -1435,7 +1441,7 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
             mj[j] = kNegBig;
             lj[j] = 0.f;
             oj[j] = float4{0.f, 0.f, 0.f, 0.f};
-            if (w <= wb && (every_share_has_rows || wg_start(w, total, N) < wg_start(w + 1, total, N))) {
+            if (w <= wb) {
                 const size_t kk = (size_t)(w + u) * gt + hh;
                 mj[j] = part_ml[kk * 2];
                 lj[j] = part_ml[kk * 2 + 1];
@@ -1771,7 +1777,7 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     args.err = reinterpret_cast<int32_t *>(ws);
     args.row_bytes = desc->d_k * elem_size(desc->kv_dtype);
     args.unit_wg = reinterpret_cast<int2 *>(ws + p.unit_off);
-    args.rows_total = reinterpret_cast<int64_t *>(ws + kTotalOff);
+    args.dv = desc->d_v;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (out)
         launch_split<true>(desc->kv_dtype, desc->d_k, p.gt, p.mfma, dim3(p.nwg), st, args);
@@ -1793,7 +1799,6 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
     char *ws = static_cast<char *>(workspace);
     const float *ml = reinterpret_cast<const float *>(ws + p.ml_off);
     const int2 *uw = reinterpret_cast<const int2 *>(ws + p.unit_off);
-    const int64_t *tot = reinterpret_cast<const int64_t *>(ws + kTotalOff);
     const float *po = reinterpret_cast<const float *>(ws + p.o_off);
     int32_t *err = reinterpret_cast<int32_t *>(ws);
     if (append && n_queries(desc) > 1)
@@ -1819,10 +1824,10 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
     int32_t *lupd = append ? lens : nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (desc->d_v == 64)
-        hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, tot, ml, po, out, err,
+        hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, ml, po, out, err,
                            desc->h_q, p.gt, rw, pt, skip_single);
     else
-        hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, tot, ml, po, out, err,
+        hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, ml, po, out, err,
                            desc->h_q, p.gt, rw, pt, skip_single);
     return launch_status("lse_combine_kernel");
 }
