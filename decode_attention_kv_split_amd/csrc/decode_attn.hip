@@ -578,6 +578,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
@@ -917,6 +919,26 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
     at.finish(a, b, kvh, h0, slen, k, direct, vscale, s_oo, s_mm, s_ll);
 }
 
+// int8 codes on the matrix cores go through fp16, whose 11-bit significand holds 1024 + u
+// exactly for any byte u: with the code's sign bit flipped (u = code + 128) and 0x64 as the
+// high byte, a half is 1024 + u = code + 1152, two halves per v_perm. That costs 0.75
+// instructions per code, against 1.5 for an exact int8 -> bf16 conversion.
+// Eight codes -> fp16 code + 1152 (as raw halves).
+__device__ __forceinline__ uint4 i8x8_to_f16x8_offset(const uint2 &v) {
+    const uint32_t x = v.x ^ 0x80808080u, y = v.y ^ 0x80808080u;
+    return uint4{__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u),
+                 __builtin_amdgcn_perm(0x64646464u, y, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, y, 0x04030402u)};
+}
+// Eight codes -> fp16, exactly (the offset taken off by a packed half subtraction).
+__device__ __forceinline__ uint4 i8x8_to_f16x8(const uint2 &v) {
+    const uint4 h = i8x8_to_f16x8_offset(v);
+    const f16x2_t off = {(_Float16)1152.f, (_Float16)1152.f};
+    return uint4{__builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, h.x) - off),
+                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, h.y) - off),
+                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, h.z) - off),
+                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, h.w) - off)};
+}
+
 // Matrix-core segment for 8-bit codes (fp8, int8) with workgroup-wide LDS stages filled by DMA
 // (buffer_load ... lds), so that no registers hold K or V in flight and 64 KiB per CU are
 // outstanding.
@@ -966,6 +988,17 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     constexpr int VM_STAGE = 2 * DPW;          // DMA ops of one stage per wave
     constexpr bool kLines = ROWB == 128;       // 8-bit codes, d = 128: whole-line DMA layout
     static_assert(NBLK % WPH == 0 && (HALF / 1024) % kWaves == 0, "stage split");
+    // int8 goes through fp16: K exactly, q scaled by a power of two per head into fp16's
+    // range (the factor moves to the score scale), P split into fp16 hi + lo, and V as
+    // code + 1152, whose excess, 1152 times the sum of the P the products used, a ones A
+    // operand accumulates beside O and the end takes off.
+    constexpr bool kF16 = KV == DA_INT8;
+    // fp16 P is taken 2^7 times larger (at most 2^15 with the lazy rescaling), which keeps
+    // small weights out of fp16's subnormals; the segment's sums and rows carry the factor,
+    // and its partial reports a maximum 7 lower, which the combine's weights undo
+    constexpr float kPShift = kF16 ? 7.f : 0.f;
+    using PV = std::conditional_t<kF16, f16x8_t, bf16x8_t>;
+    using PE = std::conditional_t<kF16, _Float16, __bf16>;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int lr = lane % 16, lg = lane / 16;
     const int ht = wave % HT;  // this wave's head tile
@@ -987,8 +1020,9 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     }
     // q^T of this wave's 16 heads as the B operand of Step I (zero past GT), and the end of
     // the rows this lane's head may see (the segment's, or the causal bound)
-    bf16x8_t qb[KB];
+    uint4 qb[KB];  // bf16, or fp16 for int8
     int rend;
+    float scl = sc;  // this lane's head's score scale
     {
         const int head = ht * 16 + lr;
         const QRow qr = query_row(a, b, kvh, h0, head < GT ? head : 0, slen);
@@ -998,13 +1032,46 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
             uint4 x = {0u, 0u, 0u, 0u};
             if (head < GT)
                 x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qr.row * D + kb * 32 + 8 * lg);
-            qb[kb] = __builtin_bit_cast(bf16x8_t, x);
+            qb[kb] = x;
+        }
+        if constexpr (kF16) {
+            // the head's largest |q| (its elements sit in lanes l, l^16, l^32, l^48), then
+            // q * 2^-e in fp16 with the largest at 2^14 .. 2^15, in fp16's normal range (exact:
+            // a bf16 significand fits fp16's; e stays >= -100 so that 2^-e is a finite float)
+            float mx = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const uint32_t w4[4] = {qb[kb].x, qb[kb].y, qb[kb].z, qb[kb].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(w4[j] << 16)), fabsf(__uint_as_float(w4[j] & 0xffff0000u))));
+            }
+            mx = xor32_max(xor16_max(mx));
+            int ex = 0;
+            (void)frexpf(mx, &ex);  // mx < 2^ex
+            const int e = max(-100, ex - 15);
+            const float down = ldexpf(1.f, -e);
+            scl = ldexpf(sc, e);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const uint32_t w4[4] = {qb[kb].x, qb[kb].y, qb[kb].z, qb[kb].w};
+                uint32_t h4[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f16x2_t hv = {(_Float16)(__uint_as_float(w4[j] << 16) * down),
+                                        (_Float16)(__uint_as_float(w4[j] & 0xffff0000u) * down)};
+                    h4[j] = __builtin_bit_cast(uint32_t, hv);
+                }
+                qb[kb] = uint4{h4[0], h4[1], h4[2], h4[3]};
+            }
         }
     }
     float m = kNegBig, lp = 0.f;
     f32x4_t o[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t osum = {0.f, 0.f, 0.f, 0.f};  // int8: the sum of P as the products used it, per head
+    const f16x8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
     // Rows at or past r1 are never fetched, so their stage bytes must be finite: the stages
     // start zeroed (they may hold the previous segment's merge data otherwise).
@@ -1035,7 +1102,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     // scores; returns P split into bf16 hi / lo in the lane's row order and rescales O.
     // (lazy rescaling as in MfmaAttn::tile: m moves only when a tile max passes it by
     // kLazyRescale)
-    auto softmax = [&](float *x, auto &phi, auto &plo, int nr) {
+    auto softmax = [&](float *x, PV &phi, PV &plo, int nr) {
         float tmax = x[0];
         for (int i = 1; i < nr; ++i) tmax = fmaxf(tmax, x[i]);
         tmax = xor32_max(xor16_max(tmax));
@@ -1048,10 +1115,10 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
         }
         float ps = 0.f;
         for (int i = 0; i < nr; ++i) {
-            const float p = __builtin_amdgcn_exp2f(x[i] - m);
+            const float p = __builtin_amdgcn_exp2f(x[i] - m + kPShift);
             ps += p;
-            phi[i] = (__bf16)p;
-            plo[i] = (__bf16)(p - (float)phi[i]);
+            phi[i] = (PE)p;
+            plo[i] = (PE)(p - (float)phi[i]);
         }
         lp = fmaf(lp, corr, ps);
         if (rescale) {
@@ -1060,6 +1127,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
             for (int nb = 0; nb < NB; ++nb) {
                 o[nb][0] *= corr; o[nb][1] *= corr; o[nb][2] *= corr; o[nb][3] *= corr;
             }
+            if constexpr (kF16) osum *= corr;
         }
     };
 
@@ -1073,14 +1141,14 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                          (((lg / 2) ^ piece_key(2 * t + lr / 8)) << 7);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            uint4 raw;
-            if constexpr (kLines) {
-                raw = to_bf16x8<KV>(*reinterpret_cast<const uint2 *>(kl + kb * 256));
-            } else {
-                const uint2 v = *reinterpret_cast<const uint2 *>(kt + ((kb * 2 + lg / 2) * 16 + lr) * 16 + 8 * (lg % 2));
-                raw = to_bf16x8<KV>(v);
-            }
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, raw), qb[kb], sacc, 0, 0, 0);
+            const uint2 v = kLines ? *reinterpret_cast<const uint2 *>(kl + kb * 256)
+                                   : *reinterpret_cast<const uint2 *>(kt + ((kb * 2 + lg / 2) * 16 + lr) * 16 + 8 * (lg % 2));
+            if constexpr (kF16)
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, i8x8_to_f16x8(v)),
+                                                             __builtin_bit_cast(f16x8_t, qb[kb]), sacc, 0, 0, 0);
+            else
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, to_bf16x8<KV>(v)),
+                                                              __builtin_bit_cast(bf16x8_t, qb[kb]), sacc, 0, 0, 0);
         }
         return sacc;
     };
@@ -1097,10 +1165,10 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                 float x[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    x[i] = (rb + 4 * lg + i < rend) ? s0[i] * sc : -INFINITY;
-                    x[4 + i] = (rb + 16 + 4 * lg + i < rend) ? s1[i] * sc : -INFINITY;
+                    x[i] = (rb + 4 * lg + i < rend) ? s0[i] * scl : -INFINITY;
+                    x[4 + i] = (rb + 16 + 4 * lg + i < rend) ? s1[i] * scl : -INFINITY;
                 }
-                bf16x8_t phi, plo;
+                PV phi, plo;
                 softmax(x, phi, plo, 8);
                 // V rows in the same order: lane s of group g reads row(g, s/2), bytes
                 // 16*nb + 8*(s%2) .. +8; the transpose read hands lane l the 8 rows of column l%16.
@@ -1110,18 +1178,32 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                 const char *vt = kLines ? st + HALF + (4 * blk + rr / 8) * 1024 + (rr % 8) * 16 + 8 * (lr % 2)
                                         : st + HALF + (2 * blk + rr / 16) * TILE + (rr % 16) * 16 + 8 * (lr % 2);
                 // all hi products, then all lo ones (dependent MFMAs NB instructions apart)
-                bf16x8_t bvs[NB];
+                uint4 bvs[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     const int voff = kLines ? (nb ^ vkey) << 7 : nb * 256;
                     const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                         (__attribute__((address_space(3))) i32x2_t *)(lds_char *)(vt + voff));
-                    bvs[nb] = __builtin_bit_cast(bf16x8_t, to_bf16x8<KV>(uint2{(uint32_t)t[0], (uint32_t)t[1]}));
+                    const uint2 c8 = {(uint32_t)t[0], (uint32_t)t[1]};
+                    bvs[nb] = kF16 ? i8x8_to_f16x8_offset(c8) : to_bf16x8<KV>(c8);
                 }
+                if constexpr (kF16) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bvs[nb], phi, o[nb], 0, 0, 0);
+                    for (int nb = 0; nb < NB; ++nb)
+                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, bvs[nb]), phi, o[nb], 0, 0, 0);
+                    osum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, phi, osum, 0, 0, 0);
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bvs[nb], plo, o[nb], 0, 0, 0);
+                    for (int nb = 0; nb < NB; ++nb)
+                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, bvs[nb]), plo, o[nb], 0, 0, 0);
+                    osum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, plo, osum, 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bvs[nb]), phi, o[nb], 0, 0, 0);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bvs[nb]), plo, o[nb], 0, 0, 0);
+                }
             }
         }
     };
@@ -1146,6 +1228,13 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
         }
     }
     __builtin_amdgcn_s_waitcnt(0);  // no DMA into the stages is outstanding past this point
+    if constexpr (kF16) {  // V entered as code + 1152
+        const float excess = 1152.f * osum[0];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            o[nb][0] -= excess; o[nb][1] -= excess; o[nb][2] -= excess; o[nb][3] -= excess;
+        }
+    }
 
     // Merge: lane groups share each head's max (sums add); then waves holding the same head
     // tile merge through LDS and one wave per head tile writes.
@@ -1202,7 +1291,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                 *reinterpret_cast<f32x4_t *>(&a.part_o[(k * GT + hd) * D + nb * 16 + 4 * lg]) = v;
         }
         if (!direct && lg == 0) {
-            a.part_ml[(k * GT + hd) * 2 + 0] = mres;
+            a.part_ml[(k * GT + hd) * 2 + 0] = mres - kPShift;
             a.part_ml[(k * GT + hd) * 2 + 1] = lres;
         }
     }

@@ -215,6 +215,21 @@ def test_int8_decoding_of_every_code():
         assert np.array_equal(out.cpu().double().numpy(), np.repeat(expect, h_q, axis=1)), f"h_q={h_q}"
 
 
+@pytest.mark.parametrize("qmul", [2.0 ** -20, 2.0 ** -8, 1.0, 2.0 ** 8, 2.0 ** 17])
+@pytest.mark.parametrize("d", [128, 64])
+def test_int8_matrix_cores_across_query_magnitudes(qmul, d):
+    """The int8 matrix-core path runs Step I in fp16 with q scaled by a power of two per head:
+    queries from 2^-20 to 2^17 times N(0, 1) (beyond fp16's range at the top, in its subnormals
+    at the bottom) must still match the oracle."""
+    w = W(B=2, h_q=8, h_kv=1, d=d, cap=400, kv_dtype="int8", lens=("uniform", 1, 400), seed=91)
+    c = workloads.generate(w)
+    c["q"] = (c["q"].float() * qmul).to(torch.bfloat16)
+    log(f"case int8 q x {qmul} d={d} lens={c['lens_final'].tolist()}")
+    out, _, _, err = run_gpu(w, c)
+    assert err == 0
+    check_close(out, oracle_out(w, c), "int8")
+
+
 def test_gqa_equals_mha_on_broadcast_cache():
     """I3 on the GPU: the grouped kernel equals the one-head-per-group kernel on a
     repeat_interleave'd cache, within the bf16 tolerance."""
