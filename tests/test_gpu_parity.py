@@ -154,6 +154,24 @@ def test_parity_more_workgroups_than_rows(kv, h_q):
     check_close(two, ref, kv, "two stages")
 
 
+@pytest.mark.parametrize("kv,d,h_q,h_kv", [("fp8", 128, 64, 8), ("bf16", 64, 64, 4), ("int8", 64, 64, 8)])
+def test_parity_combine_with_several_rows_per_workgroup(kv, d, h_q, h_kv):
+    """Batches with thousands of query rows, where the combine gives each workgroup several
+    query rows of one (sequence, KV head, head tile); the two-stage form, so that every
+    unit goes through the combine."""
+    w = W(B=32, h_q=h_q, h_kv=h_kv, d=d, cap=300, kv_dtype=kv, lens=("uniform", 1, 300), seed=83)
+    c = workloads.generate(w)
+    log(f"case combine rows/workgroup {kv} d={d} h_q={h_q} h_kv={h_kv}")
+    desc = desc_of(w)
+    g = to_gpu(c)
+    ws = da.Workspace(desc, 300)
+    out = torch.empty(w.B, w.h_q, w.d, device="cuda")
+    da.decode_attn_partial(desc, g["q"], g["k_cache"], g["v_cache"], g["lens_final"], 300, g["kv_scales"], ws)
+    da.decode_attn_combine(desc, g["lens_final"], 300, out, ws)
+    assert da.da_read_device_error(ws) == 0
+    check_close(out, oracle_out(w, c), kv)
+
+
 def test_invalid_lengths_between_valid_ones():
     """Sequences with an out-of-range length hold no rows of the partition: their output
     is zeroed and flagged, and the sequences around them are unaffected."""
