@@ -598,26 +598,10 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// Two int8 codes (bytes 2*HI, 2*HI+1 of w) -> two bf16 packed in a word: each code is an
-// integer of at most 8 significant bits, so its fp32 value has zero low halves and the high
-// halves are the exact bf16 values.
-template <bool HI>
-__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w) {
-    const float lo = i8_to_f32(w, 2 * HI), hi = i8_to_f32(w, 2 * HI + 1);
-    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// Eight 8-bit codes (fp8 or int8) as bf16x8, exactly.
-template <int KV>
-__device__ __forceinline__ uint4 to_bf16x8(const uint2 &v) {
-    static_assert(Kv<KV>::kEsz == 1, "8-bit codes");
-    if constexpr (KV == DA_INT8) {
-        return uint4{i8x2_to_bf16x2<false>(v.x), i8x2_to_bf16x2<true>(v.x), i8x2_to_bf16x2<false>(v.y),
-                     i8x2_to_bf16x2<true>(v.y)};
-    } else {
-        return uint4{fp8x2_to_bf16x2<false>(v.x), fp8x2_to_bf16x2<true>(v.x), fp8x2_to_bf16x2<false>(v.y),
-                     fp8x2_to_bf16x2<true>(v.y)};
-    }
+// Eight e4m3fn codes as bf16x8, exactly.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(const uint2 &v) {
+    return uint4{fp8x2_to_bf16x2<false>(v.x), fp8x2_to_bf16x2<true>(v.x), fp8x2_to_bf16x2<false>(v.y),
+                 fp8x2_to_bf16x2<true>(v.y)};
 }
 
 // Steps I-III on the matrix cores for query heads h0 .. h0+GT-1 of one (sequence, KV head).
@@ -1147,7 +1131,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                 sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, i8x8_to_f16x8(v)),
                                                              __builtin_bit_cast(f16x8_t, qb[kb]), sacc, 0, 0, 0);
             else
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, to_bf16x8<KV>(v)),
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(v)),
                                                               __builtin_bit_cast(bf16x8_t, qb[kb]), sacc, 0, 0, 0);
         }
         return sacc;
@@ -1185,7 +1169,10 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                     const auto t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                         (__attribute__((address_space(3))) i32x2_t *)(lds_char *)(vt + voff));
                     const uint2 c8 = {(uint32_t)t[0], (uint32_t)t[1]};
-                    bvs[nb] = kF16 ? i8x8_to_f16x8_offset(c8) : to_bf16x8<KV>(c8);
+                    if constexpr (kF16)
+                        bvs[nb] = i8x8_to_f16x8_offset(c8);
+                    else
+                        bvs[nb] = fp8x8_to_bf16x8(c8);
                 }
                 if constexpr (kF16) {
 #pragma unroll
@@ -1316,7 +1303,6 @@ struct SegWalk {
     int64_t pos, end, w;
     int b, L, ul, row, upb, g, gt, tiles, append_cap;
     bool has;  // a current segment
-    int ord;   // its ordinal within the workgroup (counts on past the last)
     int sb, kvh, h0, r0, r1;
     int slen;      // rows of the segment's sequence (the walk state moves on past them)
     size_t k;
@@ -1341,7 +1327,6 @@ struct SegWalk {
         w = blockIdx.x;
         pos = wg_start(w, Tot, N);
         end = wg_start(w + 1, Tot, N);
-        ord = -1;
         b = 0, L = 1, ul = 0, row = 0;
         empty_unit = -1;
         if (pos < Tot) {
@@ -1361,7 +1346,6 @@ struct SegWalk {
         next();
     }
     __device__ __forceinline__ void next() {
-        ++ord;
         has = pos < end;
         if (!has) return;
         r0 = row;
