@@ -173,8 +173,17 @@ def main() -> int:
     lens_first = (c["lens_init"] + 1 if appends else lens_final).to(torch.int64)
     kv_bytes0 = int(lens_first.sum()) * row_bytes
     R = args.rotations or max(2, min(8, math.ceil((2 << 30) / max(kv_bytes0, 1))))
+
+    def uses_per_copy(r):  # steps (warm-up, timed, graph replays) that append to each copy
+        return -(-(args.warmup + args.steps) // r) + (max(1, args.steps // r) if args.graph else 0)
+
+    if appends and not args.rotations:
+        # a long run takes more copies, so that no sequence reaches the capacity
+        room = w.cap - int(lens_first.max()) + 1
+        while uses_per_copy(R) > room and R < 32:
+            R += 1
     graph_reps = max(1, args.steps // R) if args.graph else 0
-    uses = -(-(args.warmup + args.steps) // R) + graph_reps
+    uses = uses_per_copy(R)
     max_len = int(lens_first.max()) + (uses - 1 if appends else 0)
     if max_len > w.cap:
         print(f"bench.py: {uses} appends per cache copy overflow cap {w.cap}; use fewer steps",
