@@ -36,7 +36,8 @@ def code_digest() -> str:
     import hashlib
     with open(SRC, "rb") as f:
         src = f.read()
-    return hashlib.sha256(src + b"\0" + " ".join(FLAGS).encode()).hexdigest()
+    flags = [os.path.relpath(f, ROOT) if f.startswith(ROOT) else f for f in FLAGS]  # path-independent
+    return hashlib.sha256(src + b"\0" + " ".join(flags).encode()).hexdigest()
 
 
 def build_library(verbose: bool = False) -> str:
