@@ -131,6 +131,23 @@ def stream_ceiling(dev, reps: int = 10, warm_ms: float = 60.0) -> dict:
             "kernel": "stream_read_kernel (16-byte non-temporal buffer loads, 512 workgroups)"}
 
 
+def uses_per_copy(r: int, warmup: int, steps: int, graph: bool) -> int:
+    """Steps (warm-up, timed, graph replays) that use each of r rotating cache copies."""
+    return -(-(warmup + steps) // r) + (max(1, steps // r) if graph else 0)
+
+
+def cache_rotations(kv_bytes: int, warmup: int, steps: int, graph: bool, room=None) -> int:
+    """Cache copies to rotate: enough that they hold at least 2 GiB (so the 256 MB Infinity
+    Cache cannot serve a step from the previous one), 2 to 8; with appends (room = the
+    appends a copy takes before its longest sequence is full) more, up to 32, when a long run
+    would otherwise fill a sequence."""
+    r = max(2, min(8, math.ceil((2 << 30) / max(kv_bytes, 1))))
+    if room is not None:
+        while uses_per_copy(r, warmup, steps, graph) > room and r < 32:
+            r += 1
+    return r
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -172,18 +189,10 @@ def main() -> int:
     # use u of a cache copy (u = step // R) attends over lens_init + 1 + u rows when appending
     lens_first = (c["lens_init"] + 1 if appends else lens_final).to(torch.int64)
     kv_bytes0 = int(lens_first.sum()) * row_bytes
-    R = args.rotations or max(2, min(8, math.ceil((2 << 30) / max(kv_bytes0, 1))))
-
-    def uses_per_copy(r):  # steps (warm-up, timed, graph replays) that append to each copy
-        return -(-(args.warmup + args.steps) // r) + (max(1, args.steps // r) if args.graph else 0)
-
-    if appends and not args.rotations:
-        # a long run takes more copies, so that no sequence reaches the capacity
-        room = w.cap - int(lens_first.max()) + 1
-        while uses_per_copy(R) > room and R < 32:
-            R += 1
+    R = args.rotations or cache_rotations(kv_bytes0, args.warmup, args.steps, args.graph,
+                                          w.cap - int(lens_first.max()) + 1 if appends else None)
     graph_reps = max(1, args.steps // R) if args.graph else 0
-    uses = uses_per_copy(R)
+    uses = uses_per_copy(R, args.warmup, args.steps, args.graph)
     max_len = int(lens_first.max()) + (uses - 1 if appends else 0)
     if max_len > w.cap:
         print(f"bench.py: {uses} appends per cache copy overflow cap {w.cap}; use fewer steps",

@@ -1,0 +1,59 @@
+"""Host logic of bench.py, no GPU: the one-GPU guard, the lookup of profiled traffic by the
+device-code digest, and the number of rotating cache copies."""
+import os
+import re
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _recorded_digest(workload: str) -> str:
+    text = open(os.path.join(ROOT, "profiles", f"split_kv_attn__{workload}__pmc.txt")).read()
+    return re.search(r"^source_sha256:\s*(\S+)\s*$", text, re.M).group(1)
+
+
+def test_profiled_traffic_only_for_the_code_it_was_taken_on(monkeypatch):
+    digest = _recorded_digest("gqa8_bf16")
+    monkeypatch.setattr(bench, "source_sha", lambda: digest)
+    traffic = bench.profiled_traffic("gqa8_bf16")
+    assert traffic is not None and traffic > 1e9
+    monkeypatch.setattr(bench, "source_sha", lambda: "0" * 64)
+    assert bench.profiled_traffic("gqa8_bf16") is None
+    assert bench.profiled_traffic("no_such_workload") is None
+
+
+def test_code_digest_ignores_where_the_repository_sits(monkeypatch):
+    from decode_attention_kv_split_amd import build
+    here = build.code_digest()
+    assert re.fullmatch(r"[0-9a-f]{64}", here)
+    elsewhere = "/elsewhere/repo"
+    monkeypatch.setattr(build, "FLAGS", [f.replace(build.ROOT, elsewhere) for f in build.FLAGS])
+    monkeypatch.setattr(build, "ROOT", elsewhere)
+    assert build.code_digest() == here
+    monkeypatch.setattr(build, "FLAGS", build.FLAGS + ["-O0"])
+    assert build.code_digest() != here
+
+
+def test_cache_rotations():
+    gib = 1 << 30
+    # at least 2 GiB across the copies, 2 to 8 of them
+    assert bench.cache_rotations(2 * gib, 10, 100, False) == 2
+    assert bench.cache_rotations(gib // 4, 10, 100, False) == 8
+    assert bench.cache_rotations(gib // 100, 10, 100, False) == 8
+    # with appends, enough copies that no sequence fills up: room for 865 appends per copy
+    for warmup, steps in [(10, 100), (100, 1000), (10, 3000), (100, 20000)]:
+        r = bench.cache_rotations(2 * gib, warmup, steps, False, room=865)
+        assert bench.uses_per_copy(r, warmup, steps, False) <= 865
+        assert r == 2 or bench.uses_per_copy(r - 1, warmup, steps, False) > 865
+    # graph replays append once per copy per replay
+    assert bench.uses_per_copy(2, 10, 100, True) == 55 + 50
