@@ -30,14 +30,39 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
          "-I", os.path.join(ROOT, "include")]
 
 
+def _code_tokens(text: str) -> str:
+    """The source without comments, whitespace runs collapsed (string and character literals
+    kept as written), so that edits of comments or layout leave the digest alone."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def code_digest() -> str:
-    """sha256 of the kernel source and the compiler flags: it names the device code that a
-    measurement was taken on."""
+    """sha256 of the kernel source and header (comments and layout aside) and the compiler
+    flags (repository paths made relative): it names the device code that a measurement was
+    taken on."""
     import hashlib
-    with open(SRC, "rb") as f:
-        src = f.read()
-    flags = [os.path.relpath(f, ROOT) if f.startswith(ROOT) else f for f in FLAGS]  # path-independent
-    return hashlib.sha256(src + b"\0" + " ".join(flags).encode()).hexdigest()
+    parts = [_code_tokens(open(p, encoding="utf-8").read()) for p in (SRC, HEADER)]
+    flags = [os.path.relpath(f, ROOT) if f.startswith(ROOT) else f for f in FLAGS]
+    return hashlib.sha256("\0".join(parts + [" ".join(flags)]).encode()).hexdigest()
 
 
 def build_library(verbose: bool = False) -> str:

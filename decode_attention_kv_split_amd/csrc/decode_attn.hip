@@ -273,9 +273,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
 // the same number of rows whatever the length mix, and N is chosen so that all of them are
 // resident at once. A workgroup's range cut by unit boundaries gives "segments"; the
 // (w, u) pairs of all segments form a monotone staircase, so k = w + u numbers them
-// uniquely (k < N + units) and indexes their partial results. The workgroups that touch
-// unit u are w in [owner(P_u), owner(P_u + L - 1)], owner(x) = ((x + 1) * N - 1) / T,
-// skipping any with an empty range.
+// uniquely (k < N + units) and indexes their partial results. The workgroups holding a
+// unit's first and last rows record themselves for the combine, and every workgroup between
+// them leaves a partial for the unit (an empty one when its range holds no rows, which only
+// happens with fewer rows than workgroups).
 constexpr int kMaxBatch = 1024;
 constexpr int kMaxQueries = 1024;  // query rows per sequence in one call
 

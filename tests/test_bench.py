@@ -57,3 +57,12 @@ def test_cache_rotations():
         assert r == 2 or bench.uses_per_copy(r - 1, warmup, steps, False) > 865
     # graph replays append once per copy per replay
     assert bench.uses_per_copy(2, 10, 100, True) == 55 + 50
+
+
+def test_code_digest_keeps_comments_and_layout_out():
+    from decode_attention_kv_split_amd import build
+    a = build._code_tokens('int a = 1; // note\n/* block */ const char *s = "x // y /* z */";\n')
+    b = build._code_tokens('int a = 1;\n  const char *s = "x // y /* z */";  // other note')
+    assert a == b == 'int a = 1; const char *s = "x // y /* z */";'
+    assert build._code_tokens("int a = 2;") != build._code_tokens("int a = 1;")
+    assert build._code_tokens("char c = '/'; // x") == "char c = '/';"
