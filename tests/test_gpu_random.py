@@ -5,9 +5,11 @@ tests take one at a time: cache type (fp32, bf16, fp8, int8), head dimension (64
 size g (1 to 32, multiples of 4 or not), query rows per sequence T (1 to 8), batch, ragged
 lengths from T to the capacity, rows per workgroup (the library's choice or small shares that
 cut units into many segments), and the one-call or the two-stage form. Each must match the
-oracle within its cache type's tolerance, with no device error.
+oracle within its cache type's tolerance, with no device error; sixty more drive the fused decode step.
 """
 import random
+
+import numpy as np
 
 import pytest
 import torch
@@ -67,3 +69,42 @@ def test_random_configuration(case):
                                   kv_scales=c["kv_scales"])
     got = out if T > 1 else out.unsqueeze(1)
     check_close(got, ref, kv, f"r{i}")
+
+
+APPEND_CASES = [c for c in draw_cases(60, seed=4048)]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[f"a{c[0]}" for c in APPEND_CASES])
+def test_random_fused_step(case):
+    """The fused decode step (one query row per sequence) on random configurations: the
+    appended caches bit-exact, lengths + 1, and the output within tolerance of the oracle
+    over the appended caches."""
+    i, kv, d, h_q, h_kv, _, B, cap, block_rows, two_stage = case
+    w = workloads.Workload("rand_append", B, h_q, h_kv, d, cap, "f32" if kv == "f32" else "bf16", kv,
+                           ("uniform", 2, cap), 1, 9000 + i, workloads._inv_sqrt(d))
+    c = workloads.generate(w)
+    log(f"case random fused a{i}: {kv} d={d} h_q={h_q} h_kv={h_kv} B={B} cap={cap} block_rows={block_rows} "
+        f"two_stage={two_stage} lens={c['lens_final'].tolist()}")
+    desc = da.Desc(B, h_q, h_kv, d, cap, workloads.TORCH_DTYPE[w.q_dtype], workloads.TORCH_DTYPE[kv], w.scale,
+                   block_rows)
+    g = to_gpu(c)
+    lens = g["lens_init"].clone()
+    kn, vn = g["k_new"][0].contiguous(), g["v_new"][0].contiguous()
+    ws = da.Workspace(desc, cap)
+    out = torch.full(desc.rows_shape(), 5.0, device="cuda")
+    if two_stage:
+        da.decode_attn_append_partial(desc, g["q"], g["k_cache"], g["v_cache"], lens, kn, vn, cap, g["kv_scales"], ws)
+        da.decode_attn_append_combine(desc, lens, cap, out, ws)
+    else:
+        da.decode_attn_append_run(desc, g["q"], g["k_cache"], g["v_cache"], lens, kn, vn, cap, g["kv_scales"], out, ws)
+    assert da.da_read_device_error(ws) == 0
+    assert lens.cpu().tolist() == c["lens_final"].tolist()
+    kh, vh = oracle._np(c["k_cache"]).copy(), oracle._np(c["v_cache"]).copy()
+    lh = c["lens_init"].numpy().astype(np.int32).copy()
+    oracle.kv_append(kh, vh, lh, oracle._np(c["k_new"][0]).copy(), oracle._np(c["v_new"][0]).copy())
+    for b in range(B):  # the rows the step wrote and everything before them
+        L = int(lh[b])
+        assert np.array_equal(oracle._np(g["k_cache"][b, :, :L].cpu()), kh[b, :, :L])
+        assert np.array_equal(oracle._np(g["v_cache"][b, :, :L].cpu()), vh[b, :, :L])
+    ref = oracle.decode_f64(c["q"], kh, vh, lh, w.scale, kv_scales=c["kv_scales"])
+    check_close(out, ref, kv, f"a{i}")
