@@ -944,10 +944,12 @@ __device__ __forceinline__ uint4 i8x8_to_f16x8(const uint2 &v) {
 //   * Each wave owns one 16-head tile (its own q operand, running max, sums and O) and a
 //     share of the stage's 32-row P.V blocks (Step III by v_mfma_f32_16x16x32_bf16 with P's 8
 //     rows per lane taken from the block's two score tiles, V read as codes by
-//     ds_read_b64_tr_b8 and widened to bf16 in registers, exactly). Step I uses
-//     v_mfma_f32_16x16x32_bf16 (K widened to bf16 after its LDS read). Step III is computed transposed, O^T += V^T . P^T (the V read is the
-//     A operand, the score layout the B operand), so that each lane holds d rows of its own
-//     head and rescales them by that head's factor with no exchange.
+//     ds_read_b64_tr_b8 and widened in registers: fp8 exactly to bf16, int8 to fp16 as
+//     code + 1152). Step I uses v_mfma_f32_16x16x32_bf16 (fp8 K widened to bf16 after its LDS
+//     read; int8 K exactly to fp16 and the _f16 instruction). Step III is computed
+//     transposed, O^T += V^T . P^T (the V read is the A operand, the score layout the B
+//     operand), so that each lane holds d rows of its own head and rescales them by that
+//     head's factor with no exchange.
 //   * At the end the waves holding the same head tile merge through LDS.
 // Swizzle key of the piece (8 rows of 128 bytes) at index m of a stage: flips the parity of
 // every chunk index in pieces whose Gray code is odd, so that pieces 2t / 2t+1 (one K tile)
