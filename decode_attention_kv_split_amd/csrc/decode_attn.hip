@@ -906,8 +906,9 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
 
 // int8 codes on the matrix cores go through fp16, whose 11-bit significand holds 1024 + u
 // exactly for any byte u: with the code's sign bit flipped (u = code + 128) and 0x64 as the
-// high byte, a half is 1024 + u = code + 1152, two halves per v_perm. That costs 0.75
-// instructions per code, against 1.5 for an exact int8 -> bf16 conversion.
+// high byte, a half is 1024 + u = code + 1152, two halves per v_perm; a packed subtraction
+// of 1152 leaves the code. That costs 1.25 instructions per code, against 1.5 for an exact
+// int8 -> bf16 conversion.
 // Eight codes -> fp16 code + 1152 (as raw halves).
 __device__ __forceinline__ uint4 i8x8_to_f16x8_offset(const uint2 &v) {
     const uint32_t x = v.x ^ 0x80808080u, y = v.y ^ 0x80808080u;
@@ -975,10 +976,8 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     constexpr int VM_STAGE = 2 * DPW;          // DMA ops of one stage per wave
     constexpr bool kLines = ROWB == 128;       // 8-bit codes, d = 128: whole-line DMA layout
     static_assert(NBLK % WPH == 0 && (HALF / 1024) % kWaves == 0, "stage split");
-    // int8 goes through fp16: K exactly, q scaled by a power of two per head into fp16's
-    // range (the factor moves to the score scale), P split into fp16 hi + lo, and V as
-    // code + 1152, whose excess, 1152 times the sum of the P the products used, a ones A
-    // operand accumulates beside O and the end takes off.
+    // int8 goes through fp16: K and V exactly, q scaled by a power of two per head into
+    // fp16's range (the factor moves to the score scale), P split into fp16 hi + lo.
     constexpr bool kF16 = KV == DA_INT8;
     // fp16 P is taken 2^7 times larger (at most 2^15 with the lazy rescaling), which keeps
     // small weights out of fp16's subnormals; the segment's sums and rows carry the factor,
@@ -1057,8 +1056,6 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     f32x4_t o[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    f32x4_t osum = {0.f, 0.f, 0.f, 0.f};  // int8: the sum of P as the products used it, per head
-    const f16x8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
     // Rows at or past r1 are never fetched, so their stage bytes must be finite: the stages
     // start zeroed (they may hold the previous segment's merge data otherwise).
@@ -1114,7 +1111,6 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
             for (int nb = 0; nb < NB; ++nb) {
                 o[nb][0] *= corr; o[nb][1] *= corr; o[nb][2] *= corr; o[nb][3] *= corr;
             }
-            if constexpr (kF16) osum *= corr;
         }
     };
 
@@ -1173,7 +1169,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
                         (__attribute__((address_space(3))) i32x2_t *)(lds_char *)(vt + voff));
                     const uint2 c8 = {(uint32_t)t[0], (uint32_t)t[1]};
                     if constexpr (kF16)
-                        bvs[nb] = i8x8_to_f16x8_offset(c8);
+                        bvs[nb] = i8x8_to_f16x8(c8);
                     else
                         bvs[nb] = fp8x8_to_bf16x8(c8);
                 }
@@ -1181,11 +1177,9 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
                         o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, bvs[nb]), phi, o[nb], 0, 0, 0);
-                    osum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, phi, osum, 0, 0, 0);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
                         o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, bvs[nb]), plo, o[nb], 0, 0, 0);
-                    osum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, plo, osum, 0, 0, 0);
                 } else {
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
@@ -1218,13 +1212,6 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
         }
     }
     __builtin_amdgcn_s_waitcnt(0);  // no DMA into the stages is outstanding past this point
-    if constexpr (kF16) {  // V entered as code + 1152
-        const float excess = 1152.f * osum[0];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            o[nb][0] -= excess; o[nb][1] -= excess; o[nb][2] -= excess; o[nb][3] -= excess;
-        }
-    }
 
     // Merge: lane groups share each head's max (sums add); then waves holding the same head
     // tile merge through LDS and one wave per head tile writes.
