@@ -30,6 +30,7 @@ __all__ = [
     "Desc", "DecodeAttnError", "Workspace", "da_workspace_size", "da_plan", "da_workspace_init",
     "kv_append", "decode_attn_run", "decode_attn_partial", "decode_attn_combine",
     "decode_attn_append_run", "decode_attn_append_partial", "decode_attn_append_combine",
+    "decode_attn_run_static",
     "da_read_device_error", "da_stream_read", "da_status_string", "da_last_error", "library_path",
     "DA_F32", "DA_BF16", "DA_FP8_E4M3FN", "DA_INT8", "DEV_ERR_APPEND_FULL", "DEV_ERR_LEN_RANGE",
 ]
@@ -254,6 +255,19 @@ def decode_attn_append_combine(desc: Desc, lens, max_len: int, out, workspace) -
     cd = desc.c()
     _check(lib().decode_attn_append_combine(ctypes.byref(cd), ln, int(max_len), op, wp, wn, _stream(out)),
            "decode_attn_append_combine")
+
+
+def decode_attn_run_static(desc: Desc, q, k_cache, v_cache, lens, max_len: int, kv_scales, out,
+                           dev_err=None) -> None:
+    """decode_attn_run with the partials in the library's static per-device scratch: no
+    workspace, nothing allocated. dev_err: optional int32 GPU tensor of one element that
+    receives the device error bits (the caller clears it)."""
+    qp, kc, vc, ln, sc = _attn_args(desc, q, k_cache, v_cache, lens, kv_scales)
+    op = _dev(out, "out", desc.rows_shape(), torch.float32, q.device)
+    ep = _dev(dev_err, "dev_err", (1,), torch.int32, q.device) if dev_err is not None else ctypes.c_void_p(None)
+    cd = desc.c()
+    _check(lib().decode_attn_run_static(ctypes.byref(cd), qp, kc, vc, ln, int(max_len), sc, op, ep, _stream(q)),
+           "decode_attn_run_static")
 
 
 def da_stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:

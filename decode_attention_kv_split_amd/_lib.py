@@ -29,6 +29,7 @@ SIGNATURES = {
     "decode_attn_append_run": (ctypes.c_int, [P, P, P, P, P, P, P, I32, P, P, P, SZ, P]),
     "decode_attn_append_partial": (ctypes.c_int, [P, P, P, P, P, P, P, I32, P, P, SZ, P]),
     "decode_attn_append_combine": (ctypes.c_int, [P, P, I32, P, P, SZ, P]),
+    "decode_attn_run_static": (ctypes.c_int, [P, P, P, P, P, I32, P, P, P, P]),
     "da_stream_read": (ctypes.c_int, [P, SZ, P, P]),
     "da_read_device_error": (ctypes.c_int, [P, P, P]),
     "da_status_string": (ctypes.c_char_p, [ctypes.c_int]),

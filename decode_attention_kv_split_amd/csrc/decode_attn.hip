@@ -1798,10 +1798,11 @@ Partition partition_of(const da_desc *desc, const Plan &p, int max_len, bool app
 
 // Checks the run arguments and launches the split kernel: with out non-NULL, units that one
 // workgroup covers are written to out directly (decode_attn_run); otherwise every segment
-// writes its partial result (decode_attn_partial).
+// writes its partial result (decode_attn_partial). Device error bits go to err_word when it is
+// given, else to the workspace's own error word.
 int run_split(const da_desc *desc, const void *q, const void *k_cache, const void *v_cache, const int32_t *lens,
               const void *k_new, const void *v_new, int32_t max_len, const float *kv_scales, float *out,
-              void *workspace, size_t ws_bytes, void *stream, const char *who) {
+              void *workspace, size_t ws_bytes, void *stream, const char *who, int32_t *err_word = nullptr) {
     Plan p;
     int rc = make_plan(desc, max_len, &p);
     if (rc) return rc;
@@ -1837,7 +1838,7 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     args.k_new = k_new;
     args.v_new = v_new;
     args.lens_copy = reinterpret_cast<int32_t *>(ws + p.lens_off);
-    args.err = reinterpret_cast<int32_t *>(ws);
+    args.err = err_word ? err_word : reinterpret_cast<int32_t *>(ws);
     args.row_bytes = desc->d_k * elem_size(desc->kv_dtype);
     args.unit_wg = reinterpret_cast<int2 *>(ws + p.unit_off);
     args.dv = desc->d_v;
@@ -1850,7 +1851,8 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
 }
 
 int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out, void *workspace,
-                size_t ws_bytes, void *stream, int skip_single, bool append, const char *who) {
+                size_t ws_bytes, void *stream, int skip_single, bool append, const char *who,
+                int32_t *err_word = nullptr) {
     Plan p;
     int rc = make_plan(desc, max_len, &p);
     if (rc) return rc;
@@ -1863,7 +1865,7 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
     const float *ml = reinterpret_cast<const float *>(ws + p.ml_off);
     const int2 *uw = reinterpret_cast<const int2 *>(ws + p.unit_off);
     const float *po = reinterpret_cast<const float *>(ws + p.o_off);
-    int32_t *err = reinterpret_cast<int32_t *>(ws);
+    int32_t *err = err_word ? err_word : reinterpret_cast<int32_t *>(ws);
     if (append && n_queries(desc) > 1)
         return fail(DA_ERR_UNSUPPORTED, "%s: the fused append takes one query per sequence (n_queries %d)", who,
                     desc->n_queries);
@@ -1893,6 +1895,34 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
         hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, ml, po, out, err,
                            desc->h_q, p.gt, rw, pt, skip_single);
     return launch_status("lse_combine_kernel");
+}
+
+// Scratch of decode_attn_run_static: the workspace of decode_attn_run for callers that cannot
+// allocate. One copy per device, held from the library's load on that device until the process
+// ends. Host code never uses the array's name as an address (on the host it is only a stand-in
+// for the symbol): the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+__device__ __align__(256) char scratch[kStaticScratchBytes];
+
+// Device address of this device's scratch (looked up on the first call on each device).
+int static_scratch(void **ptr) {
+    static std::mutex mu;
+    static std::map<int, void *> addr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DA_ERR_LAUNCH, "decode_attn_run_static: hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = addr.find(dev);
+    if (it == addr.end()) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(DA_ERR_LAUNCH, "decode_attn_run_static: scratch address on device %d: %s", dev,
+                        hipGetErrorString(e));
+        it = addr.emplace(dev, p).first;
+    }
+    *ptr = it->second;
+    return DA_OK;
 }
 
 }  // namespace
@@ -2009,6 +2039,30 @@ int decode_attn_append_run(const da_desc *desc, const void *q, void *k_cache, vo
                              ws_bytes, stream, "decode_attn_append_run");
     if (rc) return rc;
     return run_combine(desc, lens, max_len, out, workspace, ws_bytes, stream, 1, true, "decode_attn_append_run");
+}
+
+int decode_attn_run_static(const da_desc *desc, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *lens, int32_t max_len, const float *kv_scales, float *out,
+                           int32_t *dev_err, void *stream) {
+    if (!out) return fail(DA_ERR_INVALID_ARG, "decode_attn_run_static: out is NULL");
+    if (dev_err && (reinterpret_cast<uintptr_t>(dev_err) & 3u))
+        return fail(DA_ERR_INVALID_ARG, "decode_attn_run_static: dev_err is not 4-byte aligned");
+    Plan p;
+    int rc = make_plan(desc, max_len, &p);
+    if (rc) return rc;
+    if (p.bytes > kStaticScratchBytes)
+        return fail(DA_ERR_WORKSPACE, "decode_attn_run_static: needs %zu bytes of scratch, the static scratch holds %zu",
+                    p.bytes, kStaticScratchBytes);
+    void *ws = nullptr;
+    rc = static_scratch(&ws);
+    if (rc) return rc;
+    // without dev_err the error bits land in the scratch's own error word, which nothing reads
+    int32_t *err = dev_err ? dev_err : static_cast<int32_t *>(ws);
+    rc = run_split(desc, q, k_cache, v_cache, lens, nullptr, nullptr, max_len, kv_scales, out, ws, p.bytes, stream,
+                   "decode_attn_run_static", err);
+    if (rc) return rc;
+    return run_combine(desc, const_cast<int32_t *>(lens), max_len, out, ws, p.bytes, stream, 1, false,
+                       "decode_attn_run_static", err);
 }
 
 int da_stream_read(const void *buf, size_t bytes, float *sink, void *stream) {

@@ -203,6 +203,25 @@ int decode_attn_append_combine(const da_desc *desc, int32_t *lens, int32_t max_l
                                void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * decode_attn_run without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops that must not allocate, harnesses that forbid
+ * it). Same arguments, kernels and results as decode_attn_run (bit for bit), except:
+ *   - the split partials live in a static scratch array the library holds on each device it
+ *     runs on (16 MiB, kept until the process ends); a (desc, max_len) whose
+ *     da_workspace_size() exceeds 16 MiB is rejected with DA_ERR_WORKSPACE, nothing launched;
+ *   - dev_err (device int32, caller-owned, 4-byte aligned, may be NULL) receives the
+ *     DA_DEV_ERR_* bits ORed in, as the workspace's error word does for decode_attn_run; the
+ *     caller clears it. With NULL the bits are dropped (the work is still skipped and zeroed).
+ * Nothing is allocated or freed on any call. Every call on a device shares that device's
+ * scratch, which keeps the last call's contents (no part of it needs clearing between calls):
+ * calls that overlap on one device (other streams, other threads) race and must be ordered
+ * by the caller.
+ */
+int decode_attn_run_static(const da_desc *desc, const void *q, const void *k_cache,
+                           const void *v_cache, const int32_t *lens, int32_t max_len,
+                           const float *kv_scales, float *out, int32_t *dev_err, void *stream);
+
+/*
  * Measurement helper, not part of the attention path: a plain streaming read of `bytes` bytes
  * at buf (16-byte aligned, bytes a positive multiple of 16) by 512 workgroups, each reading a
  * contiguous chunk with 16-byte non-temporal loads. sink is a device buffer of at least 512

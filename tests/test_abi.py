@@ -195,3 +195,17 @@ def test_multi_query_plan_and_limits(lib):
     assert lib.decode_attn_append_run(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, None, FAKE, FAKE,
                                       n, None) == -2
     assert lib.decode_attn_append_combine(ctypes.byref(d), FAKE, 100, FAKE, FAKE, n, None) == -2
+
+
+def test_static_entry_rejects_work_beyond_its_scratch(lib):
+    """decode_attn_run_static holds its partials in a 16 MiB static scratch: a plan that needs
+    more is refused on the host (DA_ERR_WORKSPACE) before anything is launched."""
+    big = _desc(batch=1024, h_q=32, h_kv=32, cap=4096)
+    rc, n = _ws_size(lib, big, 4096)
+    assert rc == 0 and n > 16 << 20
+    assert lib.decode_attn_run_static(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 4096, None, FAKE, None, None) == -3
+    assert b"static scratch" in lib.da_last_error()
+    d = _desc()
+    assert lib.decode_attn_run_static(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 100, None, None, None, None) == -1
+    assert lib.decode_attn_run_static(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 100, None, FAKE,
+                                      ctypes.c_void_p(0x10002), None) == -1
