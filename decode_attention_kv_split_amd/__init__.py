@@ -18,8 +18,6 @@ Layouts (the same as the C ABI):
 from __future__ import annotations
 
 import ctypes
-import math
-import os
 from dataclasses import dataclass
 
 import torch
@@ -66,15 +64,14 @@ class Desc:
     cap: int
     q_dtype: torch.dtype
     kv_dtype: torch.dtype
-    scale: float | None = None  # default 1/sqrt(d)
+    scale: float                # Step I's factor (1/sqrt(d) in the pages' setting), chosen by the caller
     block_rows: int = 0         # rows per workgroup at max_len; 0: one resident wave, equal shares
     n_queries: int = 1          # query rows per sequence (> 1: multi-query causal decode)
 
     def c(self) -> _CDesc:
-        scale = 1.0 / math.sqrt(self.d) if self.scale is None else self.scale
         return _CDesc(self.batch, self.h_q, self.h_kv, self.d, self.d, self.cap,
                       _TORCH_CODE.get(self.q_dtype, -1), _TORCH_CODE.get(self.kv_dtype, -1),
-                      float(scale), self.block_rows, self.n_queries)
+                      float(self.scale), self.block_rows, self.n_queries)
 
     def rows_shape(self) -> tuple:
         """Shape of q and out: [B, h_q, d], or [B, T, h_q, d] with T = n_queries > 1."""

@@ -1625,6 +1625,9 @@ int heads_per_block(const da_desc *d) {
     return g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
 }
 
+// Bytes past a segment's last row that prefetches may address (LDS stages run up to four 16 KiB
+// stages ahead; register rings one 64-row step of 512-byte rows); kept well above that.
+constexpr int64_t kSlotSlack = int64_t(1) << 20;
 constexpr int kMinRowsPerBlock = 256;  // below this a workgroup's share is mostly overhead
 constexpr int kFallbackResident = 512; // workgroups planned for when no device is visible
 
@@ -1706,6 +1709,13 @@ int make_plan(const da_desc *d, int max_len, Plan *p) {
     if (rc) return rc;
     if (max_len < 1 || max_len > d->cap)
         return fail(DA_ERR_INVALID_ARG, "max_len (%d) must be in [1, cap = %d]", max_len, d->cap);
+    // The kernels address one (sequence, KV head) slot through buffer resources whose size and
+    // lane offsets are 32-bit: every row a pass may touch (up to max_len, plus the prefetches
+    // that run past a segment's end, under kSlotSlack bytes) must lie below 4 GiB.
+    const int64_t row_bytes = (int64_t)d->d_k * elem_size(d->kv_dtype);
+    if ((int64_t)max_len * row_bytes > (int64_t)UINT32_MAX - kSlotSlack)
+        return fail(DA_ERR_UNSUPPORTED, "max_len %d rows of %lld bytes exceed the 4 GiB a (sequence, KV head) slot may span",
+                    max_len, (long long)row_bytes);
     p->mfma = use_mfma(d);
     p->gt = heads_per_block(d);
     p->tiles = group_rows(d) / p->gt;

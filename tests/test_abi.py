@@ -151,14 +151,16 @@ def test_status_strings(lib):
 
 def test_python_binding_marshalling_errors():
     """The binding refuses CPU tensors and wrong shapes before calling the library."""
-    desc = da.Desc(1, 4, 2, 64, 128, torch.bfloat16, torch.bfloat16)
+    desc = da.Desc(1, 4, 2, 64, 128, torch.bfloat16, torch.bfloat16, 0.125)
     q = torch.zeros(1, 4, 64, dtype=torch.bfloat16)
     kc = torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         da.decode_attn_run(desc, q, kc, kc, torch.ones(1, dtype=torch.int32), 1, None,
                            torch.zeros(1, 4, 64), torch.zeros(16, dtype=torch.uint8))
     with pytest.raises(da.DecodeAttnError):
-        da.da_workspace_size(da.Desc(1, 3, 2, 64, 128, torch.bfloat16, torch.bfloat16), 10)
+        da.da_workspace_size(da.Desc(1, 3, 2, 64, 128, torch.bfloat16, torch.bfloat16, 0.125), 10)
+    with pytest.raises(TypeError):  # the caller chooses the scale: the binding has no default
+        da.Desc(1, 4, 2, 64, 128, torch.bfloat16, torch.bfloat16)
 
 
 def test_int8_cache_is_built_and_needs_scales(lib):
@@ -209,3 +211,19 @@ def test_static_entry_rejects_work_beyond_its_scratch(lib):
     assert lib.decode_attn_run_static(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 100, None, None, None, None) == -1
     assert lib.decode_attn_run_static(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 100, None, FAKE,
                                       ctypes.c_void_p(0x10002), None) == -1
+
+
+@pytest.mark.parametrize("kw,max_len,ok", [
+    (dict(q_dtype=0, kv_dtype=0), 8 << 20, False),       # fp32 d=128: 512-byte rows, 4 GiB
+    (dict(q_dtype=0, kv_dtype=0), (8 << 20) - 4096, True),
+    (dict(), 16 << 20, False),                            # bf16 d=128: 256-byte rows
+    (dict(), (16 << 20) - 8192, True),
+    (dict(kv_dtype=2, d_k=64, d_v=64), 64 << 20, False),  # fp8 d=64: 64-byte rows
+])
+def test_slots_beyond_32_bit_offsets_are_refused(lib, kw, max_len, ok):
+    """The kernels' buffer offsets within one (sequence, KV head) slot are 32-bit: a max_len
+    whose rows span 4 GiB or more is refused on the host (DA_ERR_UNSUPPORTED) instead of
+    wrapping on the device."""
+    d = _desc(cap=max_len, batch=1, h_q=2, h_kv=1, **kw)
+    rc, _ = _ws_size(lib, d, max_len)
+    assert rc == (0 if ok else -2), lib.da_last_error()

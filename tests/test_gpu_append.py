@@ -58,7 +58,7 @@ def bits(t: torch.Tensor) -> np.ndarray:
 
 def run_both(kv, d, h_q, h_kv, lens, cap, seed, block_rows):
     c = make_case(kv, d, h_q, h_kv, lens, cap, seed)
-    desc = da.Desc(len(lens), h_q, h_kv, d, cap, c["q"].dtype, TORCH[kv], None, block_rows)
+    desc = da.Desc(len(lens), h_q, h_kv, d, cap, c["q"].dtype, TORCH[kv], workloads._inv_sqrt(d), block_rows)
     max_len = cap
     g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in c.items()}
     sc = g["scales"]
@@ -115,7 +115,7 @@ def test_fused_two_stage_equals_fused_run():
     lens changes only in the combine."""
     kv, d, h_q, h_kv, lens, cap = "bf16", 128, 32, 8, [1000, 1, 2047, 513, 4, 1800], 2048
     c = make_case(kv, d, h_q, h_kv, lens, cap, 377)
-    desc = da.Desc(len(lens), h_q, h_kv, d, cap, torch.bfloat16, torch.bfloat16, None, 256)
+    desc = da.Desc(len(lens), h_q, h_kv, d, cap, torch.bfloat16, torch.bfloat16, workloads._inv_sqrt(d), 256)
     g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in c.items()}
     k1, v1, l1 = g["kc"].clone(), g["vc"].clone(), g["lens"].clone()
     ws1 = da.Workspace(desc, cap)
