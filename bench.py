@@ -60,6 +60,8 @@ def parse_args():
     p.add_argument("--const-len", type=int, default=0,
                    help="override: every sequence this long (the 8K/16K/32K sweep)")
     p.add_argument("--block-rows", type=int, default=0, help="rows per split (0 = library choice)")
+    p.add_argument("--flavour", choices=["auto", "vector", "matrix"], default="auto",
+                   help="split-kernel flavour (auto = the library's choice)")
     p.add_argument("--rotations", type=int, default=0, help="cache copies to rotate (0 = auto)")
     p.add_argument("--graph", action="store_true",
                    help="also time the step replayed from a captured HIP graph (one step per cache copy)")
@@ -93,11 +95,14 @@ def profiled_traffic(workload: str):
     return float(kv["hbm_bytes_per_launch"])
 
 
-def split_kernel_name(w) -> str:
+def split_kernel_name(w, flavour: str = "auto") -> str:
     """The split kernel the library launches for this workload: query groups (g heads times
-    the query rows per sequence) that are a multiple of 4 over a bf16 / fp8 / int8 cache run
-    on the matrix cores."""
-    mfma = w.kv_dtype != "f32" and (w.h_q // w.h_kv * w.nq) % 4 == 0
+    the query rows per sequence) of at least 3 rows over a bf16 / fp8 / int8 cache run on the
+    matrix cores, unless one flavour is asked for."""
+    if flavour == "auto":
+        mfma = w.kv_dtype != "f32" and w.h_q // w.h_kv * w.nq >= 3
+    else:
+        mfma = flavour == "matrix"
     return "split_kv_attn_mfma_kernel" if mfma else "split_kv_attn_kernel"
 
 
@@ -202,8 +207,9 @@ def main() -> int:
     def step_kv_bytes(i):
         return kv_bytes0 + (w.B * (i // R) * row_bytes if appends else 0)
 
+    flavour = {"auto": da.FLAVOUR_AUTO, "vector": da.FLAVOUR_VECTOR, "matrix": da.FLAVOUR_MATRIX}[args.flavour]
     desc = da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, workloads.TORCH_DTYPE[w.q_dtype],
-                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, args.block_rows, w.nq)
+                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, args.block_rows, w.nq, flavour)
     plan = da.da_plan(desc, max_len)
     q = c["q"].to(dev)
     scales = c["kv_scales"].to(dev) if c["kv_scales"] is not None else None
@@ -301,7 +307,8 @@ def main() -> int:
     algo_bytes = kv_bytes + q_bytes
     achieved = algo_bytes / (split_ms_mean * 1e-3) / 1e9
     value = kv_bytes / (wall_ms * 1e-3) / 1e9
-    traffic = profiled_traffic(args.workload) if not args.const_len and not args.block_rows else None
+    traffic = (profiled_traffic(args.workload)
+               if not args.const_len and not args.block_rows and args.flavour == "auto" else None)
 
     result = {
         "metric": METRIC,
@@ -328,10 +335,10 @@ def main() -> int:
                      else f"uniform[{w.lens[1]},{w.lens[2]}] seed {w.seed}"),
             "sum_lens_first_step": int(lens_first.sum()), "max_len": max_len,
             "appends_per_step": int(appends), "kv_bytes_per_step": round(kv_bytes),
-            "rotations": R, "cache_bytes_per_copy": cache_bytes, **plan,
+            "rotations": R, "cache_bytes_per_copy": cache_bytes, "flavour": args.flavour, **plan,
         },
         "roofline": {
-            "kernel": split_kernel_name(w),
+            "kernel": split_kernel_name(w, args.flavour),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,

@@ -31,10 +31,12 @@ __all__ = [
     "decode_attn_run_static",
     "da_read_device_error", "da_stream_read", "da_status_string", "da_last_error", "library_path",
     "DA_F32", "DA_BF16", "DA_FP8_E4M3FN", "DA_INT8", "DEV_ERR_APPEND_FULL", "DEV_ERR_LEN_RANGE",
+    "FLAVOUR_AUTO", "FLAVOUR_VECTOR", "FLAVOUR_MATRIX",
 ]
 
 DEV_ERR_APPEND_FULL = 1
 DEV_ERR_LEN_RANGE = 2
+FLAVOUR_AUTO, FLAVOUR_VECTOR, FLAVOUR_MATRIX = 0, 1, 2
 
 _TORCH_CODE = {torch.float32: DA_F32, torch.bfloat16: DA_BF16, torch.float8_e4m3fn: DA_FP8_E4M3FN,
                torch.int8: DA_INT8}
@@ -51,7 +53,8 @@ class _CDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("cap", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("block_rows", ctypes.c_int32), ("n_queries", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("block_rows", ctypes.c_int32), ("n_queries", ctypes.c_int32),
+                ("flavour", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -67,11 +70,12 @@ class Desc:
     scale: float                # Step I's factor (1/sqrt(d) in the pages' setting), chosen by the caller
     block_rows: int = 0         # rows per workgroup at max_len; 0: one resident wave, equal shares
     n_queries: int = 1          # query rows per sequence (> 1: multi-query causal decode)
+    flavour: int = 0            # FLAVOUR_AUTO, FLAVOUR_VECTOR or FLAVOUR_MATRIX
 
     def c(self) -> _CDesc:
         return _CDesc(self.batch, self.h_q, self.h_kv, self.d, self.d, self.cap,
                       _TORCH_CODE.get(self.q_dtype, -1), _TORCH_CODE.get(self.kv_dtype, -1),
-                      float(self.scale), self.block_rows, self.n_queries)
+                      float(self.scale), self.block_rows, self.n_queries, self.flavour)
 
     def rows_shape(self) -> tuple:
         """Shape of q and out: [B, h_q, d], or [B, T, h_q, d] with T = n_queries > 1."""

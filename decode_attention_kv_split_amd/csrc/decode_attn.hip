@@ -353,6 +353,9 @@ struct SplitArgs {
     // for the combine: per unit, the workgroups holding its first and its last row
     int2 *unit_wg;
     int dv;  // output row length (the partial rows' stride)
+    // a KV group's g * nq query rows are cut into pt.tiles head tiles of gt rows (the last may
+    // hold fewer); gt is also the per-segment stride of the partial arrays
+    int gt, grp_rows;
 };
 
 // The query rows of a (sequence b, KV head kvh) are its g heads at each of the nq query
@@ -372,12 +375,13 @@ __device__ __forceinline__ QRow query_row(const SplitArgs &a, int b, int kvh, in
     return {((size_t)b * a.pt.nq + t) * a.h_q + kvh * g + fr % g, slen - a.pt.nq + 1 + t};
 }
 
-// Steps I-III over rows [r0, r1) of one (sequence b, KV head kvh) for query heads
-// h0 .. h0+GT-1, by the whole workgroup. The result (max, sum of exponentials, unnormalised
+// Steps I-III over rows [r0, r1) of one (sequence b, KV head kvh) for the hv <= GT query rows
+// h0 .. h0+hv-1 of a head tile, by the whole workgroup (slots hv .. GT-1 compute on a copy of
+// the first row and are never stored). The result (max, sum of exponentials, unnormalised
 // output; base-2 domain, V scale applied) goes to segment slot k of the partial arrays, or
 // normalised straight to out when `direct` (the segment is the whole unit).
 template <int KV, int D, int GT>
-__device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
+__device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kvh, int h0, int hv, int r0, int r1,
                                                size_t k, bool direct, int slen) {
     using T = Kv<KV>;
     using Vec = typename T::Vec;
@@ -410,7 +414,7 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
     int rend[GT];
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
-        const QRow qr = query_row(a, b, kvh, h0, h, slen);
+        const QRow qr = query_row(a, b, kvh, h0, h < hv ? h : 0, slen);
         rend[h] = min(r1, qr.lim);
         const size_t qoff = qr.row * D + sub * EPL;
         if constexpr (KV == DA_F32) {
@@ -552,7 +556,7 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
         }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < GT * D; idx += kBlock) {
+    for (int idx = threadIdx.x; idx < hv * D; idx += kBlock) {
         const int h = idx / D, d = idx % D;
         float M = s_m[0][h];
 #pragma unroll
@@ -567,8 +571,8 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
         if (direct) {
             a.out[query_row(a, b, kvh, h0, h, slen).row * D + d] = O * vscale / Ls;
         } else {
-            a.part_o[(k * GT + h) * D + d] = O * vscale;
-            if (d == 0) { a.part_ml[(k * GT + h) * 2 + 0] = M; a.part_ml[(k * GT + h) * 2 + 1] = Ls; }
+            a.part_o[(k * a.gt + h) * D + d] = O * vscale;
+            if (d == 0) { a.part_ml[(k * a.gt + h) * 2 + 0] = M; a.part_ml[(k * a.gt + h) * 2 + 1] = Ls; }
         }
     }
     __syncthreads();  // the LDS arrays are reused by the next segment
@@ -619,10 +623,11 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(const uint2 &v) {
 //     layout of P^T. Lane l then holds d = 4*(l/16)+i of head l%16: the head's rescale factor
 //     is its own, with no exchange between lanes. P is split into bf16 hi + lo parts (two
 //     MFMAs) so that P.V keeps ~16 bits of P's precision.
-// GT = 4, 8, 16 or 32 heads (HT = 1 or 2 MFMA tiles of 16; heads past GT are zero padding).
-template <int D, int GT>
+// GW = 16 or 32 query-row slots (HT = 1 or 2 MFMA tiles of 16); slots past the tile's hv rows
+// hold zero queries and are never stored.
+template <int D, int GW>
 struct MfmaAttn {
-    static constexpr int HT = (GT + 15) / 16;
+    static constexpr int HT = GW / 16;
     static constexpr int KB = D / 32;  // 32-wide k blocks of Step I
     static constexpr int NB = D / 16;  // 16-wide d blocks of Step III
     typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
@@ -635,7 +640,8 @@ struct MfmaAttn {
     int lim[HT];  // end of the rows this lane's head (ht*16 + l%16) may see (causal bound)
 
     // q^T as the B operand of Step I: lane l holds q[head ht*16 + l%16][kb*32 + 8*(l/16) ..+8].
-    __device__ __forceinline__ void init(const SplitArgs &a, int b, int kvh, int h0, int slen, float score_scale) {
+    __device__ __forceinline__ void init(const SplitArgs &a, int b, int kvh, int h0, int hv, int slen,
+                                         float score_scale) {
         lane = threadIdx.x % kWave;
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
         lr = lane % 16;
@@ -644,12 +650,12 @@ struct MfmaAttn {
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             const int head = ht * 16 + lr;
-            const QRow qr = query_row(a, b, kvh, h0, head < GT ? head : 0, slen);
+            const QRow qr = query_row(a, b, kvh, h0, head < hv ? head : 0, slen);
             lim[ht] = qr.lim;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 uint4 x = {0u, 0u, 0u, 0u};
-                if (head < GT)
+                if (head < hv)
                     x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qr.row * D + kb * 32 +
                                                           8 * lg);
                 qb[ht][kb] = __builtin_bit_cast(bf16x8_t, x);
@@ -734,8 +740,8 @@ struct MfmaAttn {
     // 16-byte pad, so that the 16 heads of a row-exchange land on distinct banks), s_mm / s_ll
     // kWaves * HT*16 each.
     static constexpr int kRowO = D + 4;
-    __device__ __forceinline__ void finish(const SplitArgs &a, int b, int kvh, int h0, int slen, size_t k, bool direct,
-                                           float vscale, float *s_oo, float *s_mm, float *s_ll) {
+    __device__ __forceinline__ void finish(const SplitArgs &a, int b, int kvh, int h0, int hv, int slen, size_t k,
+                                           bool direct, float vscale, float *s_oo, float *s_mm, float *s_ll) {
         constexpr int HP = HT * 16;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {  // the lane groups share each head's max: sums add
@@ -789,7 +795,7 @@ struct MfmaAttn {
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
                 const int head = ht * 16 + lr;
-                if (head >= GT) continue;
+                if (head >= hv) continue;
                 const float M = mres[ht], Ls = lres[ht];
                 const size_t row = query_row(a, b, kvh, h0, head, slen).row;
 #pragma unroll
@@ -798,11 +804,11 @@ struct MfmaAttn {
                     if (direct)
                         *reinterpret_cast<f32x4_t *>(&a.out[row * D + nb * 16 + 4 * lg]) = v / Ls;
                     else
-                        *reinterpret_cast<f32x4_t *>(&a.part_o[(k * GT + head) * D + nb * 16 + 4 * lg]) = v;
+                        *reinterpret_cast<f32x4_t *>(&a.part_o[(k * a.gt + head) * D + nb * 16 + 4 * lg]) = v;
                 }
                 if (!direct && lg == 0) {
-                    a.part_ml[(k * GT + head) * 2 + 0] = M;
-                    a.part_ml[(k * GT + head) * 2 + 1] = Ls;
+                    a.part_ml[(k * a.gt + head) * 2 + 0] = M;
+                    a.part_ml[(k * a.gt + head) * 2 + 1] = Ls;
                 }
             }
         }
@@ -813,12 +819,12 @@ struct MfmaAttn {
 // Matrix-core segment with the tiles staged through registers (bf16 caches): K rows are loaded
 // straight into A-operand order and V rows are stored row-major in the wave's LDS tile for the
 // transpose read.
-template <int KV, int D, int GT, int NBUF>
-__device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
-                                                    size_t k, bool direct, int slen) {
+template <int KV, int D, int GW, int NBUF>
+__device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, int kvh, int h0, int hv, int r0,
+                                                    int r1, size_t k, bool direct, int slen) {
     static_assert(KV == DA_BF16, "the register-ring segment takes bf16 caches");
     using LVec = uint4;  // 8 elements
-    using A = MfmaAttn<D, GT>;
+    using A = MfmaAttn<D, GW>;
     constexpr int KB = A::KB, HP = A::HT * 16;
     constexpr int ESZ = Kv<KV>::kEsz;
     constexpr uint32_t ROWB = D * ESZ;   // bytes per cache row
@@ -853,7 +859,7 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
     auto tile_end = [&](int t) { return t < nfull ? r1 : te; };
     const float vscale = 1.f, sc = a.qk_scale;
     A at;
-    at.init(a, b, kvh, h0, slen, sc);
+    at.init(a, b, kvh, h0, hv, slen, sc);
     const int lane = at.lane, wave = at.wave, lr = at.lr, lg = at.lg;
     const int vrow = lane / VL, vcol = (lane % VL) * 8;
 
@@ -901,7 +907,7 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
             }
         }
     }
-    at.finish(a, b, kvh, h0, slen, k, direct, vscale, s_oo, s_mm, s_ll);
+    at.finish(a, b, kvh, h0, hv, slen, k, direct, vscale, s_oo, s_mm, s_ll);
 }
 
 // int8 codes on the matrix cores go through fp16, whose 11-bit significand holds 1024 + u
@@ -957,11 +963,11 @@ __device__ __forceinline__ uint4 i8x8_to_f16x8(const uint2 &v) {
 // and m / m+2 (the rows one V transpose read gathers) use opposite halves of the banks.
 __device__ __forceinline__ int piece_key(int m) { return (m ^ (m >> 1)) & 1; }
 
-template <int KV, int D, int GT>
-__device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b, int kvh, int h0, int r0, int r1,
-                                                      size_t k, bool direct, int slen) {
+template <int KV, int D, int GW>
+__device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b, int kvh, int h0, int hv, int r0,
+                                                      int r1, size_t k, bool direct, int slen) {
     static_assert(Kv<KV>::kEsz == 1, "the LDS-staged segment takes 8-bit codes");
-    constexpr int HT = (GT + 15) / 16;
+    constexpr int HT = GW / 16;
     constexpr int KB = D / 32, NB = D / 16;
     constexpr int ESZ = Kv<KV>::kEsz;
     constexpr uint32_t ROWB = D * ESZ;         // bytes per cache row
@@ -1011,12 +1017,12 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     float scl = sc;  // this lane's head's score scale
     {
         const int head = ht * 16 + lr;
-        const QRow qr = query_row(a, b, kvh, h0, head < GT ? head : 0, slen);
+        const QRow qr = query_row(a, b, kvh, h0, head < hv ? head : 0, slen);
         rend = min(r1, qr.lim);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             uint4 x = {0u, 0u, 0u, 0u};
-            if (head < GT)
+            if (head < hv)
                 x = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qr.row * D + kb * 32 + 8 * lg);
             qb[kb] = x;
         }
@@ -1257,7 +1263,7 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
         if (wave == 0) merge_o(0, 1);
     }
     const int hd = ht * 16 + lr;
-    if (wave < HT && hd < GT) {  // wave ht now holds head tile ht
+    if (wave < HT && hd < hv) {  // wave ht now holds head tile ht
         const size_t row = query_row(a, b, kvh, h0, hd, slen).row;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -1265,11 +1271,11 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
             if (direct)
                 *reinterpret_cast<f32x4_t *>(&a.out[row * D + nb * 16 + 4 * lg]) = v / lres;
             else
-                *reinterpret_cast<f32x4_t *>(&a.part_o[(k * GT + hd) * D + nb * 16 + 4 * lg]) = v;
+                *reinterpret_cast<f32x4_t *>(&a.part_o[(k * a.gt + hd) * D + nb * 16 + 4 * lg]) = v;
         }
         if (!direct && lg == 0) {
-            a.part_ml[(k * GT + hd) * 2 + 0] = mres - kPShift;
-            a.part_ml[(k * GT + hd) * 2 + 1] = lres;
+            a.part_ml[(k * a.gt + hd) * 2 + 0] = mres - kPShift;
+            a.part_ml[(k * a.gt + hd) * 2 + 1] = lres;
         }
     }
     __syncthreads();  // the LDS arrays are reused by the next segment
@@ -1285,15 +1291,16 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 }
 
 // The segments of one workgroup, in order: rows [r0, r1) of (sequence sb, KV head kvh) for
-// query heads h0 .. h0+gt-1, partial slot k, whole = the segment is the entire unit. Every
-// field is the same in all lanes (scalar registers); copies of a walk advance independently.
+// the hv query rows h0 .. h0+hv-1 of a head tile, partial slot k, whole = the segment is the
+// entire unit. Every field is the same in all lanes (scalar registers); copies of a walk
+// advance independently.
 struct SegWalk {
     const int32_t *lens;
     const int64_t *pre;  // exclusive prefix of rows per sequence (LDS), pre[batch] = T
     int64_t pos, end, w;
-    int b, L, ul, row, upb, g, gt, tiles, append_cap;
+    int b, L, ul, row, upb, g, gt, grp_rows, tiles, append_cap;
     bool has;  // a current segment
-    int sb, kvh, h0, r0, r1;
+    int sb, kvh, h0, hv, r0, r1;
     int slen;      // rows of the segment's sequence (the walk state moves on past them)
     size_t k;
     bool whole;
@@ -1304,11 +1311,12 @@ struct SegWalk {
     int64_t empty_unit;
 
     // Positions the walk on the workgroup's first segment; pre must hold the prefix.
-    __device__ __forceinline__ void start(const SplitArgs &a, int gt_, const int64_t *s_pre) {
+    __device__ __forceinline__ void start(const SplitArgs &a, const int64_t *s_pre) {
         const Partition &pt = a.pt;
         lens = a.lens;
         pre = s_pre;
-        gt = gt_;
+        gt = a.gt;
+        grp_rows = a.grp_rows;
         tiles = pt.tiles;
         upb = pt.h_kv * pt.tiles;
         g = a.h_q / pt.h_kv;
@@ -1342,6 +1350,7 @@ struct SegWalk {
         r1 = (int)min<int64_t>((int64_t)L, row + (end - pos));
         kvh = ul / tiles;
         h0 = kvh * g + (ul % tiles) * gt;
+        hv = min(gt, grp_rows - (ul % tiles) * gt);
         sb = b;
         k = (size_t)w + (size_t)b * upb + ul;
         slen = L;
@@ -1358,7 +1367,7 @@ struct SegWalk {
 };
 
 // Computes the sequence prefix in LDS and returns the walk on the workgroup's first segment.
-__device__ __forceinline__ SegWalk first_segment(const SplitArgs &a, int gt) {
+__device__ __forceinline__ SegWalk first_segment(const SplitArgs &a) {
     __shared__ int64_t s_pre[kMaxBatch + 1];
     __shared__ int64_t s_wave[kWaves];
     if (a.pt.append_cap > 0 && blockIdx.x == 0) {
@@ -1371,12 +1380,12 @@ __device__ __forceinline__ SegWalk first_segment(const SplitArgs &a, int gt) {
     }
     sequence_prefix(a.lens, a.pt, s_pre, s_wave);
     SegWalk wk;
-    wk.start(a, gt, s_pre);
+    wk.start(a, s_pre);
     return wk;
 }
 
-// Workgroup w walks its share of the rows and calls seg(b, kvh, h0, r0, r1, k, whole) once per
-// unit it crosses. The workgroup holding a unit's first row, and the one holding its last,
+// Workgroup w walks its share of the rows and calls seg(b, kvh, h0, hv, r0, r1, k, whole, slen)
+// once per unit it crosses. The workgroup holding a unit's first row, and the one holding its last,
 // record themselves in the unit's entry of unit_wg, so that the combine finds the unit's
 // segments without redoing the partition.
 // With a fused append, a segment that ends at a unit's new last row first stores that row of
@@ -1384,10 +1393,11 @@ __device__ __forceinline__ SegWalk first_segment(const SplitArgs &a, int gt) {
 // stores visible to the loads of every wave of the workgroup. Only workgroups holding that
 // row read it in this pass, and each of them writes it (the same bytes) before reading.
 template <class SegFn>
-__device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn &&seg) {
-    SegWalk wk = first_segment(a, gt);
+__device__ __forceinline__ void walk_segments(const SplitArgs &a, SegFn &&seg) {
+    SegWalk wk = first_segment(a);
     if (wk.empty_unit >= 0) {  // (max, sum, row) = (kNegBig, 0, 0): weighs nothing in the combine
         const size_t kk = (size_t)wk.w + (size_t)wk.empty_unit;
+        const int gt = a.gt;
         for (int i = threadIdx.x; i < gt * 2; i += kBlock) a.part_ml[kk * gt * 2 + i] = (i % 2) ? 0.f : kNegBig;
         for (int i = threadIdx.x; i < gt * a.dv; i += kBlock) a.part_o[kk * gt * a.dv + i] = 0.f;
     }
@@ -1414,41 +1424,41 @@ __device__ __forceinline__ void walk_segments(const SplitArgs &a, int gt, SegFn 
             if (wk.r0 == 0) uw[0] = (int32_t)wk.w;
             if (wk.r1 == wk.slen) uw[1] = (int32_t)wk.w;
         }
-        seg(wk.sb, wk.kvh, wk.h0, wk.r0, wk.r1, wk.k, wk.whole, wk.slen);
+        seg(wk.sb, wk.kvh, wk.h0, wk.hv, wk.r0, wk.r1, wk.k, wk.whole, wk.slen);
     }
 }
 
-// VALU flavour (any group size; GT in {1, 2, 4}). DIRECT (decode_attn_run): a unit covered by
-// a single workgroup is written to out directly and lse_combine_kernel skips it; otherwise
-// every segment leaves a partial result.
+// VALU flavour (GT = 1, 2, 4 or 8 query-row slots, of which a tile's hv are live). DIRECT
+// (decode_attn_run): a unit covered by a single workgroup is written to out directly and
+// lse_combine_kernel skips it; otherwise every segment leaves a partial result.
 template <int KV, int D, int GT, bool DIRECT>
 __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a) {
-    walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole, int slen) {
-        attend_segment<KV, D, GT>(a, b, kvh, h0, r0, r1, k, DIRECT && whole, slen);
+    walk_segments(a, [&](int b, int kvh, int h0, int hv, int r0, int r1, size_t k, bool whole, int slen) {
+        attend_segment<KV, D, GT>(a, b, kvh, h0, hv, r0, r1, k, DIRECT && whole, slen);
     });
 }
 
-// Matrix-core flavour (GT in {4, 8, 16, 32}; bf16, fp8 or int8 caches): bf16 streams through
-// the register ring, 8-bit caches through the LDS stages.
-// Register targets: GT = 32 keeps all of the register file (one wave per SIMD); smaller
-// groups are held to 256 registers so that two waves fit per SIMD.
-template <int GT>
-struct MfmaWaves { static constexpr int kMin = GT == 32 ? 1 : 2; };
+// Matrix-core flavour (GW = 16 or 32 query-row slots; bf16, fp8 or int8 caches): bf16 streams
+// through the register ring, 8-bit caches through the LDS stages.
+// Register targets: GW = 32 keeps all of the register file (one wave per SIMD); 16 slots are
+// held to 256 registers so that two waves fit per SIMD.
+template <int GW>
+struct MfmaWaves { static constexpr int kMin = GW == 32 ? 1 : 2; };
 
 // Register ring depth of the bf16 matrix-core segment (tiles of 16 rows per wave); deeper
 // rings measured no faster and need more registers.
 constexpr int kMfmaRing = 2;
 
-template <int KV, int D, int GT, bool DIRECT>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MfmaWaves<GT>::kMin)))
+template <int KV, int D, int GW, bool DIRECT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MfmaWaves<GW>::kMin)))
 void split_kv_attn_mfma_kernel(const SplitArgs a) {
     if constexpr (Kv<KV>::kEsz == 1) {
-        walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole, int slen) {
-            attend_segment_staged<KV, D, GT>(a, b, kvh, h0, r0, r1, k, DIRECT && whole, slen);
+        walk_segments(a, [&](int b, int kvh, int h0, int hv, int r0, int r1, size_t k, bool whole, int slen) {
+            attend_segment_staged<KV, D, GW>(a, b, kvh, h0, hv, r0, r1, k, DIRECT && whole, slen);
         });
     } else {
-        walk_segments(a, GT, [&](int b, int kvh, int h0, int r0, int r1, size_t k, bool whole, int slen) {
-            attend_segment_mfma<KV, D, GT, kMfmaRing>(a, b, kvh, h0, r0, r1, k, DIRECT && whole, slen);
+        walk_segments(a, [&](int b, int kvh, int h0, int hv, int r0, int r1, size_t k, bool whole, int slen) {
+            attend_segment_mfma<KV, D, GW, kMfmaRing>(a, b, kvh, h0, hv, r0, r1, k, DIRECT && whole, slen);
         });
     }
 }
@@ -1456,7 +1466,10 @@ void split_kv_attn_mfma_kernel(const SplitArgs a) {
 // Merges the segments of every query row by their log-sum-exp weights. Workgroup x takes rows
 // rw * (x % (gt / rw)) .. + rw - 1 of unit u = x / (gt / rw) (a unit's rows share its
 // segments), each row with kCombineBlock / rw threads: segment groups of D / 4 threads, one
-// float4 column each. skip_single: a unit covered by one workgroup was already written.
+// float4 column each. The last head tile of a group may hold fewer than gt rows (grp_rows,
+// the group's g * nq query rows, need not be a multiple of gt): the rows past it are merged
+// from slots nothing wrote and not stored. skip_single: a unit covered by one workgroup was
+// already written.
 // With a fused append (pt.append_cap > 0) the stored lengths come from the split kernel's
 // workspace copy, and the workgroup of head 0 writes each sequence's new length to lens_upd.
 // The unit's segments are those of workgroups unit_wg[u].x .. unit_wg[u].y (slot w + u), which
@@ -1467,7 +1480,8 @@ template <int D>
 __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     const int32_t *__restrict__ lens, int32_t *__restrict__ lens_upd, const int2 *__restrict__ unit_wg,
     const float *__restrict__ part_ml, const float *__restrict__ part_o,
-    float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt, int rw, Partition pt, int skip_single) {
+    float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt, int grp_rows, int rw, Partition pt,
+    int skip_single) {
     constexpr int C4 = D / 4;  // float4 columns of a row
     constexpr int UN = 8;      // segments a group loads before using them
     const int tpr = kCombineBlock / rw, sgr = tpr / C4;  // threads and segment groups per row
@@ -1479,12 +1493,13 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     const int b = (int)(u / upb), ul = (int)(u % upb), kvh = ul / pt.tiles;
     // the row's query position and head: row hh of the tile is row fr of the group's g * nq
     const int fr = (ul % pt.tiles) * gt + hh, tq = fr / g, h = kvh * g + fr % g;
+    const bool live = fr < grp_rows;  // a query row of the group, not past its last tile's rows
     float *dst = out + ((size_t)(b * pt.nq + tq) * h_q + h) * D;
     const int L = attended_len(lens[b], pt.append_cap);
     const int2 ww = unit_wg[u];
     if (lens_upd && ul == 0 && threadIdx.x == 0 && blockIdx.x % per_unit == 0) lens_upd[b] = L;
     if (unit_rows(L, pt.max_len, pt.nq) == 0) {
-        if (sg == 0) reinterpret_cast<float4 *>(dst)[c4] = float4{0.f, 0.f, 0.f, 0.f};
+        if (sg == 0 && live) reinterpret_cast<float4 *>(dst)[c4] = float4{0.f, 0.f, 0.f, 0.f};
         if (threadIdx.x == 0) atomicOr(err, DA_DEV_ERR_LEN_RANGE);
         return;
     }
@@ -1552,7 +1567,7 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
             x.w = fmaf(y.w, f, x.w);
             z = fmaf(s_l[grp + i], f, z);
         }
-        reinterpret_cast<float4 *>(dst)[c4] = float4{x.x / z, x.y / z, x.z / z, x.w / z};
+        if (live) reinterpret_cast<float4 *>(dst)[c4] = float4{x.x / z, x.y / z, x.z / z, x.w / z};
     }
 }
 
@@ -1594,6 +1609,8 @@ int validate(const da_desc *d) {
                     (d->q_dtype == DA_BF16 && d->kv_dtype == DA_FP8_E4M3FN) ||
                     (d->q_dtype == DA_BF16 && d->kv_dtype == DA_INT8);
     if (!ok) return fail(DA_ERR_UNSUPPORTED, "dtype pair (q %d, kv %d) is not built", d->q_dtype, d->kv_dtype);
+    if (d->flavour != DA_FLAVOUR_AUTO && d->flavour != DA_FLAVOUR_VECTOR && d->flavour != DA_FLAVOUR_MATRIX)
+        return fail(DA_ERR_INVALID_ARG, "flavour must be DA_FLAVOUR_AUTO, _VECTOR or _MATRIX (got %d)", d->flavour);
     if (d->n_queries < 0 || d->n_queries > kMaxQueries)
         return fail(DA_ERR_INVALID_ARG, "n_queries must be in [0, %d] (got %d)", kMaxQueries, d->n_queries);
     return DA_OK;
@@ -1607,22 +1624,37 @@ int group_rows(const da_desc *d) { return d->h_q / d->h_kv * n_queries(d); }
 // (N + units) * GT * 2 fp32][segment output rows, (N + units) * GT * d_v fp32], each section
 // starting on a 256-byte boundary (N workgroups, units = batch * h_kv * head tiles).
 struct Plan {
-    int gt, tiles, nwg;
+    int gt;     // query rows per head tile (the last tile of a group may hold fewer)
+    int gw;     // the kernel's query-row slots, >= gt (slots past a tile's rows are padding)
+    int tiles;  // head tiles per KV group
+    int nwg;
     bool mfma;  // matrix-core flavour
     // workspace: header, lengths copy, per-unit first / last workgroup, (max, sum), rows
     size_t lens_off, unit_off, ml_off, o_off, bytes;
 };
 
-// Flavour and query heads per workgroup: groups that are a multiple of 4 query heads over a
-// bf16 / fp8 / int8 cache run on the matrix cores with 4, 8, 16 or 32 heads per workgroup
-// (fewer than 16 heads pad the 16-wide head tile with zero queries: the matrix cores still
-// take the arithmetic off the vector ALUs, measured equal or faster at g = 4); everything
-// else runs on the vector ALUs with 4, 2 or 1.
-bool use_mfma(const da_desc *d) { return d->kv_dtype != DA_F32 && group_rows(d) % 4 == 0; }
-int heads_per_block(const da_desc *d) {
-    const int g = group_rows(d);
-    if (use_mfma(d)) return g % 32 == 0 ? 32 : g % 16 == 0 ? 16 : g % 8 == 0 ? 8 : 4;
-    return g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
+// Flavour and head tiles. A KV group's g * T query rows (T query rows per sequence) read each K
+// and V row once per head tile, so a group is cut into as few tiles as the flavour's widest
+// workgroup allows, of nearly equal size, and each tile is padded up to the kernel's slot
+// count with zero queries instead of being split further:
+//   * bf16 / fp8 / int8 caches with at least 3 query rows per group run on the matrix cores,
+//     tiles of up to 32 rows in 16 or 32 slots (one tile, one read of the group's rows, for
+//     every g * T <= 32);
+//   * otherwise the vector ALUs: fp32 caches with tiles of up to 8 rows, 8-bit and bf16 caches
+//     with 1 or 2 rows (up to 4 when the vector ALUs are asked for), in 1, 2, 4 or 8 slots.
+// desc->flavour asks for one flavour (measurement: both flavours on one shape).
+int plan_tiles(const da_desc *d, Plan *p) {
+    const int rows = group_rows(d);
+    const bool can_mfma = d->kv_dtype != DA_F32;
+    if (d->flavour == DA_FLAVOUR_MATRIX && !can_mfma)
+        return fail(DA_ERR_UNSUPPORTED, "the matrix-core flavour takes bf16, fp8 or int8 caches");
+    p->mfma = d->flavour == DA_FLAVOUR_MATRIX || (d->flavour == DA_FLAVOUR_AUTO && can_mfma && rows >= 3);
+    const int widest = p->mfma ? 32 : d->kv_dtype == DA_F32 ? 8 : 4;
+    p->tiles = (rows + widest - 1) / widest;
+    p->gt = (rows + p->tiles - 1) / p->tiles;
+    if (p->mfma) p->gw = p->gt <= 16 ? 16 : 32;
+    else p->gw = p->gt <= 1 ? 1 : p->gt <= 2 ? 2 : p->gt <= 4 ? 4 : 8;
+    return DA_OK;
 }
 
 // Bytes past a segment's last row that prefetches may address (LDS stages run up to four 16 KiB
@@ -1679,29 +1711,26 @@ int resident_workgroups(const void *kernel) {
 }
 
 template <int KV, int D>
-const void *split_kernel_ptr(int gt, bool mfma) {
+const void *split_kernel_ptr(int gw, bool mfma) {
     if constexpr (KV != DA_F32) {
-        if (mfma) {
-            switch (gt) {
-            case 32: return reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 32, false>);
-            case 16: return reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 16, false>);
-            case 4: return reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 4, false>);
-            default: return reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 8, false>);
-            }
-        }
+        if (mfma)
+            return gw == 32 ? reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 32, false>)
+                            : reinterpret_cast<const void *>(&split_kv_attn_mfma_kernel<KV, D, 16, false>);
+    } else {
+        if (gw == 8) return reinterpret_cast<const void *>(&split_kv_attn_kernel<KV, D, 8, false>);
     }
-    switch (gt) {
+    switch (gw) {
     case 4: return reinterpret_cast<const void *>(&split_kv_attn_kernel<KV, D, 4, false>);
     case 2: return reinterpret_cast<const void *>(&split_kv_attn_kernel<KV, D, 2, false>);
     default: return reinterpret_cast<const void *>(&split_kv_attn_kernel<KV, D, 1, false>);
     }
 }
 
-const void *split_kernel_ptr(int kv, int d, int gt, bool mfma) {
-    if (kv == DA_F32) return d == 64 ? split_kernel_ptr<DA_F32, 64>(gt, false) : split_kernel_ptr<DA_F32, 128>(gt, false);
-    if (kv == DA_BF16) return d == 64 ? split_kernel_ptr<DA_BF16, 64>(gt, mfma) : split_kernel_ptr<DA_BF16, 128>(gt, mfma);
-    if (kv == DA_INT8) return d == 64 ? split_kernel_ptr<DA_INT8, 64>(gt, mfma) : split_kernel_ptr<DA_INT8, 128>(gt, mfma);
-    return d == 64 ? split_kernel_ptr<DA_FP8_E4M3FN, 64>(gt, mfma) : split_kernel_ptr<DA_FP8_E4M3FN, 128>(gt, mfma);
+const void *split_kernel_ptr(int kv, int d, int gw, bool mfma) {
+    if (kv == DA_F32) return d == 64 ? split_kernel_ptr<DA_F32, 64>(gw, false) : split_kernel_ptr<DA_F32, 128>(gw, false);
+    if (kv == DA_BF16) return d == 64 ? split_kernel_ptr<DA_BF16, 64>(gw, mfma) : split_kernel_ptr<DA_BF16, 128>(gw, mfma);
+    if (kv == DA_INT8) return d == 64 ? split_kernel_ptr<DA_INT8, 64>(gw, mfma) : split_kernel_ptr<DA_INT8, 128>(gw, mfma);
+    return d == 64 ? split_kernel_ptr<DA_FP8_E4M3FN, 64>(gw, mfma) : split_kernel_ptr<DA_FP8_E4M3FN, 128>(gw, mfma);
 }
 
 int make_plan(const da_desc *d, int max_len, Plan *p) {
@@ -1716,16 +1745,15 @@ int make_plan(const da_desc *d, int max_len, Plan *p) {
     if ((int64_t)max_len * row_bytes > (int64_t)UINT32_MAX - kSlotSlack)
         return fail(DA_ERR_UNSUPPORTED, "max_len %d rows of %lld bytes exceed the 4 GiB a (sequence, KV head) slot may span",
                     max_len, (long long)row_bytes);
-    p->mfma = use_mfma(d);
-    p->gt = heads_per_block(d);
-    p->tiles = group_rows(d) / p->gt;
+    rc = plan_tiles(d, p);
+    if (rc) return rc;
     const int64_t units = (int64_t)d->batch * d->h_kv * p->tiles;
     const int64_t rows_max = units * max_len;  // rows of all units at max_len
     int64_t nwg;
     if (d->block_rows) {
         nwg = (rows_max + d->block_rows - 1) / d->block_rows;
     } else {
-        nwg = resident_workgroups(split_kernel_ptr(d->kv_dtype, d->d_k, p->gt, p->mfma));
+        nwg = resident_workgroups(split_kernel_ptr(d->kv_dtype, d->d_k, p->gw, p->mfma));
         nwg = std::min<int64_t>(nwg, (rows_max + kMinRowsPerBlock - 1) / kMinRowsPerBlock);
     }
     p->nwg = (int)std::max<int64_t>(1, std::min<int64_t>(nwg, 1 << 20));
@@ -1746,8 +1774,14 @@ int launch_status(const char *what) {
 }
 
 template <int KV, int D, bool DIRECT>
-void launch_split_gt(int gt, dim3 grid, hipStream_t st, const SplitArgs &args) {
-    switch (gt) {
+void launch_split_gt(int gw, dim3 grid, hipStream_t st, const SplitArgs &args) {
+    if constexpr (KV == DA_F32) {
+        if (gw == 8) {
+            hipLaunchKernelGGL((split_kv_attn_kernel<KV, D, 8, DIRECT>), grid, dim3(kBlock), 0, st, args);
+            return;
+        }
+    }
+    switch (gw) {
     case 4: hipLaunchKernelGGL((split_kv_attn_kernel<KV, D, 4, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
     case 2: hipLaunchKernelGGL((split_kv_attn_kernel<KV, D, 2, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
     default: hipLaunchKernelGGL((split_kv_attn_kernel<KV, D, 1, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
@@ -1755,42 +1789,40 @@ void launch_split_gt(int gt, dim3 grid, hipStream_t st, const SplitArgs &args) {
 }
 
 template <int KV, int D, bool DIRECT>
-void launch_split_mfma_gt(int gt, dim3 grid, hipStream_t st, const SplitArgs &args) {
-    switch (gt) {
-    case 32: hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 32, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
-    case 16: hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 16, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
-    case 4: hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 4, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
-    default: hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 8, DIRECT>), grid, dim3(kBlock), 0, st, args); break;
-    }
+void launch_split_mfma_gt(int gw, dim3 grid, hipStream_t st, const SplitArgs &args) {
+    if (gw == 32)
+        hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 32, DIRECT>), grid, dim3(kBlock), 0, st, args);
+    else
+        hipLaunchKernelGGL((split_kv_attn_mfma_kernel<KV, D, 16, DIRECT>), grid, dim3(kBlock), 0, st, args);
 }
 
 template <bool DIRECT>
-void launch_split(int kv, int d, int gt, bool mfma, dim3 grid, hipStream_t st, const SplitArgs &args) {
+void launch_split(int kv, int d, int gw, bool mfma, dim3 grid, hipStream_t st, const SplitArgs &args) {
     if (mfma) {
         if (kv == DA_BF16) {
-            if (d == 64) launch_split_mfma_gt<DA_BF16, 64, DIRECT>(gt, grid, st, args);
-            else launch_split_mfma_gt<DA_BF16, 128, DIRECT>(gt, grid, st, args);
+            if (d == 64) launch_split_mfma_gt<DA_BF16, 64, DIRECT>(gw, grid, st, args);
+            else launch_split_mfma_gt<DA_BF16, 128, DIRECT>(gw, grid, st, args);
         } else if (kv == DA_INT8) {
-            if (d == 64) launch_split_mfma_gt<DA_INT8, 64, DIRECT>(gt, grid, st, args);
-            else launch_split_mfma_gt<DA_INT8, 128, DIRECT>(gt, grid, st, args);
+            if (d == 64) launch_split_mfma_gt<DA_INT8, 64, DIRECT>(gw, grid, st, args);
+            else launch_split_mfma_gt<DA_INT8, 128, DIRECT>(gw, grid, st, args);
         } else {
-            if (d == 64) launch_split_mfma_gt<DA_FP8_E4M3FN, 64, DIRECT>(gt, grid, st, args);
-            else launch_split_mfma_gt<DA_FP8_E4M3FN, 128, DIRECT>(gt, grid, st, args);
+            if (d == 64) launch_split_mfma_gt<DA_FP8_E4M3FN, 64, DIRECT>(gw, grid, st, args);
+            else launch_split_mfma_gt<DA_FP8_E4M3FN, 128, DIRECT>(gw, grid, st, args);
         }
         return;
     }
     if (kv == DA_F32) {
-        if (d == 64) launch_split_gt<DA_F32, 64, DIRECT>(gt, grid, st, args);
-        else launch_split_gt<DA_F32, 128, DIRECT>(gt, grid, st, args);
+        if (d == 64) launch_split_gt<DA_F32, 64, DIRECT>(gw, grid, st, args);
+        else launch_split_gt<DA_F32, 128, DIRECT>(gw, grid, st, args);
     } else if (kv == DA_BF16) {
-        if (d == 64) launch_split_gt<DA_BF16, 64, DIRECT>(gt, grid, st, args);
-        else launch_split_gt<DA_BF16, 128, DIRECT>(gt, grid, st, args);
+        if (d == 64) launch_split_gt<DA_BF16, 64, DIRECT>(gw, grid, st, args);
+        else launch_split_gt<DA_BF16, 128, DIRECT>(gw, grid, st, args);
     } else if (kv == DA_INT8) {
-        if (d == 64) launch_split_gt<DA_INT8, 64, DIRECT>(gt, grid, st, args);
-        else launch_split_gt<DA_INT8, 128, DIRECT>(gt, grid, st, args);
+        if (d == 64) launch_split_gt<DA_INT8, 64, DIRECT>(gw, grid, st, args);
+        else launch_split_gt<DA_INT8, 128, DIRECT>(gw, grid, st, args);
     } else {
-        if (d == 64) launch_split_gt<DA_FP8_E4M3FN, 64, DIRECT>(gt, grid, st, args);
-        else launch_split_gt<DA_FP8_E4M3FN, 128, DIRECT>(gt, grid, st, args);
+        if (d == 64) launch_split_gt<DA_FP8_E4M3FN, 64, DIRECT>(gw, grid, st, args);
+        else launch_split_gt<DA_FP8_E4M3FN, 128, DIRECT>(gw, grid, st, args);
     }
 }
 
@@ -1852,11 +1884,13 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     args.row_bytes = desc->d_k * elem_size(desc->kv_dtype);
     args.unit_wg = reinterpret_cast<int2 *>(ws + p.unit_off);
     args.dv = desc->d_v;
+    args.gt = p.gt;
+    args.grp_rows = group_rows(desc);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (out)
-        launch_split<true>(desc->kv_dtype, desc->d_k, p.gt, p.mfma, dim3(p.nwg), st, args);
+        launch_split<true>(desc->kv_dtype, desc->d_k, p.gw, p.mfma, dim3(p.nwg), st, args);
     else
-        launch_split<false>(desc->kv_dtype, desc->d_k, p.gt, p.mfma, dim3(p.nwg), st, args);
+        launch_split<false>(desc->kv_dtype, desc->d_k, p.gw, p.mfma, dim3(p.nwg), st, args);
     return launch_status("split_kv_attn_kernel");
 }
 
@@ -1900,10 +1934,10 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (desc->d_v == 64)
         hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, ml, po, out, err,
-                           desc->h_q, p.gt, rw, pt, skip_single);
+                           desc->h_q, p.gt, group_rows(desc), rw, pt, skip_single);
     else
         hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, ml, po, out, err,
-                           desc->h_q, p.gt, rw, pt, skip_single);
+                           desc->h_q, p.gt, group_rows(desc), rw, pt, skip_single);
     return launch_status("lse_combine_kernel");
 }
 

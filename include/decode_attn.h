@@ -50,7 +50,8 @@ extern "C" {
 #define DA_OK 0
 #define DA_ERR_INVALID_ARG (-1) /* null or misaligned pointer, bad shape, h_q % h_kv != 0,
                                    max_len outside [1, cap], non-finite scale */
-#define DA_ERR_UNSUPPORTED (-2) /* head size or dtype combination not built */
+#define DA_ERR_UNSUPPORTED (-2) /* head size or dtype combination not built, a slot of 4 GiB
+                                   or more, the matrix-core flavour asked for an fp32 cache */
 #define DA_ERR_WORKSPACE (-3)   /* workspace smaller than da_workspace_size() */
 #define DA_ERR_LAUNCH (-4)      /* the HIP runtime refused a launch (see da_last_error) */
 
@@ -60,6 +61,10 @@ extern "C" {
 #define DA_DEV_ERR_LEN_RANGE 2   /* decode: lens[b] outside [max(1, n_queries), max_len]; out[b] zeroed */
 
 typedef enum { DA_F32 = 0, DA_BF16 = 1, DA_FP8_E4M3FN = 2, DA_INT8 = 3 } da_dtype;
+
+/* Kernel flavour (da_desc.flavour): the library's choice, or one flavour asked for (to measure
+ * both on one shape). The matrix-core flavour takes bf16, fp8 and int8 caches only. */
+typedef enum { DA_FLAVOUR_AUTO = 0, DA_FLAVOUR_VECTOR = 1, DA_FLAVOUR_MATRIX = 2 } da_flavour;
 
 /*
  * Problem descriptor. Supported: d_k == d_v in {64, 128}; (q_dtype, kv_dtype) in
@@ -78,10 +83,19 @@ typedef enum { DA_F32 = 0, DA_BF16 = 1, DA_FP8_E4M3FN = 2, DA_INT8 = 3 } da_dtyp
  * Attention", introduction (the decode form is the forward form with the query-row index
  * fixed to the current step; here it spans the last T steps) and page "Phase 3, Section 6:
  * StoryLM-0 head-parallel attention", §3 (softmax over the key axis of the scaled scores
- * plus a mask, T query rows). The g * T query rows of a KV group share each K and V row
- * read: it is read once per head tile of up to 32 of them, i.e. once when g * T <= 32.
- * lens[b] must be at least T (else the device error DA_DEV_ERR_LEN_RANGE). The fused-append
- * entry points take T = 1 only.
+ * plus a mask, T query rows). lens[b] must be at least T (else the device error
+ * DA_DEV_ERR_LEN_RANGE). The fused-append entry points take T = 1 only.
+ *
+ * Reads per KV row (same page, §6: the g query heads of a group select one copy of its rows):
+ * the g * T query rows of a KV group share each K and V row read, once per head tile. With a
+ * bf16, fp8 or int8 cache and g * T >= 3 (matrix cores) a tile holds up to 32 query rows, so
+ * every group with g * T <= 32 reads its rows once (ceil(g * T / 32) times beyond); g * T <= 2
+ * reads once on the vector ALUs; an fp32 cache reads once for g * T <= 8 (ceil(g * T / 8)
+ * times beyond). da_plan's heads_per_block is the tile's query-row count.
+ *
+ * flavour (da_flavour): DA_FLAVOUR_AUTO (0) for the rule above; DA_FLAVOUR_VECTOR or
+ * DA_FLAVOUR_MATRIX to run one flavour regardless (the vector ALUs then cut 8-bit and bf16
+ * groups into tiles of up to 4 rows). Results agree within the tolerances either way.
  */
 typedef struct {
     int32_t batch;
@@ -95,6 +109,7 @@ typedef struct {
     float scale;
     int32_t block_rows;
     int32_t n_queries; /* query rows per sequence; 0 or 1 = single-query decode */
+    int32_t flavour;   /* da_flavour; 0 = the library's choice */
 } da_desc;
 
 /*

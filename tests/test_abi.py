@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def _desc(**kw):
     base = dict(batch=2, h_q=8, h_kv=2, d_k=128, d_v=128, cap=1024, q_dtype=1, kv_dtype=1,
-                scale=0.088, block_rows=0, n_queries=0)
+                scale=0.088, block_rows=0, n_queries=0, flavour=0)
     base.update(kw)
     return da._CDesc(**base)
 
@@ -96,16 +96,38 @@ def test_workspace_size_and_plan(lib):
     assert n >= 256 + segs * gt * 2 * 4 + segs * gt * 128 * 4
     d2 = _desc(batch=16, h_q=32, h_kv=8, cap=32768, block_rows=512)
     assert _plan(lib, d2, 1000) == (512, -(-128 * 1000 // 512), 4)
-    # query heads per workgroup: groups that are a multiple of 4 (bf16 / fp8) go to the matrix
-    # cores with 32, 16, 8 or 4 heads; the rest to the vector ALUs with the largest of 4, 2, 1
-    # dividing g
-    assert _plan(lib, _desc(h_q=6, h_kv=2), 100)[2] == 1
-    assert _plan(lib, _desc(h_q=12, h_kv=2), 100)[2] == 2
+    # query rows per head tile: a group's g query rows in as few tiles as the flavour allows
+    # (32 rows on the matrix cores, 8 for fp32 on the vector ALUs), of nearly equal size
+    assert _plan(lib, _desc(h_q=6, h_kv=2), 100)[2] == 3
+    assert _plan(lib, _desc(h_q=12, h_kv=2), 100)[2] == 6
     assert _plan(lib, _desc(h_q=8, h_kv=2), 100)[2] == 4
-    assert _plan(lib, _desc(h_q=64, h_kv=2), 100)[2] == 32
-    assert _plan(lib, _desc(h_q=48, h_kv=2), 100)[2] == 8
-    assert _plan(lib, _desc(h_q=32, h_kv=2), 100)[2] == 16
-    assert _plan(lib, _desc(h_q=64, h_kv=2, q_dtype=0, kv_dtype=0), 100)[2] == 4
+    assert _plan(lib, _desc(h_q=64, h_kv=1), 100)[2] == 32
+    assert _plan(lib, _desc(h_q=80, h_kv=2), 100)[2] == 20   # 40 rows: two tiles of 20
+    assert _plan(lib, _desc(h_q=74, h_kv=2), 100)[2] == 19   # 37 rows: tiles of 19 and 18
+    assert _plan(lib, _desc(h_q=64, h_kv=2, q_dtype=0, kv_dtype=0), 100)[2] == 8
+    assert _plan(lib, _desc(h_q=18, h_kv=2, q_dtype=0, kv_dtype=0), 100)[2] == 5  # 9 rows: 5 + 4
+
+
+@pytest.mark.parametrize("g,nq", [(3, 1), (5, 1), (6, 1), (7, 1), (12, 1), (24, 1), (28, 1), (32, 1),
+                                  (5, 3), (5, 4), (6, 4), (7, 4), (3, 8), (4, 5), (1, 7)])
+def test_one_head_tile_per_group_up_to_32_query_rows(lib, g, nq):
+    """Every KV group with g * T <= 32 query rows over a bf16, fp8 or int8 cache is one head
+    tile (its K and V rows are read once), whatever g * T's divisors."""
+    for kv in (1, 2, 3):
+        d = _desc(batch=3, h_q=2 * g, h_kv=2, kv_dtype=kv, n_queries=nq)
+        rows_per_block, nblocks, gt = _plan(lib, d, 1000)
+        assert gt == g * nq, (kv, g, nq, gt)
+        # the partition spans the rows of one tile per (sequence, KV head)
+        assert rows_per_block * nblocks >= 3 * 2 * 1000 and (rows_per_block - 1) * nblocks < 3 * 2 * 1000 + nblocks
+
+
+def test_flavour_override(lib):
+    """DA_FLAVOUR_VECTOR / _MATRIX pick one flavour; the matrix cores refuse an fp32 cache."""
+    assert _plan(lib, _desc(h_q=32, h_kv=8, flavour=1), 100)[2] == 4   # vector ALUs: tiles of <= 4
+    assert _plan(lib, _desc(h_q=48, h_kv=2, flavour=1), 100)[2] == 4   # 24 rows: six tiles of 4
+    assert _plan(lib, _desc(h_q=8, h_kv=8, flavour=2), 100)[2] == 1    # one row padded to 16 slots
+    assert _ws_size(lib, _desc(q_dtype=0, kv_dtype=0, flavour=2), 100)[0] == -2
+    assert _ws_size(lib, _desc(flavour=3), 100)[0] == -1
 
 
 def test_null_and_misaligned_pointers_fail_before_launch(lib):
@@ -183,12 +205,14 @@ def test_stream_read_rejects_bad_sizes(lib):
 
 def test_multi_query_plan_and_limits(lib):
     """T query rows per sequence multiply the rows of each KV group: g * T picks the flavour and
-    the head tile (g = 2, T = 2 -> 4 rows on the matrix cores; g = 1, T = 3 -> vector ALUs), the
-    workspace grows with the units, and the fused append refuses T > 1."""
+    the head tile (g = 2, T = 2 -> 4 rows and g = 1, T = 3 -> 3 rows on the matrix cores; g = 1,
+    T = 2 -> vector ALUs), the workspace grows with the units, and the fused append refuses
+    T > 1."""
     assert _plan(lib, _desc(h_q=4, h_kv=2, n_queries=2), 100)[2] == 4
-    assert _plan(lib, _desc(h_q=2, h_kv=2, n_queries=3), 100)[2] == 1
+    assert _plan(lib, _desc(h_q=2, h_kv=2, n_queries=3), 100)[2] == 3
+    assert _plan(lib, _desc(h_q=2, h_kv=2, n_queries=2), 100)[2] == 2
     assert _plan(lib, _desc(h_q=32, h_kv=8, n_queries=4), 100)[2] == 16
-    assert _plan(lib, _desc(h_q=32, h_kv=1, n_queries=8), 100)[2] == 32
+    assert _plan(lib, _desc(h_q=32, h_kv=1, n_queries=8), 100)[2] == 32  # 256 rows: 8 tiles of 32
     one = _ws_size(lib, _desc(h_q=32, h_kv=8), 1000)[1]
     four = _ws_size(lib, _desc(h_q=32, h_kv=8, n_queries=4), 1000)[1]
     assert four > one > 0

@@ -2,8 +2,9 @@
 
 Small cases span several row tiles, several splits and ragged tails; the
 full-size workloads run in the launch configuration the benchmark times and
-are compared on sampled sequences. Caches are NaN-poisoned past each
-sequence's length, so a read out of range shows up as a non-finite output.
+are compared over every sequence, the benchmarked fused decode step included.
+Caches are NaN-poisoned past each sequence's length, so a read out of range
+shows up as a non-finite output.
 """
 import numpy as np
 import pytest
@@ -78,6 +79,20 @@ CASES = [
     ("bf16", 128, 32, 2, ("uniform", 1, 40), 0),
     ("fp8", 128, 32, 2, ("uniform", 1, 40), 0),
     ("bf16", 64, 64, 4, ("uniform", 1, 100), 0),
+    # groups whose g has no factor of 4 or of 8: one head tile per group, padded to 16 or 32
+    # query-row slots (each K and V row read once per group)
+    ("bf16", 128, 10, 2, ("uniform", 1, 1500), 256),
+    ("bf16", 128, 12, 1, ("uniform", 1, 1500), 0),
+    ("bf16", 64, 21, 3, ("uniform", 1, 1500), 100),
+    ("bf16", 128, 48, 2, ("uniform", 1, 1500), 0),
+    ("fp8", 128, 9, 3, ("uniform", 1, 1500), 0),
+    ("fp8", 64, 40, 2, ("uniform", 1, 1500), 256),
+    ("int8", 128, 15, 3, ("uniform", 1, 1500), 0),
+    ("int8", 64, 28, 1, ("uniform", 1, 1500), 100),
+    ("fp8", 128, 80, 2, ("uniform", 1, 1500), 0),       # 40 rows: two tiles of 20
+    ("bf16", 128, 74, 2, ("uniform", 1, 1500), 256),    # 37 rows: tiles of 19 and 18
+    ("f32", 128, 12, 2, ("uniform", 1, 1500), 0),       # fp32, 6 rows in 8 vector-ALU slots
+    ("f32", 64, 18, 1, ("uniform", 1, 1500), 200),      # fp32, 18 rows: tiles of 6
 ]
 
 
@@ -172,6 +187,38 @@ def test_parity_combine_with_several_rows_per_workgroup(kv, d, h_q, h_kv):
     check_close(out, oracle_out(w, c), kv)
 
 
+FLAVOUR_CASES = [
+    # kv, d, h_q, h_kv: each run on the vector ALUs and on the matrix cores
+    ("bf16", 128, 32, 8),   # g = 4, the GQA workload's group
+    ("bf16", 64, 16, 2),    # g = 8: vector ALUs in two tiles of 4
+    ("bf16", 128, 4, 4),    # g = 1: one query row in 16 matrix-core slots
+    ("fp8", 128, 16, 2),
+    ("int8", 64, 6, 3),     # g = 2
+    ("fp8", 64, 12, 1),     # g = 12: three vector-ALU tiles
+]
+
+
+@pytest.mark.parametrize("kv,d,h_q,h_kv", FLAVOUR_CASES)
+def test_both_flavours_match_the_oracle(kv, d, h_q, h_kv):
+    """DA_FLAVOUR_VECTOR and DA_FLAVOUR_MATRIX on the same inputs: both within tolerance of
+    the oracle, whatever the library would choose."""
+    w = W(kv_dtype=kv, d=d, h_q=h_q, h_kv=h_kv, B=4, cap=2000, lens=("uniform", 1, 2000),
+          seed=300 + FLAVOUR_CASES.index((kv, d, h_q, h_kv)))
+    c = workloads.generate(w)
+    ref = oracle_out(w, c)
+    g = to_gpu(c)
+    ml = int(c["lens_final"].max())
+    for flavour in (da.FLAVOUR_VECTOR, da.FLAVOUR_MATRIX):
+        desc = da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, workloads.TORCH_DTYPE[w.q_dtype],
+                       workloads.TORCH_DTYPE[kv], w.scale, 0, 1, flavour)
+        log(f"case flavour {flavour} {kv} d={d} h_q={h_q} h_kv={h_kv} plan {da.da_plan(desc, ml)}")
+        ws = da.Workspace(desc, ml)
+        out = torch.empty(w.B, w.h_q, w.d, device="cuda")
+        da.decode_attn_run(desc, g["q"], g["k_cache"], g["v_cache"], g["lens_final"], ml, g["kv_scales"], out, ws)
+        assert da.da_read_device_error(ws) == 0
+        check_close(out, ref, kv, f"flavour {flavour}")
+
+
 def test_invalid_lengths_between_valid_ones():
     """Sequences with an out-of-range length hold no rows of the partition: their output
     is zeroed and flagged, and the sequences around them are unaffected."""
@@ -201,20 +248,26 @@ def test_single_row_returns_that_value_row_exactly():
     assert torch.equal(out.cpu(), expect)
 
 
-def test_fp8_decoding_of_every_finite_code():
-    """The in-register e4m3fn decode: with one row per sequence out = decode(code) * v_scale,
-    checked for all 254 finite codes against the oracle's decoder (v_scale = 1, exact)."""
-    codes = [c for c in range(256) if c not in (0x7F, 0xFF)]
-    codes += [0] * (256 - len(codes))
-    w = W(B=2, h_q=1, h_kv=1, d=128, cap=64, kv_dtype="fp8", lens=("const", 1))
-    c = workloads.generate(w)
-    v = torch.tensor(codes, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).reshape(2, 128)
-    c["v_cache"][:, 0, 0] = v
-    c["kv_scales"][:] = 1.0
-    out, _, _, err = run_gpu(w, c, max_len=1)
-    assert err == 0
-    expect = np.array([oracle.e4m3fn_to_f64(x) for x in codes]).reshape(2, 1, 128)
-    assert np.array_equal(out.cpu().double().numpy(), expect)
+@pytest.mark.parametrize("h_q", [1, 4])
+def test_fp8_decoding_of_every_finite_code(h_q):
+    """The e4m3fn decode of V: with one row per sequence out = decode(code) * v_scale, checked
+    for all 254 finite codes against the oracle's decoder (v_scale = 1, exact), on both
+    flavours (one query head: the vector ALUs' bit decoder; four: the matrix cores' paired
+    conversion, after the LDS stage), and with every code at each of the four byte positions of
+    a 32-bit word (four rotations of the code order)."""
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    for rot in range(4):
+        codes = [0] * rot + finite
+        codes += [0] * (512 - len(codes))
+        w = W(B=4, h_q=h_q, h_kv=1, d=128, cap=64, kv_dtype="fp8", lens=("const", 1))
+        c = workloads.generate(w)
+        v = torch.tensor(codes, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).reshape(4, 128)
+        c["v_cache"][:, 0, 0] = v
+        c["kv_scales"][:] = 1.0
+        out, _, _, err = run_gpu(w, c, max_len=1)
+        assert err == 0
+        expect = np.array([oracle.e4m3fn_to_f64(x) for x in codes]).reshape(4, 1, 128)
+        assert np.array_equal(out.cpu().double().numpy(), np.repeat(expect, h_q, axis=1)), f"rotation {rot}"
 
 
 def test_int8_decoding_of_every_code():
@@ -356,9 +409,9 @@ FULL = ["mha_bf16", "gqa8_bf16", "mqa_bf16", "gqa8_fp8", "gqa8_int8"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_workload_sampled(name):
-    """The workloads at their real sizes in the default launch plan; the oracle checks
-    every head of three sampled sequences (first, last and the longest)."""
+def test_full_size_workload(name):
+    """The workloads at their real sizes in the default launch plan; the oracle checks every
+    head of every sequence."""
     w = workloads.WORKLOADS[name]
     log(f"case full {name}: generating")
     c = workloads.generate(w)
@@ -367,10 +420,42 @@ def test_full_size_workload_sampled(name):
     assert err == 0
     out = out.cpu()
     assert torch.isfinite(out).all()
-    samples = sorted({0, w.B - 1, int(c["lens_final"].argmax())})
-    for b in samples:
-        log(f"case full {name}: oracle b={b} L={int(c['lens_final'][b])}")
-        check_close(out[b:b + 1], oracle_out(w, c, batch_index=b), w.kv_dtype, f"{name} b={b}")
+    log(f"case full {name}: oracle over all {w.B} sequences")
+    check_close(out, oracle_out(w, c), w.kv_dtype, name)
+
+
+@pytest.mark.parametrize("form", ["one call", "two stages"])
+def test_full_size_fused_decode_step(form):
+    """The step the benchmark times, at full size: decode_attn_append_run on the GQA 32q/8kv
+    bf16 workload (16 ragged sequences up to 32768 rows, one appended row each), in the
+    one-call form and in the two-stage form the benchmark brackets with events. Every head of
+    every sequence against the oracle over the oracle's own appended cache; the whole cache
+    buffers bit-exact against that cache; every length one longer."""
+    w = workloads.WORKLOADS["gqa8_bf16"]
+    log(f"case full fused step ({form}): generating")
+    c = workloads.generate(w)
+    desc = desc_of(w)
+    g = to_gpu(c)
+    lens = g["lens_init"].clone()
+    ml = int(c["lens_final"].max())
+    ws = da.Workspace(desc, ml)
+    out = torch.empty(w.B, w.h_q, w.d, device="cuda")
+    kn, vn = g["k_new"][0].contiguous(), g["v_new"][0].contiguous()
+    log(f"case full fused step ({form}): running GPU, plan {da.da_plan(desc, ml)}")
+    if form == "one call":
+        da.decode_attn_append_run(desc, g["q"], g["k_cache"], g["v_cache"], lens, kn, vn, ml, None, out, ws)
+    else:
+        da.decode_attn_append_partial(desc, g["q"], g["k_cache"], g["v_cache"], lens, kn, vn, ml, None, ws)
+        da.decode_attn_append_combine(desc, lens, ml, out, ws)
+    assert da.da_read_device_error(ws) == 0
+    assert torch.equal(lens.cpu(), c["lens_final"])
+    log(f"case full fused step ({form}): oracle append and attention")
+    kc, vc = oracle._np(c["k_cache"]).copy(), oracle._np(c["v_cache"]).copy()
+    ln = c["lens_init"].numpy().copy()
+    oracle.kv_append(kc, vc, ln, oracle._np(c["k_new"][0]).copy(), oracle._np(c["v_new"][0]).copy())
+    assert np.array_equal(oracle._np(g["k_cache"].cpu()), kc)
+    assert np.array_equal(oracle._np(g["v_cache"].cpu()), vc)
+    check_close(out, oracle.decode_f64(c["q"], kc, vc, ln, w.scale), "bf16", f"fused step, {form}")
 
 
 def test_stream_read_reads_every_byte_once():
