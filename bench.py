@@ -19,15 +19,19 @@ Prints ONE JSON line:
                 reaches ms_per_step)
   step_us_p10_p50_p90 = each step's time on the GPU's clock (from the event before its split
                 kernel to the next step's) at the 10th, 50th and 90th percentile
-  roofline    = the split-KV attention kernel, timed with HIP events around it on the
-                stream it runs on (the timed steps call the step in its two-stage form,
-                the partial then the combine entry point, with the events around the
-                first):
+  roofline    = the step's dominant kernel, timed with HIP events around it on the stream
+                it runs on: on the split path the split-KV attention kernel (the timed steps
+                call the step in its two-stage form, the partial then the combine entry
+                point, with the events around the first); on the single pass (small
+                problems, one kernel per step) the whole one-call step:
                 algorithmic bytes per launch (the KV rows of every sequence plus q) / mean
                 launch duration, against the 8 TB/s HBM3E peak; `traffic` is
                 the HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, read
                 from the profiles/ summary when it was taken on the current kernel source
   cpu_baseline= the fp64 CPU oracle on the same inputs, full step, host cores
+  one_call_form = split path only: the same number of steps again in the one-call form the
+                product calls (decode_attn_append_run / decode_attn_run, no events inside a
+                step), bracketed by two events
   stream_ceiling = the read rate of a plain streaming read (da_stream_read over 2 GiB), and
                 value and roofline.achieved as percentages of it; measured before the warm-up
                 steps, after some 60 ms of untimed streaming that brings the part to steady
@@ -62,6 +66,8 @@ def parse_args():
     p.add_argument("--block-rows", type=int, default=0, help="rows per split (0 = library choice)")
     p.add_argument("--flavour", choices=["auto", "vector", "matrix"], default="auto",
                    help="split-kernel flavour (auto = the library's choice)")
+    p.add_argument("--path", choices=["auto", "split", "single"], default="auto",
+                   help="launch path of the one-call step (auto = the library's choice)")
     p.add_argument("--rotations", type=int, default=0, help="cache copies to rotate (0 = auto)")
     p.add_argument("--graph", action="store_true",
                    help="also time the step replayed from a captured HIP graph (one step per cache copy)")
@@ -136,9 +142,10 @@ def stream_ceiling(dev, reps: int = 10, warm_ms: float = 60.0) -> dict:
             "kernel": "stream_read_kernel (16-byte non-temporal buffer loads, 512 workgroups)"}
 
 
-def uses_per_copy(r: int, warmup: int, steps: int, graph: bool) -> int:
-    """Steps (warm-up, timed, graph replays) that use each of r rotating cache copies."""
-    return -(-(warmup + steps) // r) + (max(1, steps // r) if graph else 0)
+def uses_per_copy(r: int, warmup: int, steps: int, graph: bool, one_call: bool = True) -> int:
+    """Steps (warm-up, timed, the one-call loop, graph replays) that use each of r rotating
+    cache copies."""
+    return -(-(warmup + steps + (steps if one_call else 0)) // r) + (max(1, steps // r) if graph else 0)
 
 
 def cache_rotations(kv_bytes: int, warmup: int, steps: int, graph: bool, room=None) -> int:
@@ -208,9 +215,12 @@ def main() -> int:
         return kv_bytes0 + (w.B * (i // R) * row_bytes if appends else 0)
 
     flavour = {"auto": da.FLAVOUR_AUTO, "vector": da.FLAVOUR_VECTOR, "matrix": da.FLAVOUR_MATRIX}[args.flavour]
+    path = {"auto": da.PATH_AUTO, "split": da.PATH_SPLIT, "single": da.PATH_SINGLE}[args.path]
     desc = da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, workloads.TORCH_DTYPE[w.q_dtype],
-                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, args.block_rows, w.nq, flavour)
+                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, args.block_rows, w.nq, flavour, path)
     plan = da.da_plan(desc, max_len)
+    # the single pass is one kernel per step; the split path two (split kernel, combine)
+    single = plan["path"] == da.PATH_SINGLE
     q = c["q"].to(dev)
     scales = c["kv_scales"].to(dev) if c["kv_scales"] is not None else None
     lens_init = c["lens_init"].to(dev) if appends else lens_final.to(dev)
@@ -228,12 +238,18 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     def step(i, ev=None):
+        """One step; with events ev = (a, b), a and b bracket its dominant kernel: the whole
+        one-call step on the single pass, the split kernel of the two-stage form otherwise."""
         kc, vc, lens = slots[i % R]
-        if ev is None:
+        if ev is None or single:
+            if ev is not None:
+                ev[0].record(stream)
             if appends:
                 da.decode_attn_append_run(desc, q, kc, vc, lens, k_new, v_new, max_len, scales, out, ws)
             else:
                 da.decode_attn_run(desc, q, kc, vc, lens, max_len, scales, out, ws)
+            if ev is not None:
+                ev[1].record(stream)
             return
         ev[0].record(stream)
         if appends:
@@ -268,11 +284,29 @@ def main() -> int:
     t1 = time.perf_counter()
     assert da.da_read_device_error(ws) == 0, "device error flagged during the timed steps"
 
+    one_call = None
+    if not single:
+        # the same number of steps in the one-call form the product calls (no events inside a
+        # step), to show what the two-stage timed form and its events cost
+        o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        base = args.warmup + args.steps
+        torch.cuda.synchronize()
+        o0.record(stream)
+        for i in range(args.steps):
+            step(base + i)
+        o1.record(stream)
+        torch.cuda.synchronize()
+        assert da.da_read_device_error(ws) == 0, "device error flagged during the one-call steps"
+        o_ms = o0.elapsed_time(o1) / args.steps
+        o_bytes = sum(step_kv_bytes(base + i) for i in range(args.steps)) / args.steps
+        one_call = {"us_per_step": round(o_ms * 1e3, 2), "GBs": round(o_bytes / (o_ms * 1e-3) / 1e9, 2),
+                    "steps": args.steps}
+
     graph = None
     if args.graph:
         # one step per cache copy captured on a side stream, replayed graph_reps times; the
         # lengths live on the device, so every replay appends and attends one row further
-        base = args.warmup + args.steps
+        base = args.warmup + 2 * args.steps
         base += (-base) % R  # the next step of copy 0
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream(device=dev)
@@ -308,7 +342,8 @@ def main() -> int:
     achieved = algo_bytes / (split_ms_mean * 1e-3) / 1e9
     value = kv_bytes / (wall_ms * 1e-3) / 1e9
     traffic = (profiled_traffic(args.workload)
-               if not args.const_len and not args.block_rows and args.flavour == "auto" else None)
+               if not args.const_len and not args.block_rows and args.flavour == "auto" and args.path == "auto"
+               else None)
 
     result = {
         "metric": METRIC,
@@ -335,10 +370,11 @@ def main() -> int:
                      else f"uniform[{w.lens[1]},{w.lens[2]}] seed {w.seed}"),
             "sum_lens_first_step": int(lens_first.sum()), "max_len": max_len,
             "appends_per_step": int(appends), "kv_bytes_per_step": round(kv_bytes),
-            "rotations": R, "cache_bytes_per_copy": cache_bytes, "flavour": args.flavour, **plan,
+            "rotations": R, "cache_bytes_per_copy": cache_bytes, "flavour": args.flavour,
+            **{k: v for k, v in plan.items() if k != "path"}, "path": "single" if single else "split",
         },
         "roofline": {
-            "kernel": split_kernel_name(w, args.flavour),
+            "kernel": "decode_step_single_kernel" if single else split_kernel_name(w, args.flavour),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
@@ -354,6 +390,8 @@ def main() -> int:
     }
     if graph is not None:
         result["graph_replay"] = graph
+    if one_call is not None:
+        result["one_call_form"] = one_call
     if ceil is not None:
         ceil["value_pct_of_ceiling"] = round(100 * value / ceil["GBs"], 2)
         ceil["achieved_pct_of_ceiling"] = round(100 * achieved / ceil["GBs"], 2)

@@ -31,12 +31,13 @@ __all__ = [
     "decode_attn_run_static",
     "da_read_device_error", "da_stream_read", "da_status_string", "da_last_error", "library_path",
     "DA_F32", "DA_BF16", "DA_FP8_E4M3FN", "DA_INT8", "DEV_ERR_APPEND_FULL", "DEV_ERR_LEN_RANGE",
-    "FLAVOUR_AUTO", "FLAVOUR_VECTOR", "FLAVOUR_MATRIX",
+    "FLAVOUR_AUTO", "FLAVOUR_VECTOR", "FLAVOUR_MATRIX", "PATH_AUTO", "PATH_SPLIT", "PATH_SINGLE",
 ]
 
 DEV_ERR_APPEND_FULL = 1
 DEV_ERR_LEN_RANGE = 2
 FLAVOUR_AUTO, FLAVOUR_VECTOR, FLAVOUR_MATRIX = 0, 1, 2
+PATH_AUTO, PATH_SPLIT, PATH_SINGLE = 0, 1, 2
 
 _TORCH_CODE = {torch.float32: DA_F32, torch.bfloat16: DA_BF16, torch.float8_e4m3fn: DA_FP8_E4M3FN,
                torch.int8: DA_INT8}
@@ -54,7 +55,7 @@ class _CDesc(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("cap", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("block_rows", ctypes.c_int32), ("n_queries", ctypes.c_int32),
-                ("flavour", ctypes.c_int32)]
+                ("flavour", ctypes.c_int32), ("path", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -71,11 +72,12 @@ class Desc:
     block_rows: int = 0         # rows per workgroup at max_len; 0: one resident wave, equal shares
     n_queries: int = 1          # query rows per sequence (> 1: multi-query causal decode)
     flavour: int = 0            # FLAVOUR_AUTO, FLAVOUR_VECTOR or FLAVOUR_MATRIX
+    path: int = 0               # PATH_AUTO, PATH_SPLIT or PATH_SINGLE (one-call entry points)
 
     def c(self) -> _CDesc:
         return _CDesc(self.batch, self.h_q, self.h_kv, self.d, self.d, self.cap,
                       _TORCH_CODE.get(self.q_dtype, -1), _TORCH_CODE.get(self.kv_dtype, -1),
-                      float(self.scale), self.block_rows, self.n_queries, self.flavour)
+                      float(self.scale), self.block_rows, self.n_queries, self.flavour, self.path)
 
     def rows_shape(self) -> tuple:
         """Shape of q and out: [B, h_q, d], or [B, T, h_q, d] with T = n_queries > 1."""
@@ -125,11 +127,11 @@ def da_workspace_size(desc: Desc, max_len: int) -> int:
 
 
 def da_plan(desc: Desc, max_len: int) -> dict:
-    c, s, g = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    c, s, g, pa = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     cd = desc.c()
-    _check(lib().da_plan(ctypes.byref(cd), int(max_len), ctypes.byref(c), ctypes.byref(s), ctypes.byref(g)),
-           "da_plan")
-    return {"rows_per_block": c.value, "n_blocks": s.value, "heads_per_block": g.value}
+    _check(lib().da_plan(ctypes.byref(cd), int(max_len), ctypes.byref(c), ctypes.byref(s), ctypes.byref(g),
+                         ctypes.byref(pa)), "da_plan")
+    return {"rows_per_block": c.value, "n_blocks": s.value, "heads_per_block": g.value, "path": pa.value}
 
 
 def da_workspace_init(ws: torch.Tensor) -> None:

@@ -20,7 +20,7 @@ _lib = None
 P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 SIGNATURES = {
     "da_workspace_size": (ctypes.c_int, [P, I32, P]),
-    "da_plan": (ctypes.c_int, [P, I32, P, P, P]),
+    "da_plan": (ctypes.c_int, [P, I32, P, P, P, P]),
     "da_workspace_init": (ctypes.c_int, [P, SZ, P]),
     "kv_append": (ctypes.c_int, [P, P, P, P, P, P, P, P]),
     "decode_attn_run": (ctypes.c_int, [P, P, P, P, P, I32, P, P, P, SZ, P]),

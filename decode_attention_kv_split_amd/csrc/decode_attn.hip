@@ -337,7 +337,7 @@ __device__ void sequence_prefix(const int32_t *__restrict__ lens, const Partitio
 // Arguments of the split kernel (passed by value as one kernel argument).
 struct SplitArgs {
     const void *q, *kc, *vc;
-    const int32_t *lens;
+    int32_t *lens;            // written only by the single-pass kernel with an append
     const float *kv_scales;   // [B, h_kv, 2] for fp8 / int8 caches, else unused
     float *part_ml, *part_o;  // per segment: [GT][2] (max, sum) and [GT][D] output rows
     float *out;               // decode_attn_run: output rows of units one workgroup covers
@@ -356,6 +356,10 @@ struct SplitArgs {
     // a KV group's g * nq query rows are cut into pt.tiles head tiles of gt rows (the last may
     // hold fewer); gt is also the per-segment stride of the partial arrays
     int gt, grp_rows;
+    // single pass: splits per unit, and the arrival counters (per sequence, per unit; at zero
+    // between launches)
+    int nsplit;
+    int32_t *seq_cnt, *unit_cnt;
 };
 
 // The query rows of a (sequence b, KV head kvh) are its g heads at each of the nq query
@@ -380,7 +384,10 @@ __device__ __forceinline__ QRow query_row(const SplitArgs &a, int b, int kvh, in
 // the first row and are never stored). The result (max, sum of exponentials, unnormalised
 // output; base-2 domain, V scale applied) goes to segment slot k of the partial arrays, or
 // normalised straight to out when `direct` (the segment is the whole unit).
-template <int KV, int D, int GT>
+// NW waves per workgroup, U row loads per lane per tile. COH: the partial results are stored
+// at agent scope (write-through to the device's coherence point), for a merge by another
+// workgroup of the same launch.
+template <int KV, int D, int GT, int NW = kWaves, int U = kUnroll, bool COH = false>
 __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kvh, int h0, int hv, int r0, int r1,
                                                size_t k, bool direct, int slen) {
     using T = Kv<KV>;
@@ -388,8 +395,8 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
     constexpr int EPL = T::kEpl;
     constexpr int LPR = D / EPL;         // lanes per row
     constexpr int RPL = kWave / LPR;     // rows per wave load
-    constexpr int TILE = kUnroll * RPL;  // rows per wave per iteration
-    constexpr int STEP = TILE * kWaves;  // rows per workgroup per iteration
+    constexpr int TILE = U * RPL;        // rows per wave per iteration
+    constexpr int STEP = TILE * NW;      // rows per workgroup per iteration
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int grp = lane / LPR, sub = lane % LPR;
 
@@ -443,10 +450,10 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
 
     // Steps I-III on one tile already in registers: scores for the GT heads, an online
     // softmax update of (m, l, o), then the weighted V rows.
-    auto process = [&](const Vec (&kt)[kUnroll], const Vec (&vt)[kUnroll], int tbase) {
-        float s[GT][kUnroll];
+    auto process = [&](const Vec (&kt)[U], const Vec (&vt)[U], int tbase) {
+        float s[GT][U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int row = tbase + u * RPL + grp;
             float kf[EPL];
             if constexpr (KV != DA_BF16) widen<KV>(kt[u], kf);
@@ -473,19 +480,19 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
         for (int h = 0; h < GT; ++h) {
             float mx = s[h][0];
 #pragma unroll
-            for (int u = 1; u < kUnroll; ++u) mx = fmaxf(mx, s[h][u]);
+            for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[h][u]);
             const float mn = fmaxf(m[h], mx);
             const float corr = __builtin_amdgcn_exp2f(m[h] - mn);
             m[h] = mn;
             float ps = 0.f;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) { s[h][u] = __builtin_amdgcn_exp2f(s[h][u] - mn); ps += s[h][u]; }
+            for (int u = 0; u < U; ++u) { s[h][u] = __builtin_amdgcn_exp2f(s[h][u] - mn); ps += s[h][u]; }
             l[h] = fmaf(l[h], corr, ps);
 #pragma unroll
             for (int e = 0; e < EPL; ++e) o[h][e] *= corr;
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             float vf[EPL];
             widen<KV>(vt[u], vf);
 #pragma unroll
@@ -498,11 +505,11 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
     // Software pipeline over two register buffers: while one tile is computed the loads of
     // the next are in flight. The whole byte offset sits in the per-lane offset (the scalar
     // offset is not range-checked), so rows at or past r1 read as zeros.
-    Vec ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
-    auto load = [&](Vec (&kt)[kUnroll], Vec (&vt)[kUnroll], int tbase) {
+    Vec ka[U], va[U], kb[U], vb[U];
+    auto load = [&](Vec (&kt)[U], Vec (&vt)[U], int tbase) {
         const uint32_t off = lane_off + tbase * ROWB;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             kt[u] = buffer_load<Vec>(krs, off + u * RPL * ROWB, 0);
             vt[u] = buffer_load<Vec>(vrs, off + u * RPL * ROWB, 0);
         }
@@ -545,8 +552,8 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
     }
 
     // Merge the waves in LDS and write this segment's result.
-    __shared__ float s_m[kWaves][GT], s_l[kWaves][GT];
-    __shared__ float s_o[kWaves][GT][D];
+    __shared__ float s_m[NW][GT], s_l[NW][GT];
+    __shared__ float s_o[NW][GT][D];
     if (grp == 0) {
 #pragma unroll
         for (int h = 0; h < GT; ++h) {
@@ -556,14 +563,14 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
         }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < hv * D; idx += kBlock) {
+    for (int idx = threadIdx.x; idx < hv * D; idx += NW * kWave) {
         const int h = idx / D, d = idx % D;
         float M = s_m[0][h];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
         float Ls = 0.f, O = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);
             Ls = fmaf(s_l[w][h], f, Ls);
             O = fmaf(s_o[w][h][d], f, O);
@@ -571,8 +578,17 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
         if (direct) {
             a.out[query_row(a, b, kvh, h0, h, slen).row * D + d] = O * vscale / Ls;
         } else {
-            a.part_o[(k * a.gt + h) * D + d] = O * vscale;
-            if (d == 0) { a.part_ml[(k * a.gt + h) * 2 + 0] = M; a.part_ml[(k * a.gt + h) * 2 + 1] = Ls; }
+            if constexpr (COH) {
+                __hip_atomic_store(&a.part_o[(k * a.gt + h) * D + d], O * vscale, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                if (d == 0) {
+                    __hip_atomic_store(&a.part_ml[(k * a.gt + h) * 2 + 0], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&a.part_ml[(k * a.gt + h) * 2 + 1], Ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            } else {
+                a.part_o[(k * a.gt + h) * D + d] = O * vscale;
+                if (d == 0) { a.part_ml[(k * a.gt + h) * 2 + 0] = M; a.part_ml[(k * a.gt + h) * 2 + 1] = Ls; }
+            }
         }
     }
     __syncthreads();  // the LDS arrays are reused by the next segment
@@ -1463,6 +1479,146 @@ void split_kv_attn_mfma_kernel(const SplitArgs a) {
     }
 }
 
+// Single pass (one launch), for latency-bound problems. Workgroup x takes split s of unit ul of
+// sequence b (x = (b * units + ul) * nsplit + s; a unit is a (KV head, head tile) as in the
+// split path, here on the vector ALUs): rows [s * n / nsplit, (s + 1) * n / nsplit) of the
+// sequence's n rows. With an append the workgroup whose rows end at the new last row stores it
+// first (as in the split path). Each split leaves its partial result, written through to the
+// device's coherence point (agent-scope stores), and counts itself in the unit's counter; the
+// split that arrives last merges the unit's partials by their log-sum-exp weights and writes out.
+// The order stores -> counter -> loads is made by the hardware's own means: every thread waits
+// for its stores to complete (vmcnt) before the barrier that precedes the counter's atomic add,
+// and the merging workgroup reads the partials with agent-scope loads, issued after its own
+// add returned. No workgroup ever waits for another, so no launch order or residency is
+// assumed. Every workgroup of a sequence also counts itself in the sequence's counter once it
+// has read lens[b]; the last of them advances lens[b] (with an append), when no workgroup of the
+// launch will read it again. Counters rest at zero: the last arrival resets each one.
+constexpr int kMaxSingleSplits = 64;
+
+template <int KV, int D, int GT>
+__global__ __launch_bounds__(kBlock) void decode_step_single_kernel(const SplitArgs a) {
+    const int S = a.nsplit, upb = a.pt.h_kv * a.pt.tiles;
+    const int x = blockIdx.x;
+    const int b = x / (upb * S), ul = (x / S) % upb, s = x % S;
+    const int kvh = ul / a.pt.tiles, t = ul % a.pt.tiles;
+    const int g = a.h_q / a.pt.h_kv;
+    const int h0 = kvh * g + t * a.gt, hv = min(a.gt, a.grp_rows - t * a.gt);
+    const bool append = a.pt.append_cap > 0;
+    // lens[b] is read by thread 0 alone and handed to the others through LDS, so that it is
+    // certainly read before this workgroup counts itself in the sequence's counter
+    __shared__ int s_len, s_last;
+    if (threadIdx.x == 0) s_len = a.lens[b];
+    __syncthreads();
+    const int L = s_len;
+    const int n = attended_len(L, append ? a.pt.append_cap : 0);
+    // count this workgroup in the sequence's counter now (lens[b] is read); the answer is only
+    // looked at when the workgroup ends, so the atomic's round trip overlaps the attention
+    int seq_arrived = 0;
+    if (threadIdx.x == 0) {
+        if (append && n == L && ul == 0 && s == 0) atomicOr(a.err, DA_DEV_ERR_APPEND_FULL);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        seq_arrived = __hip_atomic_fetch_add(&a.seq_cnt[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the last of the sequence's workgroups to count itself advances lens[b]: every workgroup of
+    // the launch that reads it has read it
+    auto finish_sequence = [&]() {
+        if (threadIdx.x == 0 && seq_arrived == upb * S - 1) {
+            __hip_atomic_store(&a.seq_cnt[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (append && n != L) a.lens[b] = n;
+        }
+    };
+    const size_t slot = (size_t)b * upb + ul;  // the unit's index
+    if (unit_rows(n, a.pt.max_len, a.pt.nq) == 0) {
+        if (s == 0) {  // this unit's query rows are zeroed
+            for (int i = threadIdx.x; i < hv * D; i += kBlock)
+                a.out[query_row(a, b, kvh, h0, i / D, n).row * D + i % D] = 0.f;
+            if (threadIdx.x == 0) atomicOr(a.err, DA_DEV_ERR_LEN_RANGE);
+        }
+        finish_sequence();
+        return;
+    }
+    const int r0 = (int)((int64_t)s * n / S), r1 = (int)((int64_t)(s + 1) * n / S);
+    if (append && n != L && r1 == n) {
+        const int n16 = a.row_bytes / 16;
+        const size_t kv = (size_t)b * a.pt.h_kv + kvh;
+        if (threadIdx.x < 2 * n16) {
+            const bool v = threadIdx.x >= n16;
+            const int j = threadIdx.x % n16;
+            const uint4 y = reinterpret_cast<const uint4 *>(static_cast<const char *>(v ? a.v_new : a.k_new) +
+                                                            kv * a.row_bytes)[j];
+            char *dst = const_cast<char *>(static_cast<const char *>(v ? a.vc : a.kc)) +
+                        (kv * a.cap + L) * (size_t)a.row_bytes;
+            reinterpret_cast<uint4 *>(dst)[j] = y;
+        }
+        __syncthreads();
+        // a 64-byte row shares its cache line with the previous row, which another workgroup on
+        // this CU may hold, stale, in the vector L1: drop it
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    if (S == 1) {  // the whole unit: normalised straight to out
+        attend_segment<KV, D, GT>(a, b, kvh, h0, hv, 0, n, 0, true, n);
+        finish_sequence();
+        return;
+    }
+    const size_t k = slot * S + s;
+    attend_segment<KV, D, GT, kWaves, kUnroll, true>(a, b, kvh, h0, hv, r0, r1, k, false, n);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int arrived = __hip_atomic_fetch_add(&a.unit_cnt[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = arrived == S - 1;
+        if (s_last) __hip_atomic_store(&a.unit_cnt[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    finish_sequence();
+    if (!s_last) return;
+    // The last split of the unit merges the nsplit partials of each of its hv query rows. Each
+    // (row, column) item takes tp threads (consecutive lanes, as many as 256 threads give each
+    // item, at most 8), each of which loads its share of the splits in one batch and keeps a
+    // running maximum; the tp threads then merge by lane exchanges. The partials are read with
+    // agent-scope (sc1) buffer loads, which the coherence point serves, and which, unlike atomic
+    // loads, the compiler issues together.
+    constexpr int kSc1 = 16;  // cache-policy bit of an agent-scope access
+    const __amdgpu_buffer_rsrc_t mls = make_rsrc(a.part_ml + slot * S * a.gt * 2, (uint32_t)(S * a.gt * 2 * 4));
+    const __amdgpu_buffer_rsrc_t os = make_rsrc(a.part_o + slot * S * a.gt * D, (uint32_t)(S * a.gt * D * 4));
+    const int items = hv * D;
+    const int tp = items >= kBlock / 2 ? 1 : items >= kBlock / 4 ? 2 : items >= kBlock / 8 ? 4 : 8;
+    for (int i0 = 0; i0 < items * tp; i0 += kBlock) {
+        const int i = (i0 + (int)threadIdx.x) / tp, sub = (i0 + (int)threadIdx.x) % tp;
+        const int h = min(i, items - 1) / D, d = min(i, items - 1) % D;
+        float M = kNegBig, Z = 0.f, O = 0.f;
+        for (int j0 = sub; j0 < S; j0 += 8 * tp) {
+            float mj[8], lj[8], oj[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {  // splits past nsplit are past the resources: zeros
+                const uint32_t kk = (uint32_t)((j0 + u * tp) * a.gt + h);
+                mj[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mls, kk * 8, 0, kSc1));
+                lj[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mls, kk * 8 + 4, 0, kSc1));
+                oj[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(os, (kk * D + d) * 4, 0, kSc1));
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (j0 + u * tp >= S) break;
+                const float Mn = fmaxf(M, mj[u]);
+                const float c = __builtin_amdgcn_exp2f(M - Mn), f = __builtin_amdgcn_exp2f(mj[u] - Mn);
+                Z = fmaf(Z, c, lj[u] * f);
+                O = fmaf(O, c, oj[u] * f);
+                M = Mn;
+            }
+        }
+        for (int off = 1; off < tp; off *= 2) {  // the item's tp lanes are consecutive
+            const float Mo = __shfl_xor(M, off), Zo = __shfl_xor(Z, off), Oo = __shfl_xor(O, off);
+            const float Mn = fmaxf(M, Mo);
+            const float c = __builtin_amdgcn_exp2f(M - Mn), f = __builtin_amdgcn_exp2f(Mo - Mn);
+            Z = fmaf(Z, c, Zo * f);
+            O = fmaf(O, c, Oo * f);
+            M = Mn;
+        }
+        if (sub == 0 && i < items) a.out[query_row(a, b, kvh, h0, h, n).row * D + d] = O / Z;
+    }
+}
+
 // Merges the segments of every query row by their log-sum-exp weights. Workgroup x takes rows
 // rw * (x % (gt / rw)) .. + rw - 1 of unit u = x / (gt / rw) (a unit's rows share its
 // segments), each row with kCombineBlock / rw threads: segment groups of D / 4 threads, one
@@ -1609,6 +1765,10 @@ int validate(const da_desc *d) {
                     (d->q_dtype == DA_BF16 && d->kv_dtype == DA_FP8_E4M3FN) ||
                     (d->q_dtype == DA_BF16 && d->kv_dtype == DA_INT8);
     if (!ok) return fail(DA_ERR_UNSUPPORTED, "dtype pair (q %d, kv %d) is not built", d->q_dtype, d->kv_dtype);
+    if (d->path != DA_PATH_AUTO && d->path != DA_PATH_SPLIT && d->path != DA_PATH_SINGLE)
+        return fail(DA_ERR_INVALID_ARG, "path must be DA_PATH_AUTO, _SPLIT or _SINGLE (got %d)", d->path);
+    if (d->path == DA_PATH_SINGLE && d->block_rows)
+        return fail(DA_ERR_INVALID_ARG, "block_rows sizes the split path's shares: it must be 0 with DA_PATH_SINGLE");
     if (d->flavour != DA_FLAVOUR_AUTO && d->flavour != DA_FLAVOUR_VECTOR && d->flavour != DA_FLAVOUR_MATRIX)
         return fail(DA_ERR_INVALID_ARG, "flavour must be DA_FLAVOUR_AUTO, _VECTOR or _MATRIX (got %d)", d->flavour);
     if (d->n_queries < 0 || d->n_queries > kMaxQueries)
@@ -1629,6 +1789,13 @@ struct Plan {
     int tiles;  // head tiles per KV group
     int nwg;
     bool mfma;  // matrix-core flavour
+    // one-call entry points: the single pass (one launch, splits merged by the last to finish)
+    // instead of the split kernel and the combine; its tiling (vector ALUs) replaces
+    // gt / gw / tiles when set
+    bool single;
+    int nsplit;      // single pass: splits per unit
+    size_t cnt_off;  // single pass: arrival counters, per sequence then per unit
+    size_t ncnt;     // single pass: counters (batch + units)
     // workspace: header, lengths copy, per-unit first / last workgroup, (max, sum), rows
     size_t lens_off, unit_off, ml_off, o_off, bytes;
 };
@@ -1643,11 +1810,12 @@ struct Plan {
 //   * otherwise the vector ALUs: fp32 caches with tiles of up to 8 rows, 8-bit and bf16 caches
 //     with 1 or 2 rows (up to 4 when the vector ALUs are asked for), in 1, 2, 4 or 8 slots.
 // desc->flavour asks for one flavour (measurement: both flavours on one shape).
-int plan_tiles(const da_desc *d, Plan *p) {
+int plan_tiles(const da_desc *d, Plan *p, bool vector_only = false) {
     const int rows = group_rows(d);
-    const bool can_mfma = d->kv_dtype != DA_F32;
+    const bool can_mfma = d->kv_dtype != DA_F32 && !vector_only;
     if (d->flavour == DA_FLAVOUR_MATRIX && !can_mfma)
-        return fail(DA_ERR_UNSUPPORTED, "the matrix-core flavour takes bf16, fp8 or int8 caches");
+        return fail(DA_ERR_UNSUPPORTED, vector_only ? "the single pass runs on the vector ALUs only"
+                                                    : "the matrix-core flavour takes bf16, fp8 or int8 caches");
     p->mfma = d->flavour == DA_FLAVOUR_MATRIX || (d->flavour == DA_FLAVOUR_AUTO && can_mfma && rows >= 3);
     const int widest = p->mfma ? 32 : d->kv_dtype == DA_F32 ? 8 : 4;
     p->tiles = (rows + widest - 1) / widest;
@@ -1661,6 +1829,12 @@ int plan_tiles(const da_desc *d, Plan *p) {
 // stages ahead; register rings one 64-row step of 512-byte rows); kept well above that.
 constexpr int64_t kSlotSlack = int64_t(1) << 20;
 constexpr int kMinRowsPerBlock = 256;  // below this a workgroup's share is mostly overhead
+// The library's choice of the single pass for the one-call entry points: every sequence's K and
+// V bytes at max_len (all its head tiles) at most this.
+constexpr int64_t kSingleMaxBytes = int64_t(1) << 20;
+// Rows per split of the single pass at max_len (each unit is cut into ceil(max_len / kSingleRows)
+// splits, at most kMaxSingleSplits): one 64-row step of a 4-wave workgroup.
+constexpr int kSingleRows = 64;
 constexpr int kFallbackResident = 512; // workgroups planned for when no device is visible
 
 // Workgroups to launch for one split-kernel instantiation on the current device: every CU
@@ -1733,7 +1907,9 @@ const void *split_kernel_ptr(int kv, int d, int gw, bool mfma) {
     return d == 64 ? split_kernel_ptr<DA_FP8_E4M3FN, 64>(gw, mfma) : split_kernel_ptr<DA_FP8_E4M3FN, 128>(gw, mfma);
 }
 
-int make_plan(const da_desc *d, int max_len, Plan *p) {
+// single_ok: the caller is a one-call entry point (decode_attn_run, decode_attn_append_run,
+// decode_attn_run_static), which may take the single pass.
+int make_plan(const da_desc *d, int max_len, Plan *p, bool single_ok = false) {
     int rc = validate(d);
     if (rc) return rc;
     if (max_len < 1 || max_len > d->cap)
@@ -1757,13 +1933,36 @@ int make_plan(const da_desc *d, int max_len, Plan *p) {
         nwg = std::min<int64_t>(nwg, (rows_max + kMinRowsPerBlock - 1) / kMinRowsPerBlock);
     }
     p->nwg = (int)std::max<int64_t>(1, std::min<int64_t>(nwg, 1 << 20));
-    const size_t segs = (size_t)p->nwg + units;
+    // the single pass's tiling (vector ALUs) and splits per unit; it fails only for the
+    // matrix-core flavour, which the single pass does not have
+    Plan v = *p;
+    const int rc_single = plan_tiles(d, &v, true);
+    const int64_t units_single = rc_single ? 0 : (int64_t)d->batch * d->h_kv * v.tiles;
+    p->nsplit = (int)std::min<int64_t>(kMaxSingleSplits, std::max<int64_t>(1, (max_len + kSingleRows - 1) / kSingleRows));
+    // workspace: the partial rows of either path, and the single pass's counters (which the
+    // split path never writes, so that they stay at zero)
+    const size_t part_rows = std::max<size_t>(((size_t)p->nwg + units) * p->gt,
+                                              (size_t)units_single * p->nsplit * (rc_single ? 0 : v.gt));
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     p->lens_off = kHeaderBytes;
-    p->unit_off = p->lens_off + up((size_t)d->batch * sizeof(int32_t));
+    p->cnt_off = p->lens_off + up((size_t)d->batch * sizeof(int32_t));
+    p->ncnt = (size_t)(d->batch + units_single);
+    p->unit_off = p->cnt_off + up((size_t)(d->batch + units_single) * sizeof(int32_t));
     p->ml_off = p->unit_off + up((size_t)units * sizeof(int2));
-    p->o_off = p->ml_off + up(segs * p->gt * 2 * sizeof(float));
-    p->bytes = p->o_off + up(segs * p->gt * d->d_v * sizeof(float));
+    p->o_off = p->ml_off + up(part_rows * 2 * sizeof(float));
+    p->bytes = p->o_off + up(part_rows * d->d_v * sizeof(float));
+    p->single = false;
+    if (single_ok && d->path != DA_PATH_SPLIT && d->block_rows == 0) {
+        if (rc_single && d->path == DA_PATH_SINGLE) return rc_single;
+        const int64_t seq_bytes = (int64_t)d->h_kv * v.tiles * max_len * 2 * row_bytes;
+        if (!rc_single && (d->path == DA_PATH_SINGLE || seq_bytes <= kSingleMaxBytes)) {
+            p->single = true;
+            p->mfma = false;
+            p->gt = v.gt;
+            p->gw = v.gw;
+            p->tiles = v.tiles;
+        }
+    }
     return DA_OK;
 }
 
@@ -1826,6 +2025,37 @@ void launch_split(int kv, int d, int gw, bool mfma, dim3 grid, hipStream_t st, c
     }
 }
 
+template <int KV, int D>
+void launch_single_gw(int gw, dim3 grid, hipStream_t st, const SplitArgs &args) {
+    if constexpr (KV == DA_F32) {
+        if (gw == 8) {
+            hipLaunchKernelGGL((decode_step_single_kernel<KV, D, 8>), grid, dim3(kBlock), 0, st, args);
+            return;
+        }
+    }
+    switch (gw) {
+    case 4: hipLaunchKernelGGL((decode_step_single_kernel<KV, D, 4>), grid, dim3(kBlock), 0, st, args); break;
+    case 2: hipLaunchKernelGGL((decode_step_single_kernel<KV, D, 2>), grid, dim3(kBlock), 0, st, args); break;
+    default: hipLaunchKernelGGL((decode_step_single_kernel<KV, D, 1>), grid, dim3(kBlock), 0, st, args); break;
+    }
+}
+
+void launch_single(int kv, int d, int gw, dim3 grid, hipStream_t st, const SplitArgs &args) {
+    if (kv == DA_F32) {
+        if (d == 64) launch_single_gw<DA_F32, 64>(gw, grid, st, args);
+        else launch_single_gw<DA_F32, 128>(gw, grid, st, args);
+    } else if (kv == DA_BF16) {
+        if (d == 64) launch_single_gw<DA_BF16, 64>(gw, grid, st, args);
+        else launch_single_gw<DA_BF16, 128>(gw, grid, st, args);
+    } else if (kv == DA_INT8) {
+        if (d == 64) launch_single_gw<DA_INT8, 64>(gw, grid, st, args);
+        else launch_single_gw<DA_INT8, 128>(gw, grid, st, args);
+    } else {
+        if (d == 64) launch_single_gw<DA_FP8_E4M3FN, 64>(gw, grid, st, args);
+        else launch_single_gw<DA_FP8_E4M3FN, 128>(gw, grid, st, args);
+    }
+}
+
 Partition partition_of(const da_desc *desc, const Plan &p, int max_len, bool append) {
     Partition pt;
     pt.batch = desc->batch;
@@ -1838,16 +2068,28 @@ Partition partition_of(const da_desc *desc, const Plan &p, int max_len, bool app
     return pt;
 }
 
-// Checks the run arguments and launches the split kernel: with out non-NULL, units that one
-// workgroup covers are written to out directly (decode_attn_run); otherwise every segment
-// writes its partial result (decode_attn_partial). Device error bits go to err_word when it is
-// given, else to the workspace's own error word.
+// Checks the run arguments and launches the split kernel: with out non-NULL (the one-call entry
+// points), units that one workgroup covers are written to out directly, or the plan may take
+// the single pass, which writes every output itself (*whole = true: no combine follows);
+// otherwise every segment writes its partial result (decode_attn_partial). Device error bits go
+// to err_word when it is given, else to the workspace's own error word.
 int run_split(const da_desc *desc, const void *q, const void *k_cache, const void *v_cache, const int32_t *lens,
               const void *k_new, const void *v_new, int32_t max_len, const float *kv_scales, float *out,
-              void *workspace, size_t ws_bytes, void *stream, const char *who, int32_t *err_word = nullptr) {
+              void *workspace, size_t ws_bytes, void *stream, const char *who, int32_t *err_word = nullptr,
+              bool *whole = nullptr, int32_t *counters = nullptr, size_t max_counters = 0) {
     Plan p;
-    int rc = make_plan(desc, max_len, &p);
+    int rc = make_plan(desc, max_len, &p, out != nullptr);
     if (rc) return rc;
+    if (p.single && counters && p.ncnt > max_counters) {  // too many counters for the caller's area
+        if (desc->path == DA_PATH_SINGLE)
+            return fail(DA_ERR_UNSUPPORTED, "%s: the single pass needs %zu counters, %zu available", who, p.ncnt,
+                        max_counters);
+        da_desc split = *desc;
+        split.path = DA_PATH_SPLIT;
+        rc = make_plan(&split, max_len, &p, true);
+        if (rc) return rc;
+    }
+    if (whole) *whole = p.single;
     if (!q || !k_cache || !v_cache || !lens || !workspace)
         return fail(DA_ERR_INVALID_ARG, "%s: a buffer pointer is NULL", who);
     const bool append = k_new || v_new;
@@ -1868,7 +2110,7 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     args.q = q;
     args.kc = k_cache;
     args.vc = v_cache;
-    args.lens = lens;
+    args.lens = const_cast<int32_t *>(lens);  // written by the single pass with an append only
     args.kv_scales = kv_scales;
     args.part_ml = reinterpret_cast<float *>(ws + p.ml_off);
     args.part_o = reinterpret_cast<float *>(ws + p.o_off);
@@ -1887,6 +2129,14 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     args.gt = p.gt;
     args.grp_rows = group_rows(desc);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.single) {
+        args.nsplit = p.nsplit;
+        args.seq_cnt = counters ? counters : reinterpret_cast<int32_t *>(ws + p.cnt_off);
+        args.unit_cnt = args.seq_cnt + desc->batch;
+        const int64_t grid = (int64_t)desc->batch * desc->h_kv * p.tiles * p.nsplit;
+        launch_single(desc->kv_dtype, desc->d_k, p.gw, dim3((unsigned)grid), st, args);
+        return launch_status("decode_step_single_kernel");
+    }
     if (out)
         launch_split<true>(desc->kv_dtype, desc->d_k, p.gw, p.mfma, dim3(p.nwg), st, args);
     else
@@ -1945,7 +2195,11 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
 // allocate. One copy per device, held from the library's load on that device until the process
 // ends. Host code never uses the array's name as an address (on the host it is only a stand-in
 // for the symbol): the device address comes from hipGetSymbolAddress, once per device.
+// Its first kStaticCounterBytes hold the single pass's arrival counters, which start at zero
+// (static storage) and which every single pass leaves at zero; no other use of the scratch
+// writes them, whatever the descriptor. The plan's workspace follows.
 constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+constexpr size_t kStaticCounterBytes = size_t(256) << 10;
 __device__ __align__(256) char scratch[kStaticScratchBytes];
 
 // Device address of this device's scratch (looked up on the first call on each device).
@@ -1997,14 +2251,16 @@ int da_workspace_size(const da_desc *desc, int32_t max_len, size_t *bytes) {
 }
 
 int da_plan(const da_desc *desc, int32_t max_len, int32_t *rows_per_block, int32_t *n_blocks,
-            int32_t *heads_per_block_out) {
+            int32_t *heads_per_block_out, int32_t *path_out) {
     Plan p;
-    const int rc = make_plan(desc, max_len, &p);
+    const int rc = make_plan(desc, max_len, &p, true);
     if (rc) return rc;
     const int64_t rows_max = (int64_t)desc->batch * desc->h_kv * p.tiles * max_len;
-    if (rows_per_block) *rows_per_block = (int32_t)((rows_max + p.nwg - 1) / p.nwg);
-    if (n_blocks) *n_blocks = p.nwg;
+    const int64_t nwg = p.single ? (int64_t)desc->batch * desc->h_kv * p.tiles * p.nsplit : p.nwg;
+    if (rows_per_block) *rows_per_block = (int32_t)((rows_max + nwg - 1) / nwg);
+    if (n_blocks) *n_blocks = (int32_t)nwg;
     if (heads_per_block_out) *heads_per_block_out = p.gt;
+    if (path_out) *path_out = p.single ? DA_PATH_SINGLE : DA_PATH_SPLIT;
     return DA_OK;
 }
 
@@ -2053,9 +2309,10 @@ int decode_attn_run(const da_desc *desc, const void *q, const void *k_cache, con
                     const int32_t *lens, int32_t max_len, const float *kv_scales, float *out, void *workspace,
                     size_t ws_bytes, void *stream) {
     if (!out) return fail(DA_ERR_INVALID_ARG, "decode_attn_run: out is NULL");
+    bool whole = false;
     const int rc = run_split(desc, q, k_cache, v_cache, lens, nullptr, nullptr, max_len, kv_scales, out, workspace,
-                             ws_bytes, stream, "decode_attn_run");
-    if (rc) return rc;
+                             ws_bytes, stream, "decode_attn_run", nullptr, &whole);
+    if (rc || whole) return rc;
     return run_combine(desc, const_cast<int32_t *>(lens), max_len, out, workspace, ws_bytes, stream, 1, false,
                        "decode_attn_run");
 }
@@ -2079,9 +2336,10 @@ int decode_attn_append_run(const da_desc *desc, const void *q, void *k_cache, vo
                            float *out, void *workspace, size_t ws_bytes, void *stream) {
     if (!out) return fail(DA_ERR_INVALID_ARG, "decode_attn_append_run: out is NULL");
     if (!k_new || !v_new) return fail(DA_ERR_INVALID_ARG, "decode_attn_append_run: k_new or v_new is NULL");
+    bool whole = false;
     const int rc = run_split(desc, q, k_cache, v_cache, lens, k_new, v_new, max_len, kv_scales, out, workspace,
-                             ws_bytes, stream, "decode_attn_append_run");
-    if (rc) return rc;
+                             ws_bytes, stream, "decode_attn_append_run", nullptr, &whole);
+    if (rc || whole) return rc;
     return run_combine(desc, lens, max_len, out, workspace, ws_bytes, stream, 1, true, "decode_attn_append_run");
 }
 
@@ -2094,17 +2352,20 @@ int decode_attn_run_static(const da_desc *desc, const void *q, const void *k_cac
     Plan p;
     int rc = make_plan(desc, max_len, &p);
     if (rc) return rc;
-    if (p.bytes > kStaticScratchBytes)
+    if (p.bytes > kStaticScratchBytes - kStaticCounterBytes)
         return fail(DA_ERR_WORKSPACE, "decode_attn_run_static: needs %zu bytes of scratch, the static scratch holds %zu",
-                    p.bytes, kStaticScratchBytes);
-    void *ws = nullptr;
-    rc = static_scratch(&ws);
+                    p.bytes, kStaticScratchBytes - kStaticCounterBytes);
+    void *base = nullptr;
+    rc = static_scratch(&base);
     if (rc) return rc;
+    int32_t *counters = static_cast<int32_t *>(base);
+    void *ws = static_cast<char *>(base) + kStaticCounterBytes;
     // without dev_err the error bits land in the scratch's own error word, which nothing reads
     int32_t *err = dev_err ? dev_err : static_cast<int32_t *>(ws);
+    bool whole = false;
     rc = run_split(desc, q, k_cache, v_cache, lens, nullptr, nullptr, max_len, kv_scales, out, ws, p.bytes, stream,
-                   "decode_attn_run_static", err);
-    if (rc) return rc;
+                   "decode_attn_run_static", err, &whole, counters, kStaticCounterBytes / sizeof(int32_t));
+    if (rc || whole) return rc;
     return run_combine(desc, const_cast<int32_t *>(lens), max_len, out, ws, p.bytes, stream, 1, false,
                        "decode_attn_run_static", err);
 }

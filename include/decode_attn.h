@@ -66,6 +66,10 @@ typedef enum { DA_F32 = 0, DA_BF16 = 1, DA_FP8_E4M3FN = 2, DA_INT8 = 3 } da_dtyp
  * both on one shape). The matrix-core flavour takes bf16, fp8 and int8 caches only. */
 typedef enum { DA_FLAVOUR_AUTO = 0, DA_FLAVOUR_VECTOR = 1, DA_FLAVOUR_MATRIX = 2 } da_flavour;
 
+/* Launch path of the one-call entry points (da_desc.path): the library's choice; the split
+ * path (split kernel + log-sum-exp combine, two launches); or the single pass (one launch). */
+typedef enum { DA_PATH_AUTO = 0, DA_PATH_SPLIT = 1, DA_PATH_SINGLE = 2 } da_path;
+
 /*
  * Problem descriptor. Supported: d_k == d_v in {64, 128}; (q_dtype, kv_dtype) in
  * {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN), (BF16, INT8)}; any h_q that is a
@@ -96,6 +100,21 @@ typedef enum { DA_FLAVOUR_AUTO = 0, DA_FLAVOUR_VECTOR = 1, DA_FLAVOUR_MATRIX = 2
  * flavour (da_flavour): DA_FLAVOUR_AUTO (0) for the rule above; DA_FLAVOUR_VECTOR or
  * DA_FLAVOUR_MATRIX to run one flavour regardless (the vector ALUs then cut 8-bit and bf16
  * groups into tiles of up to 4 rows). Results agree within the tolerances either way.
+ *
+ * path (da_path) applies to the one-call entry points (decode_attn_run, decode_attn_append_run,
+ * decode_attn_run_static); the two-stage entry points always take the split path. The single
+ * pass runs the whole step in one kernel launch, on the vector ALUs: every (sequence, KV head,
+ * head tile) is cut into ceil(max_len / 64) splits (at most 64) of one workgroup each; the
+ * workgroup holding a sequence's new last row appends it first, each split leaves a partial
+ * result in the workspace, and the split that finishes last merges the unit's partials into
+ * out (no workgroup waits for another). It is for latency-bound problems, where a second
+ * launch costs more than the rows. DA_PATH_AUTO (0) takes it when every sequence's K and V
+ * bytes at max_len (over all its head tiles) are at most 1 MiB, and block_rows is 0;
+ * DA_PATH_SINGLE asks for it whatever the size (block_rows must then be 0; it refuses
+ * DA_FLAVOUR_MATRIX); DA_PATH_SPLIT never takes it. The single pass keeps arrival counters in
+ * the workspace that rest at zero between calls: the workspace must have been zeroed by
+ * da_workspace_init once, and again before it serves a descriptor with another batch, h_kv,
+ * h_q, n_queries or head size (the static scratch of decode_attn_run_static needs nothing).
  */
 typedef struct {
     int32_t batch;
@@ -110,6 +129,7 @@ typedef struct {
     int32_t block_rows;
     int32_t n_queries; /* query rows per sequence; 0 or 1 = single-query decode */
     int32_t flavour;   /* da_flavour; 0 = the library's choice */
+    int32_t path;      /* da_path; 0 = the library's choice */
 } da_desc;
 
 /*
@@ -124,16 +144,18 @@ typedef struct {
 int da_workspace_size(const da_desc *desc, int32_t max_len, size_t *bytes);
 
 /*
- * Chosen work partition for (desc, max_len), all outputs host int32 (any may be NULL):
- * cache rows per workgroup when every sequence has max_len rows, workgroups launched,
- * query heads each workgroup serves.
+ * Chosen work partition of the one-call entry points for (desc, max_len), all outputs host
+ * int32 (any may be NULL): cache rows per workgroup when every sequence has max_len rows,
+ * workgroups launched (batch for the single pass), query rows per head tile, and the path
+ * taken (DA_PATH_SPLIT or DA_PATH_SINGLE).
  */
 int da_plan(const da_desc *desc, int32_t max_len, int32_t *rows_per_block, int32_t *n_blocks,
-            int32_t *heads_per_block);
+            int32_t *heads_per_block, int32_t *path);
 
 /*
  * Zeroes the whole workspace with a kernel (not a memset), clearing its error word. Call
- * once after allocating it.
+ * once after allocating it, and before the workspace serves another descriptor (its single
+ * pass counters must be at zero; every call leaves them so for its own descriptor).
  */
 int da_workspace_init(void *workspace, size_t ws_bytes, void *stream);
 
@@ -222,8 +244,10 @@ int decode_attn_append_combine(const da_desc *desc, int32_t *lens, int32_t max_l
  * (code under HIP graph capture, serving loops that must not allocate, harnesses that forbid
  * it). Same arguments, kernels and results as decode_attn_run (bit for bit), except:
  *   - the split partials live in a static scratch array the library holds on each device it
- *     runs on (16 MiB, kept until the process ends); a (desc, max_len) whose
- *     da_workspace_size() exceeds 16 MiB is rejected with DA_ERR_WORKSPACE, nothing launched;
+ *     runs on (16 MiB, kept until the process ends): 256 KiB of it for the single pass's
+ *     counters, the rest for the workspace; a (desc, max_len) whose da_workspace_size()
+ *     exceeds 16 MiB - 256 KiB is rejected with DA_ERR_WORKSPACE, nothing launched (and one
+ *     whose single pass would need more than 65536 counters takes the split path);
  *   - dev_err (device int32, caller-owned, 4-byte aligned, may be NULL) receives the
  *     DA_DEV_ERR_* bits ORed in, as the workspace's error word does for decode_attn_run; the
  *     caller clears it. With NULL the bits are dropped (the work is still skipped and zeroed).

@@ -42,9 +42,9 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-def desc_of(w: workloads.Workload, block_rows: int = 0) -> da.Desc:
+def desc_of(w: workloads.Workload, block_rows: int = 0, path: int = da.PATH_AUTO) -> da.Desc:
     return da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, workloads.TORCH_DTYPE[w.q_dtype],
-                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, block_rows)
+                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, block_rows, 1, da.FLAVOUR_AUTO, path)
 
 
 def to_gpu(case: dict, dev="cuda") -> dict:
@@ -73,9 +73,9 @@ def check_close(got: torch.Tensor, ref: np.ndarray, kv: str, what: str = "") -> 
 
 
 def run_gpu(w: workloads.Workload, c: dict, block_rows: int = 0, max_len: int | None = None,
-            lens_key: str = "lens_final"):
+            lens_key: str = "lens_final", path: int = da.PATH_AUTO):
     """Appends `steps` rows (if any) then attends once; returns out (GPU) and the GPU caches."""
-    desc = desc_of(w, block_rows)
+    desc = desc_of(w, block_rows, path)
     g = to_gpu(c)
     lens = g["lens_init"].clone()
     ml = int(c["lens_final"].max()) if max_len is None else max_len

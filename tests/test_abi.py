@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def _desc(**kw):
     base = dict(batch=2, h_q=8, h_kv=2, d_k=128, d_v=128, cap=1024, q_dtype=1, kv_dtype=1,
-                scale=0.088, block_rows=0, n_queries=0, flavour=0)
+                scale=0.088, block_rows=0, n_queries=0, flavour=0, path=1)  # the split path's plan
     base.update(kw)
     return da._CDesc(**base)
 
@@ -79,7 +79,7 @@ def test_invalid_descriptors_are_rejected(lib, kw, max_len, code):
 
 def _plan(lib, d, max_len):
     r, n, g = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    assert lib.da_plan(ctypes.byref(d), max_len, ctypes.byref(r), ctypes.byref(n), ctypes.byref(g)) == 0
+    assert lib.da_plan(ctypes.byref(d), max_len, ctypes.byref(r), ctypes.byref(n), ctypes.byref(g), None) == 0
     return r.value, n.value, g.value
 
 
@@ -228,7 +228,7 @@ def test_static_entry_rejects_work_beyond_its_scratch(lib):
     more is refused on the host (DA_ERR_WORKSPACE) before anything is launched."""
     big = _desc(batch=1024, h_q=32, h_kv=32, cap=4096)
     rc, n = _ws_size(lib, big, 4096)
-    assert rc == 0 and n > 16 << 20
+    assert rc == 0 and n > (16 << 20) - (256 << 10)
     assert lib.decode_attn_run_static(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 4096, None, FAKE, None, None) == -3
     assert b"static scratch" in lib.da_last_error()
     d = _desc()
@@ -251,3 +251,28 @@ def test_slots_beyond_32_bit_offsets_are_refused(lib, kw, max_len, ok):
     d = _desc(cap=max_len, batch=1, h_q=2, h_kv=1, **kw)
     rc, _ = _ws_size(lib, d, max_len)
     assert rc == (0 if ok else -2), lib.da_last_error()
+
+
+def test_single_pass_choice(lib):
+    """The one-call entry points take the single pass when every sequence's K and V bytes at
+    max_len are at most 1 MiB, unless a path or block_rows is given; da_plan then reports its
+    workgroups (every unit cut into ceil(max_len / 64) splits, at most 64) and the vector-ALU
+    head tile."""
+    one = _desc(batch=1, h_q=1, h_kv=1, d_k=64, d_v=64, cap=1024, q_dtype=0, kv_dtype=0, path=0)
+    assert _plan(lib, one, 1024) == (64, 16, 1)              # fp32 d=64: 512 KiB per sequence
+    gqa = _desc(batch=16, h_q=32, h_kv=8, cap=32768, path=0)
+    assert _plan(lib, gqa, 256) == (64, 16 * 8 * 4, 4)       # 8 KV heads x 256 rows x 512 B = 1 MiB
+    assert _plan(lib, gqa, 257)[1] == -(-16 * 8 * 257 // 256)   # beyond: the split path, 256-row shares
+    assert _plan(lib, _desc(batch=16, h_q=32, h_kv=8, cap=32768, path=2), 32768) == (512, 16 * 8 * 64, 4)
+    assert _plan(lib, _desc(batch=16, h_q=32, h_kv=8, cap=32768, path=0, block_rows=64), 200)[1] > 16
+    assert _ws_size(lib, _desc(path=2, block_rows=64), 100)[0] == -1
+    assert _ws_size(lib, _desc(path=3), 100)[0] == -1
+    # the single pass runs on the vector ALUs: the matrix-core flavour refuses it, the automatic
+    # flavour falls back to the split path
+    rc = lib.da_plan(ctypes.byref(_desc(path=2, flavour=2)), 100, None, None, None, None)
+    assert rc == -2
+    pa = ctypes.c_int32(-1)
+    assert lib.da_plan(ctypes.byref(one), 1024, None, None, None, ctypes.byref(pa)) == 0 and pa.value == 2
+    assert lib.da_plan(ctypes.byref(gqa), 4096, None, None, None, ctypes.byref(pa)) == 0 and pa.value == 1
+    # the workspace does not depend on the path
+    assert _ws_size(lib, _desc(path=0), 100) == _ws_size(lib, _desc(path=1), 100)

@@ -50,13 +50,15 @@ def test_cache_rotations():
     assert bench.cache_rotations(2 * gib, 10, 100, False) == 2
     assert bench.cache_rotations(gib // 4, 10, 100, False) == 8
     assert bench.cache_rotations(gib // 100, 10, 100, False) == 8
-    # with appends, enough copies that no sequence fills up: room for 865 appends per copy
-    for warmup, steps in [(10, 100), (100, 1000), (10, 3000), (100, 20000)]:
+    # with appends, enough copies that no sequence fills up: room for 865 appends per copy (the
+    # timed steps run twice: the two-stage form, then the one-call form)
+    for warmup, steps in [(10, 100), (100, 1000), (10, 3000), (100, 12000)]:
         r = bench.cache_rotations(2 * gib, warmup, steps, False, room=865)
         assert bench.uses_per_copy(r, warmup, steps, False) <= 865
         assert r == 2 or bench.uses_per_copy(r - 1, warmup, steps, False) > 865
     # graph replays append once per copy per replay
-    assert bench.uses_per_copy(2, 10, 100, True) == 55 + 50
+    assert bench.uses_per_copy(2, 10, 100, True) == 105 + 50
+    assert bench.uses_per_copy(2, 10, 100, False, one_call=False) == 55
 
 
 def test_code_digest_keeps_comments_and_layout_out():

@@ -56,9 +56,10 @@ def bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().contiguous().view(torch.uint8).numpy()
 
 
-def run_both(kv, d, h_q, h_kv, lens, cap, seed, block_rows):
+def run_both(kv, d, h_q, h_kv, lens, cap, seed, block_rows, path=da.PATH_AUTO):
     c = make_case(kv, d, h_q, h_kv, lens, cap, seed)
-    desc = da.Desc(len(lens), h_q, h_kv, d, cap, c["q"].dtype, TORCH[kv], workloads._inv_sqrt(d), block_rows)
+    desc = da.Desc(len(lens), h_q, h_kv, d, cap, c["q"].dtype, TORCH[kv], workloads._inv_sqrt(d), block_rows,
+                   1, da.FLAVOUR_AUTO, path)
     max_len = cap
     g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in c.items()}
     sc = g["scales"]
@@ -91,12 +92,14 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("block_rows", [0, 37])
+@pytest.mark.parametrize("block_rows,path", [(0, da.PATH_SPLIT), (37, da.PATH_SPLIT), (0, da.PATH_SINGLE)])
 @pytest.mark.parametrize("kv,d,h_q,h_kv,lens", CASES)
-def test_fused_step_equals_append_then_run(kv, d, h_q, h_kv, lens, block_rows):
+def test_fused_step_equals_append_then_run(kv, d, h_q, h_kv, lens, block_rows, path):
+    """Both paths of the one-call entry points: the split kernel + combine (library shares or
+    37-row shares) and the single pass (one workgroup per sequence, one launch)."""
     seed = 300 + CASES.index((kv, d, h_q, h_kv, lens))
-    log(f"case fused append {kv} d={d} h_q={h_q} h_kv={h_kv} lens={lens} block_rows={block_rows}")
-    c, a, b = run_both(kv, d, h_q, h_kv, lens, 1500, seed, block_rows)
+    log(f"case fused append {kv} d={d} h_q={h_q} h_kv={h_kv} lens={lens} block_rows={block_rows} path={path}")
+    c, a, b = run_both(kv, d, h_q, h_kv, lens, 1500, seed, block_rows, path)
     assert np.array_equal(bits(a["out"]), bits(b["out"])), "outputs differ"
     assert np.array_equal(bits(a["k"]), bits(b["k"])) and np.array_equal(bits(a["v"]), bits(b["v"]))
     assert torch.equal(a["lens"], b["lens"])
@@ -134,12 +137,15 @@ def test_fused_two_stage_equals_fused_run():
     assert (one - two).abs().max().item() <= 1e-5
 
 
-def test_fused_steps_in_a_loop_match_the_oracle():
+@pytest.mark.parametrize("path", [da.PATH_AUTO, da.PATH_SPLIT])
+def test_fused_steps_in_a_loop_match_the_oracle(path):
     """The single-head fp32 workload driven by the fused step alone: 16 steps, n 1008 -> 1024,
-    every step within 1e-5 of the oracle and the cache bit-exact at the end."""
+    every step within 1e-5 of the oracle and the cache bit-exact at the end; the library's
+    choice (the single pass: one launch per step) and the split path."""
     w = workloads.WORKLOADS["single_head_f32"]
     c = workloads.generate(w)
-    desc = da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, torch.float32, torch.float32, w.scale)
+    desc = da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, torch.float32, torch.float32, w.scale, 0, 1, da.FLAVOUR_AUTO, path)
+    assert da.da_plan(desc, w.cap)["path"] == (da.PATH_SINGLE if path == da.PATH_AUTO else da.PATH_SPLIT)
     kc, vc = c["k_cache"].cuda(), c["v_cache"].cuda()
     lens = c["lens_init"].cuda()
     q = c["q"].cuda()

@@ -24,9 +24,9 @@ def mq_workload(kv, d, h_q, h_kv, T, lens, cap, seed):
                               workloads._inv_sqrt(d), nq=T)
 
 
-def run_multi(w, c, block_rows=0, max_len=None):
+def run_multi(w, c, block_rows=0, max_len=None, path=da.PATH_AUTO):
     desc = da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, workloads.TORCH_DTYPE[w.q_dtype],
-                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, block_rows, w.nq)
+                   workloads.TORCH_DTYPE[w.kv_dtype], w.scale, block_rows, w.nq, da.FLAVOUR_AUTO, path)
     g = to_gpu(c)
     ml = max_len or int(c["lens_final"].max())
     ws = da.Workspace(desc, ml)
@@ -55,14 +55,16 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", [da.PATH_SPLIT, da.PATH_SINGLE])
 @pytest.mark.parametrize("kv,d,h_q,h_kv,T,block_rows", CASES)
-def test_multi_query_parity(kv, d, h_q, h_kv, T, block_rows):
+def test_multi_query_parity(kv, d, h_q, h_kv, T, block_rows, path):
     seed = 500 + CASES.index((kv, d, h_q, h_kv, T, block_rows))
     w = mq_workload(kv, d, h_q, h_kv, T, ("uniform", T, 1500), 1500, seed)
     c = workloads.generate(w)
     c["lens_final"][0] = T  # the first query of sequence 0 sees exactly one row
-    log(f"case multi {kv} d={d} h_q={h_q} h_kv={h_kv} T={T} block_rows={block_rows} lens={c['lens_final'].tolist()}")
-    out, err = run_multi(w, c, block_rows)
+    log(f"case multi {kv} d={d} h_q={h_q} h_kv={h_kv} T={T} block_rows={block_rows} path={path} "
+        f"lens={c['lens_final'].tolist()}")
+    out, err = run_multi(w, c, block_rows if path == da.PATH_SPLIT else 0, path=path)
     assert err == 0
     ref = oracle.decode_multi_f64(c["q"], c["k_cache"], c["v_cache"], c["lens_final"], w.scale,
                                   kv_scales=c["kv_scales"])
@@ -84,7 +86,8 @@ def test_single_query_descriptor_is_the_decode_path():
     assert torch.equal(outs[0], outs[1])
 
 
-def test_lengths_shorter_than_T_are_flagged():
+@pytest.mark.parametrize("path", [da.PATH_SPLIT, da.PATH_SINGLE])
+def test_lengths_shorter_than_T_are_flagged(path):
     """A sequence with fewer rows than query rows has no causal prefix for its first queries:
     its output is zeroed and DA_DEV_ERR_LEN_RANGE raised; the other sequences are unaffected."""
     T = 4
@@ -93,7 +96,7 @@ def test_lengths_shorter_than_T_are_flagged():
     lens = c["lens_final"].clone()
     lens[2] = T - 1
     c2 = dict(c, lens_final=lens)
-    out, err = run_multi(w, c2, 0, 600)
+    out, err = run_multi(w, c2, 0, 600, path)
     assert err == da.DEV_ERR_LEN_RANGE
     o = out.cpu()
     assert torch.equal(o[2], torch.zeros_like(o[2]))

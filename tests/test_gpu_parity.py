@@ -29,12 +29,13 @@ def W(**kw):
 
 
 # ------------------------------------------------------------------ the single-head workload
-def test_single_head_f32_sixteen_append_then_attend_steps():
+@pytest.mark.parametrize("path", [da.PATH_SINGLE, da.PATH_SPLIT])
+def test_single_head_f32_sixteen_append_then_attend_steps(path):
     """n 1008 -> 1024, fp32, 1e-5 relative per step; cache bit-exact afterwards (I4, I5)."""
     w = workloads.WORKLOADS["single_head_f32"]
     c = workloads.generate(w)
-    log(f"case single_head_f32 B={w.B} d={w.d}")
-    desc = desc_of(w)
+    log(f"case single_head_f32 B={w.B} d={w.d} path={path}")
+    desc = desc_of(w, path=path)
     g = to_gpu(c)
     lens = g["lens_init"].clone()
     ws = da.Workspace(desc, w.cap)
@@ -96,18 +97,25 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", ["split", "single"])
 @pytest.mark.parametrize("kv,d,h_q,h_kv,lens,chunk", CASES)
-def test_parity_small(kv, d, h_q, h_kv, lens, chunk):
+def test_parity_small(kv, d, h_q, h_kv, lens, chunk, path):
+    """Every case on both paths of decode_attn_run: the split kernel (with the case's shares)
+    and the combine, and the single pass (one workgroup per sequence)."""
     w = W(kv_dtype=kv, d=d, h_q=h_q, h_kv=h_kv, lens=lens, seed=100 + CASES.index((kv, d, h_q, h_kv, lens, chunk)))
     c = workloads.generate(w)
-    log(f"case {kv} d={d} h_q={h_q} h_kv={h_kv} chunk={chunk} lens={c['lens_final'].tolist()}")
-    out, _, _, err = run_gpu(w, c, block_rows=chunk)
+    log(f"case {kv} d={d} h_q={h_q} h_kv={h_kv} chunk={chunk} path={path} lens={c['lens_final'].tolist()}")
+    if path == "split":
+        out, _, _, err = run_gpu(w, c, block_rows=chunk, path=da.PATH_SPLIT)
+    else:
+        out, _, _, err = run_gpu(w, c, path=da.PATH_SINGLE)
     assert err == 0
     check_close(out, oracle_out(w, c), kv)
 
 
+@pytest.mark.parametrize("path", [da.PATH_SPLIT, da.PATH_SINGLE])
 @pytest.mark.parametrize("kv", ["f32", "bf16", "fp8", "int8"])
-def test_parity_tile_and_split_boundaries(kv):
+def test_parity_tile_and_split_boundaries(kv, path):
     """Lengths at 1, tile edges and split edges (+-1); f32/bf16 append their last row first."""
     edges = [1, 2, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1023]
     steps = 0 if kv in workloads.SCALED else 1
@@ -125,7 +133,7 @@ def test_parity_tile_and_split_boundaries(kv):
     c["lens_final"] = torch.tensor(edges, dtype=torch.int32)
     c["lens_init"] = c["lens_final"] - steps
     log(f"case boundaries {kv} lens={edges}")
-    out, _, _, err = run_gpu(w, c, block_rows=256, max_len=1024)
+    out, _, _, err = run_gpu(w, c, block_rows=256 if path == da.PATH_SPLIT else 0, max_len=1024, path=path)
     assert err == 0
     check_close(out, oracle_out(w, c), kv)
 
@@ -219,12 +227,13 @@ def test_both_flavours_match_the_oracle(kv, d, h_q, h_kv):
         check_close(out, ref, kv, f"flavour {flavour}")
 
 
-def test_invalid_lengths_between_valid_ones():
+@pytest.mark.parametrize("path", [da.PATH_SPLIT, da.PATH_SINGLE])
+def test_invalid_lengths_between_valid_ones(path):
     """Sequences with an out-of-range length hold no rows of the partition: their output
     is zeroed and flagged, and the sequences around them are unaffected."""
     w = W(B=4, h_q=8, h_kv=2, cap=600, lens=("const", 600), seed=71)
     c = workloads.generate(w)
-    desc = desc_of(w, 100)
+    desc = desc_of(w, 100 if path == da.PATH_SPLIT else 0, path)
     g = to_gpu(c)
     lens = torch.tensor([300, 0, 600, 500], dtype=torch.int32)
     ws = da.Workspace(desc, 550)
@@ -351,6 +360,28 @@ def test_workspace_reuse_across_calls():
     assert da.da_read_device_error(ws) == 0
 
 
+def test_one_workspace_serves_both_paths_in_turn():
+    """The two-stage entry points (split path) and decode_attn_run on the single pass, in turn on
+    one workspace: the split path never touches the single pass's counters, which every single
+    pass leaves at zero."""
+    w = W(B=6, h_q=8, h_kv=2, d=64, cap=500, lens=("uniform", 1, 500), seed=48)
+    c = workloads.generate(w)
+    desc = desc_of(w)
+    assert da.da_plan(desc, w.cap)["path"] == da.PATH_SINGLE
+    g = to_gpu(c)
+    ws = da.Workspace(desc, w.cap)
+    ref = oracle_out(w, c)
+    for _ in range(3):
+        two = torch.empty(w.B, w.h_q, w.d, device="cuda")
+        da.decode_attn_partial(desc, g["q"], g["k_cache"], g["v_cache"], g["lens_final"], w.cap, None, ws)
+        da.decode_attn_combine(desc, g["lens_final"], w.cap, two, ws)
+        one = torch.full_like(two, 9.0)
+        da.decode_attn_run(desc, g["q"], g["k_cache"], g["v_cache"], g["lens_final"], w.cap, None, one, ws)
+        assert da.da_read_device_error(ws) == 0
+        check_close(two, ref, "bf16", "split path")
+        check_close(one, ref, "bf16", "single pass")
+
+
 def test_runs_are_bitwise_deterministic():
     w = W(B=4, h_q=32, h_kv=8, cap=3000, lens=("uniform", 1, 3000), seed=41)
     c = workloads.generate(w)
@@ -378,11 +409,12 @@ def test_append_is_bit_exact_over_the_whole_buffer():
     assert np.array_equal(lens.cpu().numpy(), ln) and da.da_read_device_error(ws) == 0
 
 
-def test_device_errors_are_flagged_and_work_skipped():
+@pytest.mark.parametrize("path", [da.PATH_SPLIT, da.PATH_SINGLE])
+def test_device_errors_are_flagged_and_work_skipped(path):
     """A full sequence is not appended to; an out-of-range length gives zeros; both set bits."""
     w = W(B=2, h_q=4, h_kv=2, d=128, cap=16, lens=("const", 16), steps=0, seed=2)
     c = workloads.generate(w)
-    desc = desc_of(w)
+    desc = desc_of(w, path=path)
     g = to_gpu(c)
     ws = da.Workspace(desc, 16)
     lens = torch.tensor([16, 5], dtype=torch.int32, device="cuda")

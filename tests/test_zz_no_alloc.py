@@ -90,3 +90,24 @@ def test_static_scratch_without_error_word():
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
     check_close(out, oracle_out(w, c), "bf16")
+
+
+def test_static_scratch_across_descriptors_and_paths():
+    """Calls with other descriptors and both launch paths in turn on the one static scratch (the
+    single pass keeps its counters in a part of the scratch nothing else writes): each equals
+    decode_attn_run on a fresh workspace."""
+    cases = [
+        _case(B=1, h_q=1, h_kv=1, d=64, cap=1024, kv_dtype="f32", lens=("const", 1024), seed=210),   # single
+        _case(B=3, h_q=32, h_kv=8, cap=2000, lens=("uniform", 1000, 2000), seed=211),               # split
+        _case(B=5, h_q=8, h_kv=2, d=64, cap=300, lens=("uniform", 1, 300), seed=212),                # single
+        _case(B=2, h_q=4, h_kv=4, cap=4000, kv_dtype="int8", lens=("uniform", 3000, 4000), seed=213), # split
+        _case(B=1, h_q=1, h_kv=1, d=64, cap=1024, kv_dtype="f32", lens=("const", 1000), seed=214),   # single
+    ]
+    for rep in range(2):
+        for w in cases:
+            log(f"case static round {rep}: B={w.B} h_q={w.h_q} h_kv={w.h_kv} d={w.d} {w.kv_dtype} "
+                f"path {da.da_plan(desc_of(w), w.cap)['path']}")
+            c, ref, e, out, s = _both(w)
+            assert e == 0 and s == 0
+            assert torch.equal(out, ref)
+            check_close(out, oracle_out(w, c), w.kv_dtype, "static across descriptors")
