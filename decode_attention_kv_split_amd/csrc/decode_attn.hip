@@ -50,6 +50,7 @@ constexpr float kNegBig = -3.0e38f;  // finite "minus infinity" for running maxi
 // exponent reference by this much (base 2), so the exponentials stay below 2^8 = 256.
 constexpr float kLazyRescale = 8.f;
 constexpr size_t kHeaderBytes = 256;  // error word + padding at the workspace start
+constexpr int kCacheLine = 128;        // bytes per vector L1 / L2 cache line
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -350,6 +351,7 @@ struct SplitArgs {
     const void *k_new, *v_new;
     int32_t *lens_copy, *err;
     int row_bytes;
+    int shared_lines;  // cache rows do not sit on whole cache lines of their own
     // for the combine: per unit, the workgroups holding its first and its last row
     int2 *unit_wg;
     int dv;  // output row length (the partial rows' stride)
@@ -1431,9 +1433,12 @@ __device__ __forceinline__ void walk_segments(const SplitArgs &a, SegFn &&seg) {
                 reinterpret_cast<uint4 *>(dst)[t % n16] = x;
             }
             __syncthreads();
-            // a row shorter than a cache line shares its line with the previous row, which
-            // another workgroup on this CU may hold, stale, in the vector L1: drop it
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            // A row that does not fill whole cache lines shares a line with the previous row,
+            // which another workgroup on this CU may hold, stale, in the vector L1: drop it.
+            // Rows of whole lines need nothing: no workgroup reads a new row's lines in this
+            // pass before storing them itself (the agent-scope acquire also costs the whole
+            // workgroup its L2 round trips: 6 us of an 8K-row GQA step).
+            if (a.shared_lines) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
         if (threadIdx.x == 0) {
             int32_t *uw = reinterpret_cast<int32_t *>(a.unit_wg + (wk.k - wk.w));
@@ -1552,9 +1557,9 @@ __global__ __launch_bounds__(kBlock) void decode_step_single_kernel(const SplitA
             reinterpret_cast<uint4 *>(dst)[j] = y;
         }
         __syncthreads();
-        // a 64-byte row shares its cache line with the previous row, which another workgroup on
-        // this CU may hold, stale, in the vector L1: drop it
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // a row shorter than a cache line shares its line with the previous row, which another
+        // workgroup on this CU may hold, stale, in the vector L1: drop it
+        if (a.shared_lines) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     if (S == 1) {  // the whole unit: normalised straight to out
         attend_segment<KV, D, GT>(a, b, kvh, h0, hv, 0, n, 0, true, n);
@@ -2124,6 +2129,8 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
     args.lens_copy = reinterpret_cast<int32_t *>(ws + p.lens_off);
     args.err = err_word ? err_word : reinterpret_cast<int32_t *>(ws);
     args.row_bytes = desc->d_k * elem_size(desc->kv_dtype);
+    args.shared_lines = args.row_bytes % kCacheLine != 0 || reinterpret_cast<uintptr_t>(k_cache) % kCacheLine != 0 ||
+                        reinterpret_cast<uintptr_t>(v_cache) % kCacheLine != 0;
     args.unit_wg = reinterpret_cast<int2 *>(ws + p.unit_off);
     args.dv = desc->d_v;
     args.gt = p.gt;

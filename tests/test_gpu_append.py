@@ -161,3 +161,36 @@ def test_fused_steps_in_a_loop_match_the_oracle(path):
         check_close(out, oracle.decode_f64(c["q"], kh, vh, ln, w.scale), "f32", f"step {t}")
     assert int(lens.item()) == 1024 and da.da_read_device_error(ws) == 0
     assert np.array_equal(oracle._np(kc.cpu()), kh) and np.array_equal(oracle._np(vc.cpu()), vh)
+
+
+@pytest.mark.parametrize("kv,d", [("bf16", 128), ("fp8", 128)])
+def test_fused_step_on_caches_off_cache_line_alignment(kv, d):
+    """Caches whose base is 16-byte but not cache-line aligned (rows then share lines with
+    their neighbours): the fused step must still read the new rows it stores."""
+    lens, h_q, h_kv, cap = [700, 3, 1499, 64], 8, 2, 1500
+    c = make_case(kv, d, h_q, h_kv, lens, cap, 401)
+    desc = da.Desc(len(lens), h_q, h_kv, d, cap, c["q"].dtype, TORCH[kv], workloads._inv_sqrt(d), 37)
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in c.items()}
+
+    def shifted(t):  # the same values at a base 64 bytes past a cache line
+        n = t.numel() * t.element_size()
+        raw = torch.zeros(n + 256, dtype=torch.uint8, device="cuda")
+        off = (-raw.data_ptr()) % 128 + 64
+        view = raw[off:off + n].view(t.dtype).view(t.shape)
+        view.copy_(t)
+        assert view.data_ptr() % 128 == 64 and view.is_contiguous()
+        return view
+
+    kc, vc, ln = shifted(g["kc"]), shifted(g["vc"]), g["lens"].clone()
+    ws = da.Workspace(desc, cap)
+    out = torch.empty(len(lens), h_q, d, device="cuda")
+    da.decode_attn_append_run(desc, g["q"], kc, vc, ln, g["kn"], g["vn"], cap, g["scales"], out, ws)
+    assert da.da_read_device_error(ws) == 0
+    expect = [L + 1 for L in lens]
+    assert ln.cpu().tolist() == expect
+    kh, vh = oracle._np(c["kc"]).copy(), oracle._np(c["vc"]).copy()
+    l0 = np.array(lens, dtype=np.int32)
+    oracle.kv_append(kh, vh, l0, oracle._np(c["kn"]).copy(), oracle._np(c["vn"]).copy())
+    assert np.array_equal(oracle._np(kc.cpu()), kh) and np.array_equal(oracle._np(vc.cpu()), vh)
+    ref = oracle.decode_f64(c["q"], kh, vh, l0, workloads._inv_sqrt(d), kv_scales=c["scales"])
+    check_close(out, ref, kv, "fused step, off-line caches")
