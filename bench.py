@@ -19,11 +19,13 @@ Prints ONE JSON line:
                 reaches ms_per_step)
   step_us_p10_p50_p90 = each step's time on the GPU's clock (from the event before its split
                 kernel to the next step's) at the 10th, 50th and 90th percentile
-  roofline    = the step's dominant kernel, timed with HIP events around it on the stream
-                it runs on: on the split path the split-KV attention kernel (the timed steps
-                call the step in its two-stage form, the partial then the combine entry
-                point, with the events around the first); on the single pass (small
-                problems, one kernel per step) the whole one-call step:
+  roofline    = the step's dominant kernel, timed with HIP events on the stream it runs on:
+                on the split path (two kernels per step) the split-KV attention kernel (the
+                timed steps call the step in its two-stage form, the partial then the
+                combine entry point, with events around the first); where the step is one
+                kernel (the single pass, for small problems) the timed steps are the one-call
+                step the product calls, one event at each step's start, and the kernel's time
+                is the distance between them:
                 algorithmic bytes per launch (the KV rows of every sequence plus q) / mean
                 launch duration, against the 8 TB/s HBM3E peak; `traffic` is
                 the HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, read
@@ -188,7 +190,9 @@ def main() -> int:
 
     w = workloads.WORKLOADS[args.workload]
     if args.const_len:
-        w = w.resized(lens=("const", args.const_len), cap=max(w.cap, args.const_len))
+        # room past the length for the appends of the run (a cache copy takes one per use)
+        room = (args.warmup + 2 * args.steps) + (args.steps if args.graph else 0) + 1 if w.steps else 0
+        w = w.resized(lens=("const", args.const_len), cap=max(w.cap, args.const_len + room))
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     c = workloads.generate(w, poison=False)
@@ -219,8 +223,9 @@ def main() -> int:
     desc = da.Desc(w.B, w.h_q, w.h_kv, w.d, w.cap, workloads.TORCH_DTYPE[w.q_dtype],
                    workloads.TORCH_DTYPE[w.kv_dtype], w.scale, args.block_rows, w.nq, flavour, path)
     plan = da.da_plan(desc, max_len)
-    # the single pass is one kernel per step; the split path two (split kernel, combine)
-    single = plan["path"] == da.PATH_SINGLE
+    # the single pass is one kernel per step; the split path two (split kernel, combine kernel)
+    one_kernel = plan["path"] == da.PATH_SINGLE
+    step_kernel = "decode_step_single_kernel" if one_kernel else split_kernel_name(w, args.flavour)
     q = c["q"].to(dev)
     scales = c["kv_scales"].to(dev) if c["kv_scales"] is not None else None
     lens_init = c["lens_init"].to(dev) if appends else lens_final.to(dev)
@@ -238,18 +243,18 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     def step(i, ev=None):
-        """One step; with events ev = (a, b), a and b bracket its dominant kernel: the whole
-        one-call step on the single pass, the split kernel of the two-stage form otherwise."""
+        """One step. With events ev = (a, b): a is recorded where the step starts; on the split
+        path b follows its split kernel (the two-stage form), while a one-kernel step (the
+        single pass) runs as the product calls it, its kernel's time being the distance to the
+        next step's a (one event per step: each event costs the stream a few microseconds)."""
         kc, vc, lens = slots[i % R]
-        if ev is None or single:
+        if ev is None or one_kernel:
             if ev is not None:
                 ev[0].record(stream)
             if appends:
                 da.decode_attn_append_run(desc, q, kc, vc, lens, k_new, v_new, max_len, scales, out, ws)
             else:
                 da.decode_attn_run(desc, q, kc, vc, lens, max_len, scales, out, ws)
-            if ev is not None:
-                ev[1].record(stream)
             return
         ev[0].record(stream)
         if appends:
@@ -285,7 +290,7 @@ def main() -> int:
     assert da.da_read_device_error(ws) == 0, "device error flagged during the timed steps"
 
     one_call = None
-    if not single:
+    if not one_kernel:
         # the same number of steps in the one-call form the product calls (no events inside a
         # step), to show what the two-stage timed form and its events cost
         o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -333,9 +338,10 @@ def main() -> int:
     kv_bytes = sum(step_kv_bytes(i) for i in timed) / args.steps  # mean over the timed steps
     wall_ms = (t1 - t0) * 1e3 / args.steps
     gpu_ms = start.elapsed_time(end) / args.steps
-    split_ms = [a.elapsed_time(b) for a, b in evs]
     starts = [a for a, _ in evs] + [end]
-    step_sorted = sorted(starts[i].elapsed_time(starts[i + 1]) for i in range(args.steps))
+    step_ms = [starts[i].elapsed_time(starts[i + 1]) for i in range(args.steps)]
+    step_sorted = sorted(step_ms)
+    split_ms = step_ms if one_kernel else [a.elapsed_time(b) for a, b in evs]
     split_ms_mean = sum(split_ms) / len(split_ms)
     split_sorted = sorted(split_ms)
     algo_bytes = kv_bytes + q_bytes
@@ -371,10 +377,11 @@ def main() -> int:
             "sum_lens_first_step": int(lens_first.sum()), "max_len": max_len,
             "appends_per_step": int(appends), "kv_bytes_per_step": round(kv_bytes),
             "rotations": R, "cache_bytes_per_copy": cache_bytes, "flavour": args.flavour,
-            **{k: v for k, v in plan.items() if k != "path"}, "path": "single" if single else "split",
+            **{k: v for k, v in plan.items() if k != "path"},
+            "path": "single" if one_kernel else "split",
         },
         "roofline": {
-            "kernel": "decode_step_single_kernel" if single else split_kernel_name(w, args.flavour),
+            "kernel": step_kernel,
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
