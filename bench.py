@@ -14,26 +14,26 @@ step's.
 
 Prints ONE JSON line:
   value       = KV-cache bytes per step / wall-clock time per step   (GB/s, 1e9 B/s)
-  ms_per_step = wall-clock per step over the timed region, bracketed by synchronisation
+  ms_per_step = wall-clock per step over the timed region, bracketed by synchronisation. The
+                timed steps are the step as the product calls it (decode_attn_append_run or
+                decode_attn_run, one call), except every event_every-th step, which carries
+                the events of `roofline`
   host_issue_us_per_step = host time to issue a step's calls (a step is host-bound when this
                 reaches ms_per_step)
-  step_us_p10_p50_p90 = each step's time on the GPU's clock (from the event before its split
-                kernel to the next step's) at the 10th, 50th and 90th percentile
-  roofline    = the step's dominant kernel, timed with HIP events on the stream it runs on:
-                on the split path (two kernels per step) the split-KV attention kernel (the
-                timed steps call the step in its two-stage form, the partial then the
-                combine entry point, with events around the first); where the step is one
-                kernel (the single pass, for small problems) the timed steps are the one-call
-                step the product calls, one event at each step's start, and the kernel's time
-                is the distance between them:
+  step_us_p10_p50_p90 = a step's time on the GPU's clock (between the starts of consecutive
+                event-carrying steps, per step) at the 10th, 50th and 90th percentile
+  roofline    = the step's dominant kernel, timed with HIP events on the stream it runs on, in
+                every event_every-th timed step: on the split path (two kernels per step) the
+                split-KV attention kernel (that step runs in its two-stage form, the partial
+                then the combine entry point, with the events around the first); where the
+                step is one kernel (the single pass, for small problems) the whole call:
                 algorithmic bytes per launch (the KV rows of every sequence plus q) / mean
                 launch duration, against the 8 TB/s HBM3E peak; `traffic` is
                 the HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, read
                 from the profiles/ summary when it was taken on the current kernel source
   cpu_baseline= the fp64 CPU oracle on the same inputs, full step, host cores
-  one_call_form = split path only: the same number of steps again in the one-call form the
-                product calls (decode_attn_append_run / decode_attn_run, no events inside a
-                step), bracketed by two events
+  one_call_form = split path only: the same number of steps again, every one in the one-call
+                form (no events inside a step), bracketed by two events
   stream_ceiling = the read rate of a plain streaming read (da_stream_read over 2 GiB), and
                 value and roofline.achieved as percentages of it; measured before the warm-up
                 steps, after some 60 ms of untimed streaming that brings the part to steady
@@ -71,6 +71,8 @@ def parse_args():
     p.add_argument("--path", choices=["auto", "split", "single"], default="auto",
                    help="launch path of the one-call step (auto = the library's choice)")
     p.add_argument("--rotations", type=int, default=0, help="cache copies to rotate (0 = auto)")
+    p.add_argument("--event-every", type=int, default=8,
+                   help="events bracket the dominant kernel of every E-th timed step")
     p.add_argument("--graph", action="store_true",
                    help="also time the step replayed from a captured HIP graph (one step per cache copy)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -243,10 +245,10 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     def step(i, ev=None):
-        """One step. With events ev = (a, b): a is recorded where the step starts; on the split
-        path b follows its split kernel (the two-stage form), while a one-kernel step (the
-        single pass) runs as the product calls it, its kernel's time being the distance to the
-        next step's a (one event per step: each event costs the stream a few microseconds)."""
+        """One step, as the product calls it (one call). With events ev = (a, b) they bracket the
+        step's dominant kernel: the whole call on the single pass (one kernel); on the split
+        path the step runs in its two-stage form, the split kernel between a and b, then the
+        combine."""
         kc, vc, lens = slots[i % R]
         if ev is None or one_kernel:
             if ev is not None:
@@ -255,6 +257,8 @@ def main() -> int:
                 da.decode_attn_append_run(desc, q, kc, vc, lens, k_new, v_new, max_len, scales, out, ws)
             else:
                 da.decode_attn_run(desc, q, kc, vc, lens, max_len, scales, out, ws)
+            if ev is not None:
+                ev[1].record(stream)
             return
         ev[0].record(stream)
         if appends:
@@ -275,14 +279,17 @@ def main() -> int:
     torch.cuda.synchronize()
     assert da.da_read_device_error(ws) == 0, "device error flagged during warm-up"
 
-    # per step: start, split kernel done (a step ends where the next one starts)
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
+    # Every E-th timed step carries the events around its dominant kernel (each event costs the
+    # stream a few microseconds: the other steps run as the product calls them, event-free)
+    E = max(1, min(args.event_every, args.steps))
+    sampled = list(range(E - 1, args.steps, E))  # not the first timed step, which follows a sync
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in sampled]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, evs[i // E] if i % E == E - 1 else None)
     end.record(stream)
     t_issued = time.perf_counter()
     torch.cuda.synchronize()
@@ -291,8 +298,8 @@ def main() -> int:
 
     one_call = None
     if not one_kernel:
-        # the same number of steps in the one-call form the product calls (no events inside a
-        # step), to show what the two-stage timed form and its events cost
+        # the same number of steps, every one in the one-call form (no events inside a step),
+        # to show what the event-carrying steps cost
         o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         base = args.warmup + args.steps
         torch.cuda.synchronize()
@@ -338,10 +345,11 @@ def main() -> int:
     kv_bytes = sum(step_kv_bytes(i) for i in timed) / args.steps  # mean over the timed steps
     wall_ms = (t1 - t0) * 1e3 / args.steps
     gpu_ms = start.elapsed_time(end) / args.steps
+    # a step's time on the GPU's clock: between consecutive sampled starts, per step
     starts = [a for a, _ in evs] + [end]
-    step_ms = [starts[i].elapsed_time(starts[i + 1]) for i in range(args.steps)]
-    step_sorted = sorted(step_ms)
-    split_ms = step_ms if one_kernel else [a.elapsed_time(b) for a, b in evs]
+    step_sorted = sorted(starts[j].elapsed_time(starts[j + 1]) / (min(args.steps, sampled[j] + E) - sampled[j])
+                         for j in range(len(sampled)))
+    split_ms = [a.elapsed_time(b) for a, b in evs]
     split_ms_mean = sum(split_ms) / len(split_ms)
     split_sorted = sorted(split_ms)
     algo_bytes = kv_bytes + q_bytes
@@ -363,6 +371,7 @@ def main() -> int:
         "gpu_event_us_per_step": round(gpu_ms * 1e3, 2),
         "host_issue_us_per_step": round((t_issued - t0) * 1e6 / args.steps, 2),
         "step_us_p10_p50_p90": [round(step_sorted[(k * len(step_sorted)) // 10] * 1e3, 2) for k in (1, 5, 9)],
+        "event_every": E,
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
