@@ -301,9 +301,10 @@ __device__ __forceinline__ int64_t unit_rows(int L, int max_len, int nq) {
 __device__ __forceinline__ int64_t wg_start(int64_t w, int64_t T, int64_t N) { return w * T / N; }
 
 // Exclusive prefix over sequences of their rows in all units, s_pre[0..batch]; s_pre[batch] = T.
+// The stored lengths land in s_len, so that the walk reads them from LDS, not from memory again.
 // Needs batch <= kMaxBatch and blockDim.x == kBlock.
 __device__ void sequence_prefix(const int32_t *__restrict__ lens, const Partition &pt, int64_t *s_pre,
-                                int64_t *s_wave) {
+                                int64_t *s_wave, int32_t *s_len) {
     const int per = (pt.batch + kBlock - 1) / kBlock;  // <= kMaxBatch / kBlock
     const int64_t upb = (int64_t)pt.h_kv * pt.tiles;
     int64_t local[kMaxBatch / kBlock];
@@ -312,7 +313,11 @@ __device__ void sequence_prefix(const int32_t *__restrict__ lens, const Partitio
     for (int i = 0; i < kMaxBatch / kBlock; ++i) {
         const int bb = threadIdx.x * per + i;
         local[i] = sum;
-        if (i < per && bb < pt.batch) sum += unit_rows(attended_len(lens[bb], pt.append_cap), pt.max_len, pt.nq) * upb;
+        if (i < per && bb < pt.batch) {
+            const int32_t L = lens[bb];
+            s_len[bb] = L;
+            sum += unit_rows(attended_len(L, pt.append_cap), pt.max_len, pt.nq) * upb;
+        }
     }
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     int64_t incl = sum;
@@ -1313,7 +1318,7 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 // entire unit. Every field is the same in all lanes (scalar registers); copies of a walk
 // advance independently.
 struct SegWalk {
-    const int32_t *lens;
+    const int32_t *lens;  // the stored lengths, in LDS
     const int64_t *pre;  // exclusive prefix of rows per sequence (LDS), pre[batch] = T
     int64_t pos, end, w;
     int b, L, ul, row, upb, g, gt, grp_rows, tiles, append_cap;
@@ -1329,9 +1334,9 @@ struct SegWalk {
     int64_t empty_unit;
 
     // Positions the walk on the workgroup's first segment; pre must hold the prefix.
-    __device__ __forceinline__ void start(const SplitArgs &a, const int64_t *s_pre) {
+    __device__ __forceinline__ void start(const SplitArgs &a, const int64_t *s_pre, const int32_t *s_len) {
         const Partition &pt = a.pt;
-        lens = a.lens;
+        lens = s_len;
         pre = s_pre;
         gt = a.gt;
         grp_rows = a.grp_rows;
@@ -1353,7 +1358,7 @@ struct SegWalk {
                 if (uniform64(s_pre[mid]) <= pos) lo = mid; else hi = mid;
             }
             b = lo;
-            L = attended_len(lens[b], append_cap);
+            L = attended_len(__builtin_amdgcn_readfirstlane(lens[b]), append_cap);
             const int64_t off = pos - uniform64(s_pre[b]);
             ul = (int)(off / L);  // unit within the sequence
             row = (int)(off % L);
@@ -1373,13 +1378,13 @@ struct SegWalk {
         k = (size_t)w + (size_t)b * upb + ul;
         slen = L;
         whole = r0 == 0 && r1 == L;
-        new_row = append_cap > 0 && L != lens[b];
+        new_row = append_cap > 0 && L != __builtin_amdgcn_readfirstlane(lens[b]);
         pos += r1 - r0;
         row = 0;
         if (++ul == upb && pos < end) {
             ul = 0;
             do { ++b; } while (uniform64(pre[b + 1]) == uniform64(pre[b]));  // skip sequences without rows
-            L = attended_len(lens[b], append_cap);
+            L = attended_len(__builtin_amdgcn_readfirstlane(lens[b]), append_cap);
         }
     }
 };
@@ -1388,6 +1393,7 @@ struct SegWalk {
 __device__ __forceinline__ SegWalk first_segment(const SplitArgs &a) {
     __shared__ int64_t s_pre[kMaxBatch + 1];
     __shared__ int64_t s_wave[kWaves];
+    __shared__ int32_t s_len[kMaxBatch];
     if (a.pt.append_cap > 0 && blockIdx.x == 0) {
         // the combine reads the stored lengths from this copy, so that it may update lens
         for (int b = threadIdx.x; b < a.pt.batch; b += kBlock) {
@@ -1396,9 +1402,9 @@ __device__ __forceinline__ SegWalk first_segment(const SplitArgs &a) {
             if (L < 0 || L >= a.pt.append_cap) atomicOr(a.err, DA_DEV_ERR_APPEND_FULL);
         }
     }
-    sequence_prefix(a.lens, a.pt, s_pre, s_wave);
+    sequence_prefix(a.lens, a.pt, s_pre, s_wave, s_len);
     SegWalk wk;
-    wk.start(a, s_pre);
+    wk.start(a, s_pre, s_len);
     return wk;
 }
 
