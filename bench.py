@@ -65,6 +65,8 @@ def parse_args():
                    help="single_head_f32 | mha_bf16 | gqa8_bf16 | mqa_bf16 | gqa8_fp8 | gqa8_int8 | gqa8_mq4_bf16")
     p.add_argument("--const-len", type=int, default=0,
                    help="override: every sequence this long (the 8K/16K/32K sweep)")
+    p.add_argument("--h-q", type=int, default=0, help="override: query heads (a group of h_q / h_kv heads)")
+    p.add_argument("--h-kv", type=int, default=0, help="override: KV heads")
     p.add_argument("--block-rows", type=int, default=0, help="rows per split (0 = library choice)")
     p.add_argument("--flavour", choices=["auto", "vector", "matrix"], default="auto",
                    help="split-kernel flavour (auto = the library's choice)")
@@ -195,6 +197,11 @@ def main() -> int:
         # room past the length for the appends of the run (a cache copy takes one per use)
         room = (args.warmup + 2 * args.steps) + (args.steps if args.graph else 0) + 1 if w.steps else 0
         w = w.resized(lens=("const", args.const_len), cap=max(w.cap, args.const_len + room))
+    if args.h_q or args.h_kv:
+        w = w.resized(h_q=args.h_q or w.h_q, h_kv=args.h_kv or w.h_kv)
+        if w.h_q % w.h_kv:
+            print(f"bench.py: h_q {w.h_q} is not a multiple of h_kv {w.h_kv}", file=sys.stderr)
+            return 2
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     c = workloads.generate(w, poison=False)
@@ -356,8 +363,8 @@ def main() -> int:
     achieved = algo_bytes / (split_ms_mean * 1e-3) / 1e9
     value = kv_bytes / (wall_ms * 1e-3) / 1e9
     traffic = (profiled_traffic(args.workload)
-               if not args.const_len and not args.block_rows and args.flavour == "auto" and args.path == "auto"
-               else None)
+               if not (args.const_len or args.block_rows or args.h_q or args.h_kv) and args.flavour == "auto"
+               and args.path == "auto" else None)
 
     result = {
         "metric": METRIC,
