@@ -107,9 +107,12 @@ __device__ __forceinline__ void widen(const typename Kv<KV>::Vec &v, float *f) {
 // memory. Word 3 = 0x00020000 is the gfx9-family (incl. gfx950) default format.
 // KV rows are streamed exactly once, so they are loaded with the non-temporal hint (cache
 // policy bit 1, "nt"), which keeps them from displacing other lines; measured on MI355X it
-// raises the split kernel's sustained read rate by 5-10 %.
+// raises the split kernel's sustained read rate by 5-10 %. The exception is a load that reads
+// half of a 128-byte line whose other half the next load reads (kLoadCached, see the
+// matrix-core register ring).
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kLoadNonTemporal = 2;
+constexpr int kLoadCached = 0;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -153,13 +156,13 @@ __device__ __forceinline__ void lds_dma16(u32x4_t rsrc, uint32_t voff, uint32_t 
                  : "memory", "m0");
 }
 
-template <typename Vec>
+template <typename Vec, int POLICY = kLoadNonTemporal>
 __device__ __forceinline__ Vec buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     if constexpr (sizeof(Vec) == 16) {
-        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kLoadNonTemporal);
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, POLICY);
         return Vec{x[0], x[1], x[2], x[3]};
     } else {
-        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kLoadNonTemporal);
+        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, POLICY);
         return Vec{x[0], x[1]};
     }
 }
@@ -912,8 +915,17 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
         const bool in_tail = t >= nfull;
         const __amdgpu_buffer_rsrc_t kr_ = in_tail ? krt : krs, vr_ = in_tail ? vrt : vrs;
         const uint32_t koff = (tb + lr) * ROWB + lg * 8 * ESZ;
+        // K in A-operand order reads 64 bytes of each of 16 rows per instruction: the two halves
+        // of a 128-byte line come from consecutive loads (k blocks 2i, 2i+1). Cached, the vector
+        // L1 serves the second half; with the non-temporal hint it goes to the L2 as a request
+        // of its own, and with two workgroups per CU (16 slots) about 2 % of those missed there
+        // and fetched the line again (FETCH_SIZE 1.0145 x the algorithmic bytes on the ragged
+        // GQA step, against 1.0004 cached, which also runs 1.6 % faster). With 32 slots (one
+        // workgroup per CU) the second halves hit the L2 (1.0018) and the hint is kept. V loads
+        // read whole rows and keep it too.
+        constexpr int kKPolicy = GW == 16 ? kLoadCached : kLoadNonTemporal;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kt[kb] = buffer_load<LVec>(kr_, koff + kb * 32 * ESZ, 0);
+        for (int kb = 0; kb < KB; ++kb) kt[kb] = buffer_load<LVec, kKPolicy>(kr_, koff + kb * 32 * ESZ, 0);
         const uint32_t voff = (tb + vrow) * ROWB + vcol * ESZ;
 #pragma unroll
         for (int u = 0; u < VLD; ++u) vt[u] = buffer_load<LVec>(vr_, voff + u * VRPI * ROWB, 0);
