@@ -761,80 +761,60 @@ struct MfmaAttn {
                 o[ht][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bvs[nb], plo[ht], o[ht][nb], 0, 0, 0);
     }
 
-    // Merge the four waves pairwise through LDS ((0,2), (1,3), then (0,1)) and write the
-    // segment's result: s_oo holds 2 * HT*16 rows of kRowO floats (one head's D outputs and a
-    // 16-byte pad, so that the 16 heads of a row-exchange land on distinct banks), s_mm / s_ll
-    // kWaves * HT*16 each.
+    // Merge of the four waves: each puts its (max, sum) and O into its own LDS slot; after one
+    // barrier every thread merges float4 columns of the tile's rows over the four slots by
+    // their log-sum-exp weights (Step II's normalisation over the union of the waves' rows) and
+    // writes them, so the outputs leave from all four waves at once. s_oo holds kWaves * HT*16
+    // rows of kRowO floats (one head's D outputs and a 16-byte pad, so that the 16 heads of a
+    // wave's store land on distinct banks), s_mm / s_ll kWaves * HT*16 each. (The first
+    // version merged pairwise, (0,2), (1,3) then (0,1): four barriers, and wave 0 wrote every
+    // output.)
     static constexpr int kRowO = D + 4;
     __device__ __forceinline__ void finish(const SplitArgs &a, int b, int kvh, int h0, int hv, int slen, size_t k,
                                            bool direct, float vscale, float *s_oo, float *s_mm, float *s_ll) {
         constexpr int HP = HT * 16;
+        constexpr int C4 = D / 4;  // float4 columns of a row
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {  // the lane groups share each head's max: sums add
             lp[ht] = xor32_sum(xor16_sum(lp[ht]));
         }
         __syncthreads();  // every wave is done with the LDS the merge reuses
-        if (lg == 0) {
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) { s_mm[wave * HP + ht * 16 + lr] = m[ht]; s_ll[wave * HP + ht * 16 + lr] = lp[ht]; }
-        }
-        // O^T layout: lane l holds d = nb*16 + 4*(l/16) + i of head ht*16 + l%16
-        auto put_o = [&](int slot) {
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    *reinterpret_cast<f32x4_t *>(&s_oo[(slot * HP + ht * 16 + lr) * kRowO + nb * 16 + 4 * lg]) = o[ht][nb];
-        };
-        // The merged (max, sum) of each head also stay in registers (every lane of the head
-        // computes the same values): the lanes never read back what another lane of their own
-        // wave stored without a barrier in between.
-        float mres[HT], lres[HT];
-        auto merge_o = [&](int slot, int other) {
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                const int head = ht * 16 + lr;
-                const float ms = s_mm[wave * HP + head], mo = s_mm[other * HP + head];
-                const float M = fmaxf(ms, mo);
-                const float fs = __builtin_amdgcn_exp2f(ms - M), fo = __builtin_amdgcn_exp2f(mo - M);
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const f32x4_t x = *reinterpret_cast<const f32x4_t *>(&s_oo[(slot * HP + head) * kRowO + nb * 16 + 4 * lg]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[ht][nb][i] = fmaf(o[ht][nb][i], fs, x[i] * fo);
-                }
-                const float Ls = fmaf(s_ll[wave * HP + head], fs, s_ll[other * HP + head] * fo);
-                mres[ht] = M;
-                lres[ht] = Ls;
-                if (lg == 0) { s_mm[wave * HP + head] = M; s_ll[wave * HP + head] = Ls; }
+        for (int ht = 0; ht < HT; ++ht) {
+            if (lg == 0) {
+                s_mm[wave * HP + ht * 16 + lr] = m[ht];
+                s_ll[wave * HP + ht * 16 + lr] = lp[ht];
             }
-        };
-        __syncthreads();
-        if (wave >= 2) put_o(wave - 2);
-        __syncthreads();
-        if (wave < 2) merge_o(wave, wave + 2);
-        __syncthreads();
-        if (wave == 1) put_o(0);
-        __syncthreads();
-        if (wave == 0) {
-            merge_o(0, 1);
+            // O^T layout: lane l holds d = nb*16 + 4*(l/16) + i of head ht*16 + l%16
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                const int head = ht * 16 + lr;
-                if (head >= hv) continue;
-                const float M = mres[ht], Ls = lres[ht];
+            for (int nb = 0; nb < NB; ++nb)
+                *reinterpret_cast<f32x4_t *>(&s_oo[(wave * HP + ht * 16 + lr) * kRowO + nb * 16 + 4 * lg]) = o[ht][nb];
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < hv * C4; i += kBlock) {
+            const int head = i / C4, c4 = i % C4;
+            float M = s_mm[head];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_mm[w * HP + head]);
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float f = __builtin_amdgcn_exp2f(s_mm[w * HP + head] - M);
+                L = fmaf(s_ll[w * HP + head], f, L);
+                const f32x4_t x = *reinterpret_cast<const f32x4_t *>(&s_oo[(w * HP + head) * kRowO + 4 * c4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(x[e], f, acc[e]);
+            }
+            const f32x4_t v = acc * vscale;
+            if (direct) {
                 const size_t row = query_row(a, b, kvh, h0, head, slen).row;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const f32x4_t v = o[ht][nb] * vscale;
-                    if (direct)
-                        *reinterpret_cast<f32x4_t *>(&a.out[row * D + nb * 16 + 4 * lg]) = v / Ls;
-                    else
-                        *reinterpret_cast<f32x4_t *>(&a.part_o[(k * a.gt + head) * D + nb * 16 + 4 * lg]) = v;
-                }
-                if (!direct && lg == 0) {
+                *reinterpret_cast<f32x4_t *>(&a.out[row * D + 4 * c4]) = v / L;
+            } else {
+                *reinterpret_cast<f32x4_t *>(&a.part_o[(k * a.gt + head) * D + 4 * c4]) = v;
+                if (c4 == 0) {
                     a.part_ml[(k * a.gt + head) * 2 + 0] = M;
-                    a.part_ml[(k * a.gt + head) * 2 + 1] = Ls;
+                    a.part_ml[(k * a.gt + head) * 2 + 1] = L;
                 }
             }
         }
@@ -889,19 +869,23 @@ __device__ __forceinline__ void attend_segment_mfma(const SplitArgs &a, int b, i
     const int lane = at.lane, wave = at.wave, lr = at.lr, lg = at.lg;
     const int vrow = lane / VL, vcol = (lane % VL) * 8;
 
-    __shared__ __align__(16) uint16_t s_v[kWaves][TR * VROW];
-    __shared__ __align__(16) float s_oo[2 * HP * A::kRowO];
+    // the waves' V tiles while streaming, the merge's O slots at the end (finish starts and ends
+    // with a barrier): one array
+    constexpr int kVBytes = kWaves * TR * VROW * 2, kOBytes = kWaves * HP * A::kRowO * 4;
+    __shared__ __align__(16) char s_buf[kVBytes > kOBytes ? kVBytes : kOBytes];
     __shared__ float s_mm[kWaves * HP], s_ll[kWaves * HP];
+    uint16_t *const s_vw = reinterpret_cast<uint16_t *>(s_buf) + wave * TR * VROW;  // this wave's V tile
+    float *const s_oo = reinterpret_cast<float *>(s_buf);
 
     auto process = [&](const LVec (&kt)[KB], const LVec (&vt)[VLD], int t) {
 #pragma unroll
         for (int u = 0; u < VLD; ++u)
-            *reinterpret_cast<uint4 *>(&s_v[wave][(vrow + u * VRPI) * VROW + vcol]) = vt[u];
+            *reinterpret_cast<uint4 *>(&s_vw[(vrow + u * VRPI) * VROW + vcol]) = vt[u];
         bf16x8_t ka[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) ka[kb] = __builtin_bit_cast(bf16x8_t, kt[kb]);
         at.tile(ka, [&](int nb) {
-            return (__attribute__((address_space(3))) uint16_t *)&s_v[wave][0] +
+            return (__attribute__((address_space(3))) uint16_t *)s_vw +
                    (4 * lg + lr / 4) * VROW + nb * 16 + 4 * (lane % 4);
         }, tile_row(t), tile_end(t));
     };
@@ -1861,10 +1845,11 @@ constexpr int kSingleRows = 64;
 constexpr int kFallbackResident = 512; // workgroups planned for when no device is visible
 
 // Workgroups to launch for one split-kernel instantiation on the current device: every CU
-// gets the same number, min(what fits, kBlocksPerCu), cached per (device, kernel). Measured
-// on MI355X (256 CUs), counts that are not a multiple of the CU count leave some CUs with
-// more shares than others and run up to 15 % slower; two 4-wave workgroups per CU stream
-// faster than three.
+// gets the same number, min(what fits, the cap), cached per (device, kernel). Measured on
+// MI355X (256 CUs), counts that are not a multiple of the CU count leave some CUs with more
+// shares than others and run up to 15 % slower; two 4-wave workgroups per CU stream faster
+// than three. The bf16 register ring with 32 slots is capped at one per CU: two (its 255
+// registers fit twice per SIMD) took MQA from 48 to 53 us.
 constexpr int kBlocksPerCu = 2;
 // Compute units of the current device (256 when it cannot be queried).
 int cu_count() {
@@ -1886,13 +1871,13 @@ int cu_count() {
     return cache[dev] = cus;
 }
 
-int resident_workgroups(const void *kernel) {
+int resident_workgroups(const void *kernel, int max_per_cu) {
     static std::mutex mu;
     static std::map<std::pair<int, const void *>, int> cache;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();
-        return kFallbackResident;
+        return kFallbackResident / kBlocksPerCu * max_per_cu;
     }
     std::lock_guard<std::mutex> lock(mu);
     auto it = cache.find({dev, kernel});
@@ -1902,9 +1887,9 @@ int resident_workgroups(const void *kernel) {
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess || cus < 1 ||
         per_cu < 1) {
         (void)hipGetLastError();
-        return kFallbackResident;
+        return kFallbackResident / kBlocksPerCu * max_per_cu;
     }
-    return cache[{dev, kernel}] = cus * std::min(per_cu, kBlocksPerCu);
+    return cache[{dev, kernel}] = cus * std::min(per_cu, max_per_cu);
 }
 
 template <int KV, int D>
@@ -1952,7 +1937,8 @@ int make_plan(const da_desc *d, int max_len, Plan *p, bool single_ok = false) {
     if (d->block_rows) {
         nwg = (rows_max + d->block_rows - 1) / d->block_rows;
     } else {
-        nwg = resident_workgroups(split_kernel_ptr(d->kv_dtype, d->d_k, p->gw, p->mfma));
+        const bool ring32 = p->mfma && p->gw == 32 && d->kv_dtype == DA_BF16;
+        nwg = resident_workgroups(split_kernel_ptr(d->kv_dtype, d->d_k, p->gw, p->mfma), ring32 ? 1 : kBlocksPerCu);
         nwg = std::min<int64_t>(nwg, (rows_max + kMinRowsPerBlock - 1) / kMinRowsPerBlock);
     }
     p->nwg = (int)std::max<int64_t>(1, std::min<int64_t>(nwg, 1 << 20));

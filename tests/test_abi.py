@@ -213,6 +213,16 @@ def test_multi_query_plan_and_limits(lib):
     assert _plan(lib, _desc(h_q=2, h_kv=2, n_queries=2), 100)[2] == 2
     assert _plan(lib, _desc(h_q=32, h_kv=8, n_queries=4), 100)[2] == 16
     assert _plan(lib, _desc(h_q=32, h_kv=1, n_queries=8), 100)[2] == 32  # 256 rows: 8 tiles of 32
+
+
+def test_plan_caps_the_32_slot_register_ring_at_one_workgroup_per_cu(lib):
+    # host-only: with no device the plan assumes 256 CUs; bf16 with 32 slots (MQA, g = 32) gets
+    # one workgroup per CU, 16 slots and the 8-bit stages two
+    mqa = _desc(batch=4, h_q=32, h_kv=1, cap=131072)
+    assert _plan(lib, mqa, 131072)[1:] == (256, 32)
+    assert _plan(lib, _desc(batch=16, h_q=32, h_kv=8, cap=32768), 32768)[1:] == (512, 4)
+    fp8 = _desc(batch=4, h_q=32, h_kv=1, cap=131072, kv_dtype=2)
+    assert _plan(lib, fp8, 131072)[1:] == (512, 32)
     one = _ws_size(lib, _desc(h_q=32, h_kv=8), 1000)[1]
     four = _ws_size(lib, _desc(h_q=32, h_kv=8, n_queries=4), 1000)[1]
     assert four > one > 0
