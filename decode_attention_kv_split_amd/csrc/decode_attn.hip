@@ -1238,63 +1238,53 @@ __device__ __forceinline__ void attend_segment_staged(const SplitArgs &a, int b,
     }
     __builtin_amdgcn_s_waitcnt(0);  // no DMA into the stages is outstanding past this point
 
-    // Merge: lane groups share each head's max (sums add); then waves holding the same head
-    // tile merge through LDS and one wave per head tile writes.
+    // Merge: lane groups share each head's max (sums add); each wave puts its (max, sum) and O
+    // into its own LDS slot (slots 0 and 1 in stage a, 2 and 3 in stage b). After one barrier
+    // every thread merges float4 columns of the tile's rows over the slots of the waves that
+    // hold the row's head tile (waves ht, ht + HT, ...) by their log-sum-exp weights and writes
+    // them, so the outputs leave from all four waves at once. (The first version merged
+    // pairwise: up to four barriers, one wave per head tile writing.)
     lp = xor32_sum(xor16_sum(lp));
     __syncthreads();
-    // [2][16] rows of kRowO floats (a head's D outputs and a 16-byte pad: the 16 heads of a
-    // row exchange fall on distinct banks), reusing stage a
+    // a slot: 16 rows of kRowO floats (a head's D outputs and a 16-byte pad: the 16 heads of a
+    // wave's store fall on distinct banks)
     constexpr int kRowO = D + 4;
-    float *s_oo = reinterpret_cast<float *>(s_a);
+    static_assert(2 * 16 * kRowO * 4 <= 2 * HALF, "two merge slots per stage");
+    auto mslot = [&](int w) { return reinterpret_cast<float *>(w < 2 ? s_a : s_b) + (w % 2) * 16 * kRowO; };
     if (lg == 0) { s_mm[wave][lr] = m; s_ll[wave][lr] = lp; }
-    // O^T layout: lane l holds d = nb*16 + 4*(l/16) + i of head l%16
-    auto put_o = [&](int slot_) {
+    {
+        float *so = mslot(wave);
+        // O^T layout: lane l holds d = nb*16 + 4*(l/16) + i of head l%16
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-            *reinterpret_cast<f32x4_t *>(&s_oo[(slot_ * 16 + lr) * kRowO + nb * 16 + 4 * lg]) = o[nb];
-    };
-    // the merged (max, sum) of this lane's head also stay in registers (no lane reads back
-    // what another lane of its own wave stored without a barrier in between)
-    float mres = 0.f, lres = 0.f;
-    auto merge_o = [&](int slot_, int other) {
-        const float ms = s_mm[wave][lr], mo = s_mm[other][lr];
-        const float M = fmaxf(ms, mo);
-        const float fs = __builtin_amdgcn_exp2f(ms - M), fo = __builtin_amdgcn_exp2f(mo - M);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const f32x4_t x = *reinterpret_cast<const f32x4_t *>(&s_oo[(slot_ * 16 + lr) * kRowO + nb * 16 + 4 * lg]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[nb][i] = fmaf(o[nb][i], fs, x[i] * fo);
-        }
-        const float Ls = fmaf(s_ll[wave][lr], fs, s_ll[other][lr] * fo);
-        mres = M;
-        lres = Ls;
-        if (lg == 0) { s_mm[wave][lr] = M; s_ll[wave][lr] = Ls; }
-    };
-    __syncthreads();
-    if (wave >= 2) put_o(wave - 2);
-    __syncthreads();
-    if (wave < 2) merge_o(wave, wave + 2);
-    if constexpr (HT == 1) {
-        __syncthreads();
-        if (wave == 1) put_o(0);
-        __syncthreads();
-        if (wave == 0) merge_o(0, 1);
+            *reinterpret_cast<f32x4_t *>(&so[lr * kRowO + nb * 16 + 4 * lg]) = o[nb];
     }
-    const int hd = ht * 16 + lr;
-    if (wave < HT && hd < hv) {  // wave ht now holds head tile ht
-        const size_t row = query_row(a, b, kvh, h0, hd, slen).row;
+    __syncthreads();
+    constexpr int C4 = D / 4;  // float4 columns of a row
+    for (int i = threadIdx.x; i < hv * C4; i += kBlock) {
+        const int hd = i / C4, c4 = i % C4;
+        const int t = hd / 16, hr = hd % 16;  // the row's head tile and its row in it
+        float M = s_mm[t][hr];
+        for (int w = t + HT; w < kWaves; w += HT) M = fmaxf(M, s_mm[w][hr]);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        float L = 0.f;
+        for (int w = t; w < kWaves; w += HT) {
+            const float f = __builtin_amdgcn_exp2f(s_mm[w][hr] - M);
+            L = fmaf(s_ll[w][hr], f, L);
+            const f32x4_t x = *reinterpret_cast<const f32x4_t *>(&mslot(w)[hr * kRowO + 4 * c4]);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const f32x4_t v = o[nb] * vscale;
-            if (direct)
-                *reinterpret_cast<f32x4_t *>(&a.out[row * D + nb * 16 + 4 * lg]) = v / lres;
-            else
-                *reinterpret_cast<f32x4_t *>(&a.part_o[(k * a.gt + hd) * D + nb * 16 + 4 * lg]) = v;
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(x[e], f, acc[e]);
         }
-        if (!direct && lg == 0) {
-            a.part_ml[(k * a.gt + hd) * 2 + 0] = mres - kPShift;
-            a.part_ml[(k * a.gt + hd) * 2 + 1] = lres;
+        const f32x4_t v = acc * vscale;
+        if (direct) {
+            const size_t row = query_row(a, b, kvh, h0, hd, slen).row;
+            *reinterpret_cast<f32x4_t *>(&a.out[row * D + 4 * c4]) = v / L;
+        } else {
+            *reinterpret_cast<f32x4_t *>(&a.part_o[(k * a.gt + hd) * D + 4 * c4]) = v;
+            if (c4 == 0) {
+                a.part_ml[(k * a.gt + hd) * 2 + 0] = M - kPShift;
+                a.part_ml[(k * a.gt + hd) * 2 + 1] = L;
+            }
         }
     }
     __syncthreads();  // the LDS arrays are reused by the next segment
