@@ -1616,32 +1616,36 @@ __global__ __launch_bounds__(kBlock) void decode_step_single_kernel(const SplitA
     }
 }
 
-// Merges the segments of every query row by their log-sum-exp weights. Workgroup x takes rows
-// rw * (x % (gt / rw)) .. + rw - 1 of unit u = x / (gt / rw) (a unit's rows share its
-// segments), each row with kCombineBlock / rw threads: segment groups of D / 4 threads, one
-// float4 column each. The last head tile of a group may hold fewer than gt rows (grp_rows,
-// the group's g * nq query rows, need not be a multiple of gt): the rows past it are merged
-// from slots nothing wrote and not stored. skip_single: a unit covered by one workgroup was
-// already written.
+// Merges the segments of every query row by their log-sum-exp weights. Workgroup x takes
+// column slice x % cs (D / cs columns) of rows rw * (x / cs % (gt / rw)) .. + rw - 1 of unit
+// u = x / cs / (gt / rw) (a unit's rows share its segments), each row with kCombineBlock / rw
+// threads: segment groups of D / (4 cs) threads, one float4 column each. Column slices spread a
+// few rows with many segments (MQA: 4 units, 64 segments a row) over enough workgroups. The
+// last head tile of a group may hold fewer than gt rows (grp_rows, the group's g * nq query
+// rows, need not be a multiple of gt): the rows past it are merged from slots nothing wrote and
+// not stored. skip_single: a unit covered by one workgroup was already written.
 // With a fused append (pt.append_cap > 0) the stored lengths come from the split kernel's
 // workspace copy, and the workgroup of head 0 writes each sequence's new length to lens_upd.
 // The unit's segments are those of workgroups unit_wg[u].x .. unit_wg[u].y (slot w + u), which
 // the split kernel recorded; every workgroup in between left a partial for the unit (an empty
 // one if its share holds no rows). The length and that entry are read together, then every
-// segment once: each segment group keeps a running maximum, and the groups merge at the end.
+// segment once: each segment group keeps a running maximum; the groups of a row merge by
+// shuffles within a wave, then the waves of a row through LDS.
 template <int D>
 __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     const int32_t *__restrict__ lens, int32_t *__restrict__ lens_upd, const int2 *__restrict__ unit_wg,
     const float *__restrict__ part_ml, const float *__restrict__ part_o,
-    float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt, int grp_rows, int rw, Partition pt,
-    int skip_single) {
-    constexpr int C4 = D / 4;  // float4 columns of a row
-    constexpr int UN = 8;      // segments a group loads before using them
-    const int tpr = kCombineBlock / rw, sgr = tpr / C4;  // threads and segment groups per row
+    float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt, int grp_rows, int rw, int cs,
+    Partition pt, int skip_single) {
+    constexpr int UN = 8;          // segments a group loads before using them
+    const int cw = D / 4 / cs;     // float4 columns of the slice
+    const int tpr = kCombineBlock / rw, sgr = tpr / cw;  // threads and segment groups per row
     const int per_unit = gt / rw;
-    const int64_t u = blockIdx.x / per_unit;
-    const int hh = (blockIdx.x % per_unit) * rw + threadIdx.x / tpr;  // the thread's row in the unit
-    const int sg = threadIdx.x % tpr / C4, c4 = threadIdx.x % C4;
+    const int xs = blockIdx.x / cs;
+    const int64_t u = xs / per_unit;
+    const int hh = (xs % per_unit) * rw + threadIdx.x / tpr;  // the thread's row in the unit
+    const int sg = threadIdx.x % tpr / cw;
+    const int c4 = (blockIdx.x % cs) * cw + threadIdx.x % cw;  // the thread's float4 column
     const int upb = pt.h_kv * pt.tiles, g = h_q / pt.h_kv;
     const int b = (int)(u / upb), ul = (int)(u % upb), kvh = ul / pt.tiles;
     // the row's query position and head: row hh of the tile is row fr of the group's g * nq
@@ -1650,7 +1654,7 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     float *dst = out + ((size_t)(b * pt.nq + tq) * h_q + h) * D;
     const int L = attended_len(lens[b], pt.append_cap);
     const int2 ww = unit_wg[u];
-    if (lens_upd && ul == 0 && threadIdx.x == 0 && blockIdx.x % per_unit == 0) lens_upd[b] = L;
+    if (lens_upd && ul == 0 && threadIdx.x == 0 && xs % per_unit == 0 && blockIdx.x % cs == 0) lens_upd[b] = L;
     if (unit_rows(L, pt.max_len, pt.nq) == 0) {
         if (sg == 0 && live) reinterpret_cast<float4 *>(dst)[c4] = float4{0.f, 0.f, 0.f, 0.f};
         if (threadIdx.x == 0) atomicOr(err, DA_DEV_ERR_LEN_RANGE);
@@ -1659,29 +1663,25 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     const int wa = ww.x, wb = ww.y;
     if (skip_single && wa == wb) return;
 
-    __shared__ float4 s_acc[kCombineBlock / C4][C4];  // per (row, group)
-    __shared__ float s_m[kCombineBlock / C4], s_l[kCombineBlock / C4];
     float4 acc = {0.f, 0.f, 0.f, 0.f};
     float mrun = kNegBig, ls = 0.f;  // an absent segment is (kNegBig, 0, 0): weight 0 or no effect
     for (int w0 = wa + sg; w0 <= wb; w0 += sgr * UN) {
-        float mj[UN], lj[UN];
+        float2 mlj[UN];
         float4 oj[UN];
 #pragma unroll
         for (int j = 0; j < UN; ++j) {
             const int w = w0 + j * sgr;
-            mj[j] = kNegBig;
-            lj[j] = 0.f;
+            mlj[j] = float2{kNegBig, 0.f};
             oj[j] = float4{0.f, 0.f, 0.f, 0.f};
             if (w <= wb) {
                 const size_t kk = (size_t)(w + u) * gt + hh;
-                mj[j] = part_ml[kk * 2];
-                lj[j] = part_ml[kk * 2 + 1];
+                mlj[j] = reinterpret_cast<const float2 *>(part_ml)[kk];
                 oj[j] = reinterpret_cast<const float4 *>(part_o + kk * D)[c4];
             }
         }
         float mx = mrun;
 #pragma unroll
-        for (int j = 0; j < UN; ++j) mx = fmaxf(mx, mj[j]);
+        for (int j = 0; j < UN; ++j) mx = fmaxf(mx, mlj[j].x);
         const float r = __builtin_amdgcn_exp2f(mrun - mx);
         ls *= r;
         acc.x *= r;
@@ -1690,8 +1690,8 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
         acc.w *= r;
 #pragma unroll
         for (int j = 0; j < UN; ++j) {
-            const float f = __builtin_amdgcn_exp2f(mj[j] - mx);
-            ls = fmaf(lj[j], f, ls);
+            const float f = __builtin_amdgcn_exp2f(mlj[j].x - mx);
+            ls = fmaf(mlj[j].y, f, ls);
             acc.x = fmaf(oj[j].x, f, acc.x);
             acc.y = fmaf(oj[j].y, f, acc.y);
             acc.z = fmaf(oj[j].z, f, acc.z);
@@ -1699,29 +1699,50 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
         }
         mrun = mx;
     }
-    const int grp = threadIdx.x / C4;  // (row, group) slot
-    s_acc[grp][c4] = acc;
-    if (c4 == 0) {
-        s_m[grp] = mrun;
-        s_l[grp] = ls;
-    }
-    __syncthreads();
-    if (sg == 0) {
-        float M = s_m[grp];
-        for (int i = 1; i < sgr; ++i) M = fmaxf(M, s_m[grp + i]);
+    // (M, l, o) of two groups -> their merge, for a partner `off` lanes away
+    auto merge_with = [&](int off) {
+        const float Mo = __shfl_xor(mrun, off), lo = __shfl_xor(ls, off);
+        const float ox = __shfl_xor(acc.x, off), oy = __shfl_xor(acc.y, off);
+        const float oz = __shfl_xor(acc.z, off), ow = __shfl_xor(acc.w, off);
+        const float M = fmaxf(mrun, Mo);
+        const float f = __builtin_amdgcn_exp2f(mrun - M), fo = __builtin_amdgcn_exp2f(Mo - M);
+        ls = fmaf(ls, f, lo * fo);
+        acc = float4{fmaf(acc.x, f, ox * fo), fmaf(acc.y, f, oy * fo), fmaf(acc.z, f, oz * fo), fmaf(acc.w, f, ow * fo)};
+        mrun = M;
+    };
+    // the groups of a row within a wave sit cw, 2 cw, ... lanes apart
+    const int span = tpr < kWave ? tpr : kWave;  // lanes of one row within a wave
+    for (int off = cw; off < span; off *= 2) merge_with(off);
+    __shared__ float4 s_acc[kWaves][kWave];
+    __shared__ float s_m[kWaves], s_l[kWaves];
+    const int wpr = tpr / kWave;  // waves per row (0: several rows per wave, merged already)
+    if (wpr > 1) {
+        const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+        if (lane < cw) {
+            s_acc[wave][lane] = acc;
+            if (lane == 0) { s_m[wave] = mrun; s_l[wave] = ls; }
+        }
+        __syncthreads();
+        if (wave % wpr != 0 || lane >= cw) return;  // the row's first wave finishes it
+        float M = s_m[wave];
+        for (int i = 1; i < wpr; ++i) M = fmaxf(M, s_m[wave + i]);
         float4 x = {0.f, 0.f, 0.f, 0.f};
         float z = 0.f;
-        for (int i = 0; i < sgr; ++i) {
-            const float f = __builtin_amdgcn_exp2f(s_m[grp + i] - M);
-            const float4 y = s_acc[grp + i][c4];
+        for (int i = 0; i < wpr; ++i) {
+            const float f = __builtin_amdgcn_exp2f(s_m[wave + i] - M);
+            const float4 y = s_acc[wave + i][lane];
             x.x = fmaf(y.x, f, x.x);
             x.y = fmaf(y.y, f, x.y);
             x.z = fmaf(y.z, f, x.z);
             x.w = fmaf(y.w, f, x.w);
-            z = fmaf(s_l[grp + i], f, z);
+            z = fmaf(s_l[wave + i], f, z);
         }
-        if (live) reinterpret_cast<float4 *>(dst)[c4] = float4{x.x / z, x.y / z, x.z / z, x.w / z};
+        acc = x;
+        ls = z;
+    } else if (sg != 0) {
+        return;
     }
+    if (live) reinterpret_cast<float4 *>(dst)[c4] = float4{acc.x / ls, acc.y / ls, acc.z / ls, acc.w / ls};
 }
 
 // ------------------------------------------------------------------ host side
@@ -2169,15 +2190,18 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
     // and each segment group keeps at most one load batch (a unit has about nwg / units + 1
     // segments); with 2048 rows over 256 CUs, 4 rows per workgroup took the combine from 6.5
     // to 4.5 us, while fewer than two workgroups per CU were slower
+    // Too few rows for that (a few units of many segments): column slices instead, down to a
+    // quarter row (8 threads per segment group), until the workgroups fill every CU twice.
     const int64_t units = (int64_t)desc->batch * desc->h_kv * p.tiles;
     const int groups = kCombineBlock / (desc->d_v / 4);  // segment groups of a workgroup
     const int64_t segs = p.nwg / units + 1;
     const int64_t min_wg = 2 * (int64_t)cu_count();
-    int rw = 1;
+    int rw = 1, cs = 1;
     while (2 * rw <= groups && p.gt % (2 * rw) == 0 && 2 * rw * segs <= 8 * groups &&
            units * (p.gt / (2 * rw)) >= min_wg)
         rw *= 2;
-    const dim3 grid((unsigned)(units * (p.gt / rw)));
+    while (rw == 1 && 2 * cs <= 4 && units * p.gt * cs < min_wg) cs *= 2;
+    const dim3 grid((unsigned)(units * (p.gt / rw) * cs));
     const Partition pt = partition_of(desc, p, max_len, append);
     // appending: stored lengths from the split kernel's copy, new lengths written to lens
     const int32_t *lsrc = append ? reinterpret_cast<const int32_t *>(ws + p.lens_off) : lens;
@@ -2185,10 +2209,10 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (desc->d_v == 64)
         hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, ml, po, out, err,
-                           desc->h_q, p.gt, group_rows(desc), rw, pt, skip_single);
+                           desc->h_q, p.gt, group_rows(desc), rw, cs, pt, skip_single);
     else
         hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, ml, po, out, err,
-                           desc->h_q, p.gt, group_rows(desc), rw, pt, skip_single);
+                           desc->h_q, p.gt, group_rows(desc), rw, cs, pt, skip_single);
     return launch_status("lse_combine_kernel");
 }
 
