@@ -1713,8 +1713,9 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     // the groups of a row within a wave sit cw, 2 cw, ... lanes apart
     const int span = tpr < kWave ? tpr : kWave;  // lanes of one row within a wave
     for (int off = cw; off < span; off *= 2) merge_with(off);
-    __shared__ float4 s_acc[kWaves][kWave];
-    __shared__ float s_m[kWaves], s_l[kWaves];
+    constexpr int kCombineWaves = kCombineBlock / kWave;
+    __shared__ float4 s_acc[kCombineWaves][kWave];
+    __shared__ float s_m[kCombineWaves], s_l[kCombineWaves];
     const int wpr = tpr / kWave;  // waves per row (0: several rows per wave, merged already)
     if (wpr > 1) {
         const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -1950,6 +1951,11 @@ int make_plan(const da_desc *d, int max_len, Plan *p, bool single_ok = false) {
     } else {
         const bool ring32 = p->mfma && p->gw == 32 && d->kv_dtype == DA_BF16;
         nwg = resident_workgroups(split_kernel_ptr(d->kv_dtype, d->d_k, p->gw, p->mfma), ring32 ? 1 : kBlocksPerCu);
+        // Vector ALUs with exactly one unit per CU (MHA, 8 x 32 heads on 256 CUs): one workgroup
+        // per unit, so that at full length every unit is one segment written straight to out and
+        // the combine has nothing to merge (MHA step 86.3 -> 84.6 us; on the 8-bit matrix-core
+        // stages the same count was slower for int8 and no faster for fp8).
+        if (!p->mfma && units == cu_count() && nwg > units) nwg = units;
         nwg = std::min<int64_t>(nwg, (rows_max + kMinRowsPerBlock - 1) / kMinRowsPerBlock);
     }
     p->nwg = (int)std::max<int64_t>(1, std::min<int64_t>(nwg, 1 << 20));

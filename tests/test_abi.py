@@ -223,6 +223,15 @@ def test_plan_caps_the_32_slot_register_ring_at_one_workgroup_per_cu(lib):
     assert _plan(lib, _desc(batch=16, h_q=32, h_kv=8, cap=32768), 32768)[1:] == (512, 4)
     fp8 = _desc(batch=4, h_q=32, h_kv=1, cap=131072, kv_dtype=2)
     assert _plan(lib, fp8, 131072)[1:] == (512, 32)
+
+
+def test_plan_gives_one_workgroup_per_unit_when_the_vector_alu_units_match_the_cus(lib):
+    # host-only (256 CUs assumed): MHA 8 x 32 heads = 256 units on the vector ALUs -> 256
+    # workgroups, one whole unit each; 255 units keep the default two per CU, and so do the
+    # 256 units of an 8-bit matrix-core workload
+    assert _plan(lib, _desc(batch=8, h_q=32, h_kv=32, cap=4096), 4096)[:2] == (4096, 256)
+    assert _plan(lib, _desc(batch=5, h_q=51, h_kv=51, cap=4096), 4096)[1] == 512
+    assert _plan(lib, _desc(batch=32, h_q=64, h_kv=8, cap=16384, kv_dtype=2), 16384)[1] == 512
     one = _ws_size(lib, _desc(h_q=32, h_kv=8), 1000)[1]
     four = _ws_size(lib, _desc(h_q=32, h_kv=8, n_queries=4), 1000)[1]
     assert four > one > 0
