@@ -1453,8 +1453,9 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a
 
 // Matrix-core flavour (GW = 16 or 32 query-row slots; bf16, fp8 or int8 caches): bf16 streams
 // through the register ring, 8-bit caches through the LDS stages.
-// Register targets: GW = 32 keeps all of the register file (one wave per SIMD); 16 slots are
-// held to 256 registers so that two waves fit per SIMD.
+// Register targets: 16 slots are held to 256 registers so that two waves fit per SIMD; 32 slots
+// may use the whole register file (they come out at 255, and the plan gives that kernel one
+// workgroup per CU in any case: two measured slower).
 template <int GW>
 struct MfmaWaves { static constexpr int kMin = GW == 32 ? 1 : 2; };
 
