@@ -1621,7 +1621,7 @@ __global__ __launch_bounds__(kBlock) void decode_step_single_kernel(const SplitA
 // column slice x % cs (D / cs columns) of rows rw * (x / cs % (gt / rw)) .. + rw - 1 of unit
 // u = x / cs / (gt / rw) (a unit's rows share its segments), each row with kCombineBlock / rw
 // threads: segment groups of D / (4 cs) threads, one float4 column each. Column slices spread a
-// few rows with many segments (MQA: 4 units, 64 segments a row) over enough workgroups. The
+// few rows with many segments (MQA: 4 units, 64 segments a row) over more workgroups. The
 // last head tile of a group may hold fewer than gt rows (grp_rows, the group's g * nq query
 // rows, need not be a multiple of gt): the rows past it are merged from slots nothing wrote and
 // not stored. skip_single: a unit covered by one workgroup was already written.
@@ -2197,8 +2197,9 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
     // and each segment group keeps at most one load batch (a unit has about nwg / units + 1
     // segments); with 2048 rows over 256 CUs, 4 rows per workgroup took the combine from 6.5
     // to 4.5 us, while fewer than two workgroups per CU were slower
-    // Too few rows for that (a few units of many segments): column slices instead, down to a
-    // quarter row (8 threads per segment group), until the workgroups fill every CU twice.
+    // Too few rows for that (a few units of many segments): column slices instead, down to half
+    // a row (16 threads per segment group for d = 128). On MQA (128 rows of 64 segments) halves
+    // took the combine from 6.3 to 4.9 us; quarters (5.3) and eighths (7.1) were slower.
     const int64_t units = (int64_t)desc->batch * desc->h_kv * p.tiles;
     const int groups = kCombineBlock / (desc->d_v / 4);  // segment groups of a workgroup
     const int64_t segs = p.nwg / units + 1;
@@ -2207,7 +2208,7 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
     while (2 * rw <= groups && p.gt % (2 * rw) == 0 && 2 * rw * segs <= 8 * groups &&
            units * (p.gt / (2 * rw)) >= min_wg)
         rw *= 2;
-    while (rw == 1 && 2 * cs <= 4 && units * p.gt * cs < min_wg) cs *= 2;
+    while (rw == 1 && 2 * cs <= 2 && units * p.gt * cs < min_wg) cs *= 2;
     const dim3 grid((unsigned)(units * (p.gt / rw) * cs));
     const Partition pt = partition_of(desc, p, max_len, append);
     // appending: stored lengths from the split kernel's copy, new lengths written to lens
