@@ -68,3 +68,11 @@ def test_code_digest_keeps_comments_and_layout_out():
     assert a == b == 'int a = 1; const char *s = "x // y /* z */";'
     assert build._code_tokens("int a = 2;") != build._code_tokens("int a = 1;")
     assert build._code_tokens("char c = '/'; // x") == "char c = '/';"
+
+
+def test_head_count_override_must_divide_into_groups():
+    # checked before any device is touched
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--h-q", "33"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "not a multiple of h_kv" in r.stderr
