@@ -5,7 +5,9 @@ tests take one at a time: cache type (fp32, bf16, fp8, int8), head dimension (64
 size g (1 to 32, multiples of 4 or not), query rows per sequence T (1 to 8), batch, ragged
 lengths from T to the capacity, rows per workgroup (the library's choice or small shares that
 cut units into many segments), and the one-call or the two-stage form. Each must match the
-oracle within its cache type's tolerance, with no device error; sixty more drive the fused decode step.
+oracle within its cache type's tolerance, with no device error; sixteen more at production-like
+sizes (up to 16 sequences of 32768 rows) use the library's own partition; sixty more drive the
+fused decode step.
 """
 import random
 
@@ -69,6 +71,32 @@ def test_random_configuration(case):
                                   kv_scales=c["kv_scales"])
     got = out if T > 1 else out.unsqueeze(1)
     check_close(got, ref, kv, f"r{i}")
+
+
+def draw_large_cases(n=16, seed=777):
+    """Production-like sizes: up to 16 sequences of up to 32768 rows (4096 for fp32), so that
+    the library's own partition (two workgroups per CU) cuts units into many segments."""
+    rng = random.Random(seed)
+    cases = []
+    for i in range(n):
+        kv = rng.choice(["f32", "bf16", "bf16", "fp8", "int8"])
+        d = rng.choice([64, 128])
+        h_q, h_kv = rng.choice(GROUPS)
+        T = rng.choice([1, 1, 1, 2, 4])
+        B = rng.randint(1, 16)
+        cap = 4096 if kv == "f32" else rng.choice([4096, 16384, 32768])
+        block_rows = rng.choice([0, 0, 0, 4096])
+        two_stage = rng.random() < 0.5
+        cases.append((1000 + i, kv, d, h_q, h_kv, T, B, cap, block_rows, two_stage))
+    return cases
+
+
+LARGE_CASES = draw_large_cases()
+
+
+@pytest.mark.parametrize("case", LARGE_CASES, ids=[f"L{c[0]}" for c in LARGE_CASES])
+def test_random_configuration_large(case):
+    test_random_configuration(case)
 
 
 APPEND_CASES = [c for c in draw_cases(60, seed=4048)]
