@@ -146,8 +146,8 @@ int da_workspace_size(const da_desc *desc, int32_t max_len, size_t *bytes);
 /*
  * Chosen work partition of the one-call entry points for (desc, max_len), all outputs host
  * int32 (any may be NULL): cache rows per workgroup when every sequence has max_len rows,
- * workgroups launched (batch for the single pass), query rows per head tile, and the path
- * taken (DA_PATH_SPLIT or DA_PATH_SINGLE).
+ * workgroups launched (for the single pass: batch * h_kv * head tiles * splits), query rows
+ * per head tile, and the path taken (DA_PATH_SPLIT or DA_PATH_SINGLE).
  */
 int da_plan(const da_desc *desc, int32_t max_len, int32_t *rows_per_block, int32_t *n_blocks,
             int32_t *heads_per_block, int32_t *path);
