@@ -303,7 +303,8 @@ __device__ __forceinline__ int64_t unit_rows(int L, int max_len, int nq) {
 }
 __device__ __forceinline__ int64_t wg_start(int64_t w, int64_t T, int64_t N) { return w * T / N; }
 
-// Exclusive prefix over sequences of their rows in all units, s_pre[0..batch]; s_pre[batch] = T.
+// Exclusive prefix over sequences of their rows in all units, s_pre[0..batch]; s_pre[batch] = T,
+// for batches of more than one wave's lanes (smaller ones keep it in registers, in SegWalk).
 // The stored lengths land in s_len, so that the walk reads them from LDS, not from memory again.
 // Needs batch <= kMaxBatch and blockDim.x == kBlock.
 __device__ void sequence_prefix(const int32_t *__restrict__ lens, const Partition &pt, int64_t *s_pre,
@@ -1299,15 +1300,26 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// The same 64-bit value from lane `lane` (uniform) of every lane.
+__device__ __forceinline__ int64_t lane_value64(int64_t x, int lane) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)x, lane);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)x >> 32), lane);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // The segments of one workgroup, in order: rows [r0, r1) of (sequence sb, KV head kvh) for
 // the hv query rows h0 .. h0+hv-1 of a head tile, partial slot k, whole = the segment is the
-// entire unit. Every field is the same in all lanes (scalar registers); copies of a walk
-// advance independently.
+// entire unit. Every field but lane_len is the same in all lanes (scalar registers); copies of
+// a walk advance independently.
+// The walk finds its first row by the prefix over sequences of their rows; after that it needs
+// only the stored lengths (a sequence has rows iff unit_rows of its length is non-zero). A batch
+// of at most kWave sequences is held in lanes: every wave loads the lengths (lane b: sequence b)
+// and scans them itself, with no LDS and no barrier; a larger one goes through LDS.
 struct SegWalk {
-    const int32_t *lens;  // the stored lengths, in LDS
-    const int64_t *pre;  // exclusive prefix of rows per sequence (LDS), pre[batch] = T
+    const int32_t *lens;  // the stored lengths in LDS, or null: lane_len holds them
+    int32_t lane_len;     // lens[lane] in lanes < batch (a per-lane value)
     int64_t pos, end, w;
-    int b, L, ul, row, upb, g, gt, grp_rows, tiles, append_cap;
+    int b, L, stored, ul, row, upb, g, gt, grp_rows, tiles, append_cap, max_len, nq;
     bool has;  // a current segment
     int sb, kvh, h0, hv, r0, r1;
     int slen;      // rows of the segment's sequence (the walk state moves on past them)
@@ -1319,36 +1331,76 @@ struct SegWalk {
     // every workgroup between the unit's first and last, so this one leaves an empty partial.
     int64_t empty_unit;
 
-    // Positions the walk on the workgroup's first segment; pre must hold the prefix.
-    __device__ __forceinline__ void start(const SplitArgs &a, const int64_t *s_pre, const int32_t *s_len) {
+    __device__ __forceinline__ int stored_len(int i) const {
+        return lens ? __builtin_amdgcn_readfirstlane(lens[i]) : __builtin_amdgcn_readlane(lane_len, i);
+    }
+    __device__ __forceinline__ void init(const SplitArgs &a) {
         const Partition &pt = a.pt;
-        lens = s_len;
-        pre = s_pre;
         gt = a.gt;
         grp_rows = a.grp_rows;
         tiles = pt.tiles;
         upb = pt.h_kv * pt.tiles;
         g = a.h_q / pt.h_kv;
         append_cap = pt.append_cap;
-        const int64_t Tot = uniform64(s_pre[pt.batch]), N = pt.nwg;
+        max_len = pt.max_len;
+        nq = pt.nq;
         w = blockIdx.x;
+        b = 0, L = 1, stored = 0, ul = 0, row = 0;
+        empty_unit = -1;
+    }
+    // Row `pos` lies in sequence b0, whose rows start at position pre_b (b0 has rows).
+    __device__ __forceinline__ void locate(int b0, int64_t pre_b) {
+        b = b0;
+        stored = stored_len(b);
+        L = attended_len(stored, append_cap);
+        const int64_t off = pos - pre_b;
+        ul = (int)(off / L);  // unit within the sequence
+        row = (int)(off % L);
+        if (pos == end && row > 0) empty_unit = (int64_t)b * upb + ul;
+    }
+    // Positions the walk on the workgroup's first segment; s_pre must hold the prefix and
+    // s_len the stored lengths.
+    __device__ __forceinline__ void start(const SplitArgs &a, const int64_t *s_pre, const int32_t *s_len) {
+        init(a);
+        lens = s_len;
+        const int64_t Tot = uniform64(s_pre[a.pt.batch]), N = a.pt.nwg;
         pos = wg_start(w, Tot, N);
         end = wg_start(w + 1, Tot, N);
-        b = 0, L = 1, ul = 0, row = 0;
-        empty_unit = -1;
         if (pos < Tot) {
             // the sequence holding row `pos`: the last b with pre[b] <= pos (it has rows)
-            int lo = 0, hi = pt.batch;  // invariant: pre[lo] <= pos < pre[hi]
+            int lo = 0, hi = a.pt.batch;  // invariant: pre[lo] <= pos < pre[hi]
             while (hi - lo > 1) {
                 const int mid = (lo + hi) / 2;
                 if (uniform64(s_pre[mid]) <= pos) lo = mid; else hi = mid;
             }
-            b = lo;
-            L = attended_len(__builtin_amdgcn_readfirstlane(lens[b]), append_cap);
-            const int64_t off = pos - uniform64(s_pre[b]);
-            ul = (int)(off / L);  // unit within the sequence
-            row = (int)(off % L);
-            if (pos == end && row > 0) empty_unit = (int64_t)b * upb + ul;
+            locate(lo, uniform64(s_pre[lo]));
+        }
+        next();
+    }
+    // The same for a batch of at most kWave sequences, from the lengths in memory.
+    __device__ __forceinline__ void start_in_lanes(const SplitArgs &a) {
+        init(a);
+        lens = nullptr;
+        const Partition &pt = a.pt;
+        const int lane = threadIdx.x % kWave;
+        lane_len = lane < pt.batch ? a.lens[lane] : 0;
+        const int64_t own =
+            lane < pt.batch ? unit_rows(attended_len(lane_len, append_cap), max_len, nq) * upb : 0;
+        int64_t incl = own;
+#pragma unroll
+        for (int off = 1; off < kWave; off *= 2) {
+            const int64_t y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+        }
+        const int64_t excl = incl - own;
+        const int64_t Tot = lane_value64(incl, kWave - 1), N = pt.nwg;
+        pos = wg_start(w, Tot, N);
+        end = wg_start(w + 1, Tot, N);
+        if (pos < Tot) {
+            // the lanes with pre[b] <= pos are a prefix (lane 0 among them): the last one
+            const uint64_t m = __ballot(excl <= pos);
+            const int b0 = 63 - __builtin_clzll(m);
+            locate(b0, lane_value64(excl, b0));
         }
         next();
     }
@@ -1364,18 +1416,22 @@ struct SegWalk {
         k = (size_t)w + (size_t)b * upb + ul;
         slen = L;
         whole = r0 == 0 && r1 == L;
-        new_row = append_cap > 0 && L != __builtin_amdgcn_readfirstlane(lens[b]);
+        new_row = append_cap > 0 && L != stored;
         pos += r1 - r0;
         row = 0;
         if (++ul == upb && pos < end) {
             ul = 0;
-            do { ++b; } while (uniform64(pre[b + 1]) == uniform64(pre[b]));  // skip sequences without rows
-            L = attended_len(__builtin_amdgcn_readfirstlane(lens[b]), append_cap);
+            do {  // skip sequences without rows
+                ++b;
+                stored = stored_len(b);
+                L = attended_len(stored, append_cap);
+            } while (unit_rows(L, max_len, nq) == 0);
         }
     }
 };
 
-// Computes the sequence prefix in LDS and returns the walk on the workgroup's first segment.
+// Computes the sequence prefix (in lanes, or in LDS) and returns the walk on the workgroup's
+// first segment.
 __device__ __forceinline__ SegWalk first_segment(const SplitArgs &a) {
     __shared__ int64_t s_pre[kMaxBatch + 1];
     __shared__ int64_t s_wave[kWaves];
@@ -1388,9 +1444,13 @@ __device__ __forceinline__ SegWalk first_segment(const SplitArgs &a) {
             if (L < 0 || L >= a.pt.append_cap) atomicOr(a.err, DA_DEV_ERR_APPEND_FULL);
         }
     }
-    sequence_prefix(a.lens, a.pt, s_pre, s_wave, s_len);
     SegWalk wk;
-    wk.start(a, s_pre, s_len);
+    if (a.pt.batch <= kWave) {
+        wk.start_in_lanes(a);
+    } else {
+        sequence_prefix(a.lens, a.pt, s_pre, s_wave, s_len);
+        wk.start(a, s_pre, s_len);
+    }
     return wk;
 }
 

@@ -247,6 +247,34 @@ def test_invalid_lengths_between_valid_ones(path):
     check_close(o[[0, 3]], ref[[0, 3]], "bf16")
 
 
+@pytest.mark.parametrize("B", [64, 65])
+@pytest.mark.parametrize("h_q", [8, 2])  # g = 4: matrix cores; g = 1: vector ALUs
+def test_batch_at_the_edge_of_one_wave(B, h_q):
+    """64 sequences are the most that a wave holds one per lane (the prefix over lengths in
+    registers); 65 go through LDS. Shares of 37 rows cross many sequences, and sequences
+    without rows (length 0, or above max_len) lie between valid ones and at the end, so the
+    walk skips them in both forms."""
+    w = W(B=B, h_q=h_q, h_kv=2, d=64, cap=200, lens=("uniform", 1, 150), seed=300 + B + h_q)
+    c = workloads.generate(w)
+    lens = c["lens_final"].clone()
+    lens[::7] = 0
+    lens[3::11] = 190  # above max_len = 150
+    lens[-2:] = 0
+    valid = (lens >= 1) & (lens <= 150)
+    desc = desc_of(w, 37, da.PATH_SPLIT)
+    g = to_gpu(c)
+    ws = da.Workspace(desc, 150)
+    out = torch.full((w.B, w.h_q, w.d), 3.0, device="cuda")
+    log(f"case batch {B} h_q={h_q} with empty sequences")
+    da.decode_attn_run(desc, g["q"], g["k_cache"], g["v_cache"], lens.cuda(), 150, None, out, ws)
+    assert da.da_read_device_error(ws) == da.DEV_ERR_LEN_RANGE
+    o = out.cpu()
+    assert torch.equal(o[~valid], torch.zeros(int((~valid).sum()), w.h_q, w.d))
+    ref = oracle_out(w, c, lens=torch.where(valid, lens, torch.ones_like(lens)))
+    idx = valid.nonzero().flatten()
+    check_close(o[idx], ref[idx.numpy()], "bf16", f"B={B} h_q={h_q}")
+
+
 def test_single_row_returns_that_value_row_exactly():
     """I1: with one row the softmax weight is 1 and out equals the V row (bf16 widened)."""
     w = W(B=4, h_q=8, h_kv=2, cap=300, lens=("const", 1))
