@@ -99,6 +99,33 @@ def test_random_configuration_large(case):
     test_random_configuration(case)
 
 
+def draw_wide_cases(n=12, seed=4242, first=3000):
+    """Batches around and beyond one wave's 64 lanes (up to 64 sequences the split kernel finds
+    its first row from lengths held one per lane, beyond that through LDS; past 256 each thread
+    of the workgroup takes several), with short caches so that the oracle stays quick."""
+    rng = random.Random(seed)
+    cases = []
+    for i in range(n):
+        kv = rng.choice(["f32", "bf16", "bf16", "fp8", "int8"])
+        d = rng.choice([64, 128])
+        h_q, h_kv = rng.choice(GROUPS)
+        T = rng.choice([1, 1, 2])
+        B = rng.choice([63, 64, 65, 96, 257, 300])
+        cap = rng.choice([64, 300])
+        block_rows = rng.choice([0, 0, 17])
+        two_stage = rng.random() < 0.5
+        cases.append((first + i, kv, d, h_q, h_kv, T, B, cap, block_rows, two_stage))
+    return cases
+
+
+WIDE_CASES = draw_wide_cases()
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=[f"W{c[0]}" for c in WIDE_CASES])
+def test_random_configuration_wide_batch(case):
+    test_random_configuration(case)
+
+
 APPEND_CASES = [c for c in draw_cases(60, seed=4048)]
 
 
@@ -136,3 +163,11 @@ def test_random_fused_step(case):
         assert np.array_equal(oracle._np(g["v_cache"][b, :, :L].cpu()), vh[b, :, :L])
     ref = oracle.decode_f64(c["q"], kh, vh, lh, w.scale, kv_scales=c["kv_scales"])
     check_close(out, ref, kv, f"a{i}")
+
+
+WIDE_APPEND_CASES = draw_wide_cases(8, seed=4343, first=3100)
+
+
+@pytest.mark.parametrize("case", WIDE_APPEND_CASES, ids=[f"wa{c[0]}" for c in WIDE_APPEND_CASES])
+def test_random_fused_step_wide_batch(case):
+    test_random_fused_step(case)
