@@ -7,21 +7,25 @@
 // lets every query head of a group select the group's KV rows instead of a copy.
 //
 // MI355X mapping (CDNA4, wave64):
-//   * The cache rows of one (sequence, KV head) are cut into splits of `chunk` rows; one
-//     256-thread workgroup handles one split for GT query heads of the group. The grid is
-//     (splits at max_len, h_kv * g / GT, batch); splits past a sequence's end exit at once.
-//   * Lanes span the head dimension (the page's coalescing criterion, §4: adjacent lanes
-//     touch adjacent addresses): LPR lanes cover one row with one 8- or 16-byte load each,
-//     so a wave loads 64 / LPR whole rows per instruction, fully coalesced.
-//   * Each K and V row is loaded once into registers and used by all GT heads of the
-//     group: KV bytes are read once per workgroup, not once per query head.
-//   * The LPR partial dot products of a row are summed with DPP row permutes (no LDS).
-//   * Softmax runs online in fp32 in the base-2 domain (scale * log2 e folded into the
-//     score scale, v_exp_f32 for 2^x); each row group of a wave keeps its own running max,
-//     sum and output, merged at the end of the split, then the four waves merge in LDS.
-//   * Each split writes (max, sum, unnormalised output) per head; the combine kernel merges
-//     splits by log-sum-exp weights. No atomics touch the output, so results are
-//     deterministic run to run.
+//   * Work partition: a unit is (sequence, KV head, head tile of at most 32 of the group's
+//     query rows); the rows of all units, concatenated, are cut into equal shares, one per
+//     256-thread workgroup, with every workgroup resident (one or two per CU), whatever the
+//     length mix. A share cut at unit boundaries gives segments; each segment leaves (max, sum,
+//     unnormalised rows) in a partial slot of its own, and the combine kernel merges a unit's
+//     segments by their log-sum-exp weights.
+//   * Each K and V row is loaded once per head tile and used by all its query rows (the
+//     group's g heads at each query position), so KV bytes are read once per group while the
+//     group has at most 32 query rows.
+//   * Three segment flavours: the vector ALUs (fp32 caches and groups of one or two rows:
+//     lanes span the head dimension, coalesced row loads, DPP row sums); the matrix cores with
+//     a register ring (bf16: K loaded in A-operand order, V through a per-wave LDS tile read
+//     back transposed); the matrix cores with LDS stages filled by DMA (fp8 and int8 codes,
+//     widened exactly in registers).
+//   * Softmax runs online in fp32 in the base-2 domain (scale * log2 e folded into the score
+//     scale, v_exp_f32 for 2^x); the waves of a workgroup merge through LDS at a segment's end.
+//   * For latency-bound problems a single-pass kernel does it in one launch: the splits of a
+//     unit count their arrivals and the last one merges them.
+//   * No atomics touch the outputs, so results are deterministic run to run.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -605,7 +609,7 @@ __device__ __forceinline__ void attend_segment(const SplitArgs &a, int b, int kv
     __syncthreads();  // the LDS arrays are reused by the next segment
 }
 
-// ------------------------------------------------------------------ MFMA flavour (g a multiple of 4)
+// ------------------------------------------------------------------ MFMA flavour (groups of 3 or more query rows)
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
@@ -1514,8 +1518,9 @@ __global__ __launch_bounds__(kBlock) void split_kv_attn_kernel(const SplitArgs a
 // Matrix-core flavour (GW = 16 or 32 query-row slots; bf16, fp8 or int8 caches): bf16 streams
 // through the register ring, 8-bit caches through the LDS stages.
 // Register targets: 16 slots are held to 256 registers so that two waves fit per SIMD; 32 slots
-// may use the whole register file (they come out at 255, and the plan gives that kernel one
-// workgroup per CU in any case: two measured slower).
+// may use the whole register file (d = 128 bf16 comes out at 256 vector registers and a few
+// accumulation registers, one wave per SIMD; the plan gives that kernel one workgroup per CU in
+// any case: two measured slower).
 template <int GW>
 struct MfmaWaves { static constexpr int kMin = GW == 32 ? 1 : 2; };
 
@@ -1860,9 +1865,12 @@ int validate(const da_desc *d) {
 int n_queries(const da_desc *d) { return d->n_queries > 1 ? d->n_queries : 1; }
 int group_rows(const da_desc *d) { return d->h_q / d->h_kv * n_queries(d); }
 
-// Workspace layout: [error word, padded to 256 B][segment (max, sum) pairs,
-// (N + units) * GT * 2 fp32][segment output rows, (N + units) * GT * d_v fp32], each section
-// starting on a 256-byte boundary (N workgroups, units = batch * h_kv * head tiles).
+// Workspace layout, each section starting on a 256-byte boundary: [error word, padded to
+// 256 B][copy of the stored lengths, batch int32 (fused append)][the single pass's arrival
+// counters, batch + its units int32][per unit, its first and last workgroup, int2][partial
+// (max, sum) pairs, 2 fp32 a row][partial output rows, d_v fp32 a row]. The partial arrays
+// hold (N + units) * GT rows for the split path (N workgroups, units = batch * h_kv * head
+// tiles), or the single pass's units * nsplit * GT, whichever is larger.
 struct Plan {
     int gt;     // query rows per head tile (the last tile of a group may hold fewer)
     int gw;     // the kernel's query-row slots, >= gt (slots past a tile's rows are padding)
@@ -1876,7 +1884,7 @@ struct Plan {
     int nsplit;      // single pass: splits per unit
     size_t cnt_off;  // single pass: arrival counters, per sequence then per unit
     size_t ncnt;     // single pass: counters (batch + units)
-    // workspace: header, lengths copy, per-unit first / last workgroup, (max, sum), rows
+    // workspace offsets: lengths copy, per-unit first / last workgroup, (max, sum), rows; total
     size_t lens_off, unit_off, ml_off, o_off, bytes;
 };
 
@@ -1921,8 +1929,8 @@ constexpr int kFallbackResident = 512; // workgroups planned for when no device 
 // gets the same number, min(what fits, the cap), cached per (device, kernel). Measured on
 // MI355X (256 CUs), counts that are not a multiple of the CU count leave some CUs with more
 // shares than others and run up to 15 % slower; two 4-wave workgroups per CU stream faster
-// than three. The bf16 register ring with 32 slots is capped at one per CU: two (its 255
-// registers fit twice per SIMD) took MQA from 48 to 53 us.
+// than three. The bf16 register ring with 32 slots is capped at one per CU: two (the ring held
+// to 252 registers, so that two fit per SIMD) took MQA from 48 to 53 us.
 constexpr int kBlocksPerCu = 2;
 // Compute units of the current device (256 when it cannot be queried).
 int cu_count() {
