@@ -76,3 +76,15 @@ def test_head_count_override_must_divide_into_groups():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "not a multiple of h_kv" in r.stderr
+
+
+def test_cpu_baseline_fills_its_budget_with_whole_passes():
+    """A batch the oracle finishes well inside the budget is timed over repeated passes of the
+    same step, so the baseline rests on about the budget's worth of CPU work."""
+    import workloads
+    w = workloads.WORKLOADS["gqa8_bf16"].resized(B=2, lens=("const", 64), cap=64, steps=0)
+    kv_bytes = 2 * 64 * w.h_kv * 2 * w.d * 2
+    r = bench.cpu_baseline(w, 0.3, kv_bytes)
+    assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
+    assert r["passes"] > 1 and f"{r['passes']} passes" in r["sample"]
+    assert float(r["sample"].rsplit(", ", 1)[1].rstrip(" s")) >= 0.15
