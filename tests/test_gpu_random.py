@@ -171,3 +171,11 @@ WIDE_APPEND_CASES = draw_wide_cases(8, seed=4343, first=3100)
 @pytest.mark.parametrize("case", WIDE_APPEND_CASES, ids=[f"wa{c[0]}" for c in WIDE_APPEND_CASES])
 def test_random_fused_step_wide_batch(case):
     test_random_fused_step(case)
+
+
+@pytest.mark.parametrize("two_stage", [False, True])
+def test_fused_step_largest_batch(two_stage):
+    """The fused step at the largest batch one call takes (1024 sequences: the prefix over
+    lengths through LDS, four sequences per thread, and the copy of the stored lengths that the
+    combine reads), appends bit-exact and the output within tolerance of the oracle."""
+    test_random_fused_step((3200 + int(two_stage), "bf16", 64, 8, 2, 1, 1024, 64, 0, two_stage))
