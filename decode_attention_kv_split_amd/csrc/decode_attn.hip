@@ -152,7 +152,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // reads with explicit vmcnt waits and barriers instead. The compiler does not look inside
 // the assembly for hazards, so it keeps the wait states itself: five before (a vector
 // instruction that wrote one of the resource's scalar registers), one between the write of
-// M0 and the DMA that reads it.
+// M0 and the DMA that reads it. M0 is a register the compiler reserves, so it warns that the
+// clobber may not be honoured (no save or restore around the statement). That is safe here
+// only because nothing else in the device code uses M0: in the gfx950 assembly of this file
+// every M0 access is one of these statements' own s_mov_b32 (no GPR indexing, s_movrel,
+// message or LDS-DMA builtin). Code that adds such a use must not keep M0 live across this.
 __device__ __forceinline__ void lds_dma16(u32x4_t rsrc, uint32_t voff, uint32_t lds) {
     asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                  :
