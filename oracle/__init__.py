@@ -55,6 +55,10 @@ def _open(path: str):
     lib.oracle_decode_f64_traced.restype = I
     lib.oracle_decode_multi_f64.argtypes = [I] * 9 + [F] + [P] * 6 + [I]
     lib.oracle_decode_multi_f64.restype = I
+    lib.oracle_decode_lse_f64.argtypes = [I] * 9 + [F] + [P] * 7 + [I]
+    lib.oracle_decode_lse_f64.restype = I
+    lib.oracle_merge_lse_f64.argtypes = [I, ctypes.c_long, I, P, P, P, P]
+    lib.oracle_merge_lse_f64.restype = None
     lib.oracle_kv_append.argtypes = [I] * 6 + [P] * 5
     lib.oracle_kv_append.restype = I
     return lib
@@ -193,6 +197,48 @@ def decode_multi_f64(q, k_cache, v_cache, lens, scale: float, kv_scales=None, nt
     if rc:
         raise ValueError(f"oracle_decode_multi_f64 failed ({rc})")
     return out
+
+
+def decode_lse_f64(q, k_cache, v_cache, lens, scale: float, kv_scales=None, nthreads: int = 0):
+    """Decode attention over one shard of the rows, with each query row's log-sum-exp
+    ln sum_l exp(s[l]) (natural log). q [B, h_q, d_k] or [B, T, h_q, d_k] (T query rows,
+    causal over this cache's rows); lens[b] = 0 allowed (out 0, lse -inf).
+    Returns (out [..., d_v], lse [...]) float64, shaped like q."""
+    q, k_cache, v_cache, lens, kv_scales = map(_np, (q, k_cache, v_cache, lens, kv_scales))
+    q, k_cache, v_cache = (np.ascontiguousarray(a) for a in (q, k_cache, v_cache))
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    single = q.ndim == 3
+    q4 = q[:, None] if single else q
+    q4 = np.ascontiguousarray(q4)
+    B, T, h_q, d_k = q4.shape
+    _, h_kv, cap, _ = k_cache.shape
+    d_v = v_cache.shape[3]
+    if kv_scales is not None:
+        kv_scales = np.ascontiguousarray(kv_scales, dtype=np.float32)
+    out = np.zeros((B, T, h_q, d_v), dtype=np.float64)
+    lse = np.zeros((B, T, h_q), dtype=np.float64)
+    rc = _load().oracle_decode_lse_f64(
+        B, T, h_q, h_kv, d_k, d_v, cap, _dtype_code(q4), _dtype_code(k_cache),
+        float(np.float32(scale)), _ptr(q4), _ptr(k_cache), _ptr(v_cache), _ptr(lens),
+        _ptr(kv_scales), _ptr(out), _ptr(lse), int(nthreads))
+    if rc:
+        raise ValueError(f"oracle_decode_lse_f64 failed ({rc})")
+    return (out[:, 0], lse[:, 0]) if single else (out, lse)
+
+
+def merge_lse(outs, lses):
+    """Merge of P results over disjoint row sets: outs [P, ..., d], lses [P, ...] ->
+    (out [..., d], lse [...]) float64."""
+    outs = np.ascontiguousarray(outs, dtype=np.float64)
+    lses = np.ascontiguousarray(lses, dtype=np.float64)
+    P, d = outs.shape[0], outs.shape[-1]
+    rows_shape = outs.shape[1:-1]
+    assert lses.shape == (P, *rows_shape)
+    rows = int(np.prod(rows_shape)) if rows_shape else 1
+    out = np.zeros((*rows_shape, d), dtype=np.float64)
+    lse = np.zeros(rows_shape, dtype=np.float64)
+    _load().oracle_merge_lse_f64(P, rows, d, _ptr(outs), _ptr(lses), _ptr(out), _ptr(lse))
+    return out, lse
 
 
 def kv_append(k_cache, v_cache, lens, k_new, v_new):

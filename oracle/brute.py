@@ -75,3 +75,35 @@ def decode_multi(q, k_cache, v_cache, lens, scale):
                 per_t.append(rows)
             out.append(per_t)
     return out
+
+
+def decode_lse(q, k_cache, v_cache, lens, scale):
+    """Attention over one shard of the rows with each head's log-sum-exp ln sum_l exp(s[l]),
+    computed from the definition (the logarithm of the summed exponentials of the scores):
+    q [B][h_q][d_k], caches [B][h_kv][cap][d], lens [B] (0: no rows; out 0, lse -Infinity).
+    Returns (out [B][h_q][d_v], lse [B][h_q]) as Decimals."""
+    outs, lses = [], []
+    with localcontext() as ctx:
+        ctx.prec = 50
+        sc = Decimal(float(scale))
+        for b in range(len(q)):
+            h_q, h_kv = len(q[b]), len(k_cache[b])
+            g = h_q // h_kv
+            n = int(lens[b])
+            rows, ls = [], []
+            for h in range(h_q):
+                K, V = k_cache[b][h // g][:n], v_cache[b][h // g][:n]
+                d_v = len(v_cache[b][h // g][0])
+                if n == 0:
+                    rows.append([Decimal(0)] * d_v)
+                    ls.append(Decimal("-Infinity"))
+                    continue
+                qd = [Decimal(float(x)) for x in q[b][h]]
+                s = [sc * sum(qd[j] * Decimal(float(row[j])) for j in range(len(qd))) for row in K]
+                e = [x.exp() for x in s]
+                Z = sum(e)
+                rows.append([sum(e[l] / Z * Decimal(float(V[l][d])) for l in range(n)) for d in range(d_v)])
+                ls.append(Z.ln())
+            outs.append(rows)
+            lses.append(ls)
+    return outs, lses

@@ -283,6 +283,105 @@ int oracle_decode_multi_f64(int B, int T, int h_q, int h_kv, int d_k, int d_v, i
 }
 
 /*
+ * Decode attention over one shard of the rows, with each query row's log-sum-exp, for a
+ * context split over several devices: each holds a contiguous part of every sequence's rows as
+ * a cache of its own. Page "MoA-Structured Decode Attention", §2 eq. (2): Step II normalises by
+ * Z = sum_l exp(s[l] - m); over a union of disjoint row sets the normalisation is the
+ * log-sum-exp-weighted combination of the sets' own (oracle_merge_lse_f64), which needs each
+ * set's lse = ln sum_l exp(s[l]) = m + ln Z.
+ * Query t of sequence b attends over the first n = lens[b] - T + 1 + t rows of this cache
+ * (T = 1: all lens[b] rows), Steps I-III as oracle_head_f64; lse takes that head's m and Z.
+ * lens[b] = 0 (the shard holds no rows of sequence b): out 0 and lse -inf.
+ *   q [B, T, h_q, d_k]   out [B, T, h_q, d_v] double   lse [B, T, h_q] double
+ * Everything else as oracle_decode_multi_f64. Returns -3 if a lens[b] is in [1, T) or above cap.
+ */
+int oracle_decode_lse_f64(int B, int T, int h_q, int h_kv, int d_k, int d_v, int cap,
+                          int q_dtype, int kv_dtype, float scale, const void *q,
+                          const void *k_cache, const void *v_cache,
+                          const int32_t *lens, const float *kv_scales, double *out,
+                          double *lse, int nthreads) {
+    if (B < 0 || T < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv || d_k < 1 || d_v < 1 || cap < 1)
+        return -1;
+    if (!elem_bytes(q_dtype) || !elem_bytes(kv_dtype)) return -1;
+    if (scaled(kv_dtype) && !kv_scales) return -1;
+    for (int b = 0; b < B; ++b)
+        if (lens[b] < 0 || (lens[b] > 0 && lens[b] < T) || lens[b] > cap) return -3;
+    const int g = h_q / h_kv;
+    const int nthr = nthreads > 0 ? nthreads : omp_get_max_threads();
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthr) reduction(min : status)
+    for (long bth = 0; bth < (long)B * T * h_q; ++bth) {
+        const int b = (int)(bth / ((long)T * h_q));
+        const int t = (int)((bth / h_q) % T);
+        const int h = (int)(bth % h_q), kvh = h / g;
+        if (lens[b] == 0) { /* no rows of this sequence in the shard */
+            for (int d = 0; d < d_v; ++d) out[(size_t)bth * d_v + d] = 0.0;
+            lse[bth] = -INFINITY;
+            continue;
+        }
+        const int n = t + 1 + lens[b] - T; /* causal: its own row and every earlier one */
+        const size_t slot = (size_t)b * h_kv + kvh;
+        double ks = 1.0, vs = 1.0;
+        if (scaled(kv_dtype)) {
+            ks = (double)kv_scales[slot * 2 + 0];
+            vs = (double)kv_scales[slot * 2 + 1];
+        }
+        double *qd = (double *)malloc(sizeof(double) * (size_t)d_k);
+        double *Kd = (double *)malloc(sizeof(double) * (size_t)n * d_k);
+        double *Vd = (double *)malloc(sizeof(double) * (size_t)n * d_v);
+        if (!qd || !Kd || !Vd) {
+            free(qd); free(Kd); free(Vd);
+            status = -2;
+            continue;
+        }
+        for (int j = 0; j < d_k; ++j) qd[j] = load_elem(q, q_dtype, (size_t)bth * d_k + j);
+        for (int l = 0; l < n; ++l) {
+            for (int j = 0; j < d_k; ++j)
+                Kd[(size_t)l * d_k + j] = load_elem(k_cache, kv_dtype, (slot * cap + l) * d_k + j) * ks;
+            for (int d = 0; d < d_v; ++d)
+                Vd[(size_t)l * d_v + d] = load_elem(v_cache, kv_dtype, (slot * cap + l) * d_v + d) * vs;
+        }
+        double m = 0.0, Z = 0.0;
+        int rc = oracle_head_f64(n, d_k, d_v, (double)scale, qd, Kd, Vd, NULL, NULL, NULL, &m, &Z,
+                                 out + (size_t)bth * d_v);
+        lse[bth] = m + log(Z);
+        if (rc < status) status = rc;
+        free(qd); free(Kd); free(Vd);
+    }
+    return status;
+}
+
+/*
+ * Merge of P results over disjoint row sets (same passage): for every row r, with
+ * M = max_p lses[p][r] and w_p = exp(lses[p][r] - M),
+ *   out[r] = sum_p w_p * outs[p][r] / sum_p w_p,   lse_out[r] = M + ln sum_p w_p.
+ * A row that no part holds (every lse -inf) gets out 0 and lse -inf.
+ *   outs [P, rows, d], lses [P, rows]; out [rows, d], lse_out [rows]; all double.
+ */
+void oracle_merge_lse_f64(int P, long rows, int d, const double *outs, const double *lses,
+                          double *out, double *lse_out) {
+    for (long r = 0; r < rows; ++r) {
+        double M = -INFINITY;
+        for (int p = 0; p < P; ++p)
+            if (lses[(size_t)p * rows + r] > M) M = lses[(size_t)p * rows + r];
+        if (M == -INFINITY) {
+            for (int c = 0; c < d; ++c) out[(size_t)r * d + c] = 0.0;
+            lse_out[r] = -INFINITY;
+            continue;
+        }
+        double W = 0.0;
+        for (int p = 0; p < P; ++p) W += exp(lses[(size_t)p * rows + r] - M);
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int p = 0; p < P; ++p)
+                acc += exp(lses[(size_t)p * rows + r] - M) * outs[((size_t)p * rows + r) * d + c];
+            out[(size_t)r * d + c] = acc / W;
+        }
+        lse_out[r] = M + log(W);
+    }
+}
+
+/*
  * KV-cache accumulation: for every sequence b and KV head kvh, copy row
  * k_new[b][kvh] into k_cache at row lens[b] (and v_new into v_cache), then
  * lens[b] += 1. Byte copies; every other byte of the caches is unchanged.

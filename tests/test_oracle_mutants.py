@@ -4,7 +4,8 @@ Each case plants one mistake in a private copy of ``oracle/oracle.c`` (a
 dropped term, a wrong sign, index or group map, a transposed operand, a
 doubled scale, a wrong dequantisation scale, a decoder off by one, int8
 codes read as unsigned bytes, a causal bound off by one, query rows taken in
-the wrong order, a missing length update), builds it with gcc in a temporary directory, routes the
+the wrong order, a missing length update, a log-sum-exp without its maximum or in base 2, a
+merge without its normalisation or with flipped weights), builds it with gcc in a temporary directory, routes the
 oracle wrapper to it and runs the pin tests of ``test_oracle.py``. At least
 one pin must fail for every mutant; the unmutated copy must pass them all.
 Everything runs on the CPU.
@@ -16,6 +17,7 @@ import pytest
 
 import oracle
 from tests import test_oracle as pins
+from tests import test_oracle_lse as lse_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -36,6 +38,12 @@ MUTANTS = {
                             "const int t = (int)(bth % T), h = (int)(bth / T % h_q);"),
     "append_no_len_update": ("lens[b] += 1;", "lens[b] += 0;"),
     "append_wrong_row": ("(slot * cap + (size_t)lens[b]) * d_k * eb", "(slot * cap + (size_t)lens[b] / 2) * d_k * eb"),
+    "lse_without_max": ("lse[bth] = m + log(Z);", "lse[bth] = log(Z);"),
+    "lse_log2": ("lse[bth] = m + log(Z);", "lse[bth] = m + log2(Z);"),
+    "lse_causal_bound_off_by_one": ("const int n = t + 1 + lens[b] - T;", "const int n = t + lens[b] - T + (t > 0);"),
+    "merge_unnormalised": ("out[(size_t)r * d + c] = acc / W;", "out[(size_t)r * d + c] = acc;"),
+    "merge_lse_without_max": ("lse_out[r] = M + log(W);", "lse_out[r] = log(W);"),
+    "merge_weights_flipped": ("acc += exp(lses[(size_t)p * rows + r] - M) *", "acc += exp(M - lses[(size_t)p * rows + r]) *"),
     # a rewrite that changes nothing: the control that must pass every pin
     "control_noop": ("(slot * cap + (size_t)lens[b]) * d_k * eb", "(slot * cap + (size_t)lens[b] + 0) * d_k * eb"),
 }
@@ -54,6 +62,12 @@ PINS = [
     ("mq_sdpa", lambda gd: pins.test_multi_query_vs_torch_sdpa_with_causal_mask(4, 32, 8, 128, "bf16")),
     ("append_layout", lambda gd: pins.test_append_layout_gamma_offsets(gd)),
     ("append_bits", lambda gd: pins.test_append_is_bit_exact_and_touches_only_its_rows()),
+    ("lse_brute", lambda gd: [lse_pins.test_lse_vs_decimal_brute_force(s, kv) for s in range(2) for kv in ("f32", "fp8")]),
+    ("lse_scipy", lambda gd: lse_pins.test_lse_vs_scipy_logsumexp("bf16")),
+    ("lse_one_row", lambda gd: lse_pins.test_lse_single_row_is_its_score()),
+    ("lse_out", lambda gd: lse_pins.test_lse_outputs_equal_the_decode_functions()),
+    ("merge_parts", lambda gd: [lse_pins.test_merge_of_row_parts_equals_the_whole(s, "bf16") for s in range(2)]),
+    ("merge_closed", lambda gd: lse_pins.test_merge_closed_forms()),
 ]
 
 
