@@ -28,7 +28,7 @@ __all__ = [
     "Desc", "DecodeAttnError", "Workspace", "da_workspace_size", "da_plan", "da_workspace_init",
     "kv_append", "decode_attn_run", "decode_attn_partial", "decode_attn_combine",
     "decode_attn_append_run", "decode_attn_append_partial", "decode_attn_append_combine",
-    "decode_attn_run_static",
+    "decode_attn_run_static", "decode_attn_run_lse", "decode_attn_merge_lse",
     "da_read_device_error", "da_stream_read", "da_status_string", "da_last_error", "library_path",
     "DA_F32", "DA_BF16", "DA_FP8_E4M3FN", "DA_INT8", "DEV_ERR_APPEND_FULL", "DEV_ERR_LEN_RANGE",
     "FLAVOUR_AUTO", "FLAVOUR_VECTOR", "FLAVOUR_MATRIX", "PATH_AUTO", "PATH_SPLIT", "PATH_SINGLE",
@@ -271,6 +271,40 @@ def decode_attn_run_static(desc: Desc, q, k_cache, v_cache, lens, max_len: int, 
     cd = desc.c()
     _check(lib().decode_attn_run_static(ctypes.byref(cd), qp, kc, vc, ln, int(max_len), sc, op, ep, _stream(q)),
            "decode_attn_run_static")
+
+
+def decode_attn_run_lse(desc: Desc, q, k_cache, v_cache, lens, max_len: int, kv_scales, out, lse,
+                        workspace) -> None:
+    """decode_attn_run over one shard of the rows, also writing each query row's log-sum-exp
+    (natural log of the sum of exp(scale * q . K[l]) over its rows) into lse, shaped like out
+    without its last axis. lens[b] = 0: this shard holds no rows of sequence b (out 0,
+    lse -inf, no device error)."""
+    qp, kc, vc, ln, sc = _attn_args(desc, q, k_cache, v_cache, lens, kv_scales)
+    op = _dev(out, "out", desc.rows_shape(), torch.float32, q.device)
+    lp = _dev(lse, "lse", desc.rows_shape()[:-1], torch.float32, q.device)
+    wp, wn, _ = _ws(workspace)
+    cd = desc.c()
+    _check(lib().decode_attn_run_lse(ctypes.byref(cd), qp, kc, vc, ln, int(max_len), sc, op, lp, wp, wn,
+                                     _stream(q)), "decode_attn_run_lse")
+
+
+def decode_attn_merge_lse(outs, lses, out, lse=None) -> None:
+    """Merges P shard results over disjoint row sets: outs [P, *rows, d] and lses [P, *rows]
+    (fp32 GPU tensors) into out [*rows, d] and, when given, lse [*rows]."""
+    if not isinstance(outs, torch.Tensor) or outs.dim() < 2:
+        raise ValueError("outs must be a tensor [P, ..., d]")
+    P, d = outs.shape[0], outs.shape[-1]
+    rows_shape = tuple(outs.shape[1:-1])
+    dev = outs.device
+    op_in = _dev(outs, "outs", tuple(outs.shape), torch.float32, dev)
+    lp_in = _dev(lses, "lses", (P, *rows_shape), torch.float32, dev)
+    op = _dev(out, "out", (*rows_shape, d), torch.float32, dev)
+    lp = _dev(lse, "lse", rows_shape, torch.float32, dev) if lse is not None else ctypes.c_void_p(None)
+    rows = 1
+    for n in rows_shape:
+        rows *= n
+    _check(lib().decode_attn_merge_lse(ctypes.c_int64(rows), int(d), int(P), op_in, lp_in, op, lp, _stream(outs)),
+           "decode_attn_merge_lse")
 
 
 def da_stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:

@@ -30,6 +30,8 @@ SIGNATURES = {
     "decode_attn_append_partial": (ctypes.c_int, [P, P, P, P, P, P, P, I32, P, P, SZ, P]),
     "decode_attn_append_combine": (ctypes.c_int, [P, P, I32, P, P, SZ, P]),
     "decode_attn_run_static": (ctypes.c_int, [P, P, P, P, P, I32, P, P, P, P]),
+    "decode_attn_run_lse": (ctypes.c_int, [P, P, P, P, P, I32, P, P, P, P, SZ, P]),
+    "decode_attn_merge_lse": (ctypes.c_int, [ctypes.c_int64, I32, I32, P, P, P, P, P]),
     "da_stream_read": (ctypes.c_int, [P, SZ, P, P]),
     "da_read_device_error": (ctypes.c_int, [P, P, P]),
     "da_status_string": (ctypes.c_char_p, [ctypes.c_int]),

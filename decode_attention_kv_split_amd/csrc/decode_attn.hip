@@ -49,6 +49,7 @@ constexpr int kBlock = kWave * kWaves;
 constexpr int kUnroll = 4;  // row loads per lane per tile
 constexpr int kCombineBlock = 256;
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegBig = -3.0e38f;  // finite "minus infinity" for running maxima
 // Matrix-core segments rescale their running sums only when a tile's max exceeds the
 // exponent reference by this much (base 2), so the exponentials stay below 2^8 = 256.
@@ -1701,12 +1702,16 @@ __global__ __launch_bounds__(kBlock) void decode_step_single_kernel(const SplitA
 // one if its share holds no rows). The length and that entry are read together, then every
 // segment once: each segment group keeps a running maximum; the groups of a row merge by
 // shuffles within a wave, then the waves of a row through LDS.
+// lse_out (decode_attn_run_lse; NULL otherwise): each row's log-sum-exp of its scaled scores,
+// natural log, ln sum_l exp(s[l]) = ln 2 * (M + log2 l) for the merged base-2 maximum M and
+// sum l, so that results over disjoint row sets merge by decode_attn_merge_lse. In this mode a
+// sequence of length 0 holds no rows of this shard: output 0 and log-sum-exp -inf, no error.
 template <int D>
 __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     const int32_t *__restrict__ lens, int32_t *__restrict__ lens_upd, const int2 *__restrict__ unit_wg,
     const float *__restrict__ part_ml, const float *__restrict__ part_o,
     float *__restrict__ out, int32_t *__restrict__ err, int h_q, int gt, int grp_rows, int rw, int cs,
-    Partition pt, int skip_single) {
+    Partition pt, int skip_single, float *__restrict__ lse_out) {
     constexpr int UN = 8;          // segments a group loads before using them
     const int cw = D / 4 / cs;     // float4 columns of the slice
     const int tpr = kCombineBlock / rw, sgr = tpr / cw;  // threads and segment groups per row
@@ -1721,13 +1726,17 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
     // the row's query position and head: row hh of the tile is row fr of the group's g * nq
     const int fr = (ul % pt.tiles) * gt + hh, tq = fr / g, h = kvh * g + fr % g;
     const bool live = fr < grp_rows;  // a query row of the group, not past its last tile's rows
-    float *dst = out + ((size_t)(b * pt.nq + tq) * h_q + h) * D;
+    const size_t orow = (size_t)(b * pt.nq + tq) * h_q + h;
+    float *dst = out + orow * D;
     const int L = attended_len(lens[b], pt.append_cap);
     const int2 ww = unit_wg[u];
     if (lens_upd && ul == 0 && threadIdx.x == 0 && xs % per_unit == 0 && blockIdx.x % cs == 0) lens_upd[b] = L;
     if (unit_rows(L, pt.max_len, pt.nq) == 0) {
-        if (sg == 0 && live) reinterpret_cast<float4 *>(dst)[c4] = float4{0.f, 0.f, 0.f, 0.f};
-        if (threadIdx.x == 0) atomicOr(err, DA_DEV_ERR_LEN_RANGE);
+        if (sg == 0 && live) {
+            reinterpret_cast<float4 *>(dst)[c4] = float4{0.f, 0.f, 0.f, 0.f};
+            if (lse_out && c4 == 0) lse_out[orow] = -INFINITY;
+        }
+        if (threadIdx.x == 0 && !(lse_out && L == 0)) atomicOr(err, DA_DEV_ERR_LEN_RANGE);
         return;
     }
     const int wa = ww.x, wb = ww.y;
@@ -1810,10 +1819,47 @@ __global__ __launch_bounds__(kCombineBlock) void lse_combine_kernel(
         }
         acc = x;
         ls = z;
+        mrun = M;
     } else if (sg != 0) {
         return;
     }
-    if (live) reinterpret_cast<float4 *>(dst)[c4] = float4{acc.x / ls, acc.y / ls, acc.z / ls, acc.w / ls};
+    if (live) {
+        reinterpret_cast<float4 *>(dst)[c4] = float4{acc.x / ls, acc.y / ls, acc.z / ls, acc.w / ls};
+        if (lse_out && c4 == 0) lse_out[orow] = (mrun + __log2f(ls)) * kLn2;
+    }
+}
+
+// Log-sum-exp merge of `shards` results over disjoint row sets (decode_attn_merge_lse): thread
+// x takes float4 column x % (d / 4) of row x / (d / 4). With M = max_p lse_p and
+// w_p = exp(lse_p - M): out = sum_p w_p out_p / sum_p w_p and lse = M + ln sum_p w_p, Step II's
+// normalisation over the union of the shards' rows. A row that no shard holds (every lse_p
+// -inf) gets out 0 and lse -inf.
+__global__ __launch_bounds__(256) void merge_lse_kernel(int64_t rows, int d, int shards, const float *__restrict__ outs,
+                                                        const float *__restrict__ lses, float *__restrict__ out,
+                                                        float *__restrict__ lse_out) {
+    const int c4n = d / 4;
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= rows * c4n) return;
+    const int64_t r = x / c4n;
+    const int c4 = (int)(x % c4n);
+    float M = -INFINITY;
+    for (int p = 0; p < shards; ++p) M = fmaxf(M, lses[p * rows + r]);
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    float z = 0.f;
+    if (M != -INFINITY) {
+        for (int p = 0; p < shards; ++p) {
+            const float w = __builtin_amdgcn_exp2f((lses[p * rows + r] - M) * kLog2e);
+            const float4 o = reinterpret_cast<const float4 *>(outs + ((size_t)p * rows + r) * d)[c4];
+            z += w;
+            acc.x = fmaf(o.x, w, acc.x);
+            acc.y = fmaf(o.y, w, acc.y);
+            acc.z = fmaf(o.z, w, acc.z);
+            acc.w = fmaf(o.w, w, acc.w);
+        }
+        acc = float4{acc.x / z, acc.y / z, acc.z / z, acc.w / z};
+    }
+    reinterpret_cast<float4 *>(out + (size_t)r * d)[c4] = acc;
+    if (lse_out && c4 == 0) lse_out[r] = M == -INFINITY ? M : M + __logf(z);
 }
 
 // ------------------------------------------------------------------ host side
@@ -2247,7 +2293,7 @@ int run_split(const da_desc *desc, const void *q, const void *k_cache, const voi
 
 int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out, void *workspace,
                 size_t ws_bytes, void *stream, int skip_single, bool append, const char *who,
-                int32_t *err_word = nullptr) {
+                int32_t *err_word = nullptr, float *lse = nullptr) {
     Plan p;
     int rc = make_plan(desc, max_len, &p);
     if (rc) return rc;
@@ -2289,10 +2335,10 @@ int run_combine(const da_desc *desc, int32_t *lens, int32_t max_len, float *out,
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (desc->d_v == 64)
         hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, ml, po, out, err,
-                           desc->h_q, p.gt, group_rows(desc), rw, cs, pt, skip_single);
+                           desc->h_q, p.gt, group_rows(desc), rw, cs, pt, skip_single, lse);
     else
         hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineBlock), 0, st, lsrc, lupd, uw, ml, po, out, err,
-                           desc->h_q, p.gt, group_rows(desc), rw, cs, pt, skip_single);
+                           desc->h_q, p.gt, group_rows(desc), rw, cs, pt, skip_single, lse);
     return launch_status("lse_combine_kernel");
 }
 
@@ -2473,6 +2519,37 @@ int decode_attn_run_static(const da_desc *desc, const void *q, const void *k_cac
     if (rc || whole) return rc;
     return run_combine(desc, const_cast<int32_t *>(lens), max_len, out, ws, p.bytes, stream, 1, false,
                        "decode_attn_run_static", err);
+}
+
+int decode_attn_run_lse(const da_desc *desc, const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *lens, int32_t max_len, const float *kv_scales, float *out, float *lse,
+                        void *workspace, size_t ws_bytes, void *stream) {
+    if (!out || !lse) return fail(DA_ERR_INVALID_ARG, "decode_attn_run_lse: out and lse must not be NULL");
+    if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(DA_ERR_INVALID_ARG, "decode_attn_run_lse: lse is not 4-byte aligned");
+    // every unit leaves partials (no direct writes, no single pass): the combine writes out and lse
+    const int rc = run_split(desc, q, k_cache, v_cache, lens, nullptr, nullptr, max_len, kv_scales, nullptr,
+                             workspace, ws_bytes, stream, "decode_attn_run_lse");
+    if (rc) return rc;
+    return run_combine(desc, const_cast<int32_t *>(lens), max_len, out, workspace, ws_bytes, stream, 0, false,
+                       "decode_attn_run_lse", nullptr, lse);
+}
+
+int decode_attn_merge_lse(int64_t rows, int32_t d, int32_t shards, const float *outs, const float *lses, float *out,
+                          float *lse, void *stream) {
+    if (rows < 0 || d < 4 || d % 4 || d > 4096 || shards < 1 || shards > 4096)
+        return fail(DA_ERR_INVALID_ARG, "decode_attn_merge_lse: rows %lld, d %d (a positive multiple of 4, at most 4096), "
+                                        "shards %d (1..4096)", (long long)rows, d, shards);
+    if (rows == 0) return DA_OK;
+    if (!outs || !lses || !out) return fail(DA_ERR_INVALID_ARG, "decode_attn_merge_lse: a buffer pointer is NULL");
+    if (!aligned16(outs) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lses) & 3u) ||
+        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return fail(DA_ERR_INVALID_ARG, "decode_attn_merge_lse: outs and out must be 16-byte aligned, lses and lse 4-byte");
+    const int64_t threads = rows * (d / 4);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return fail(DA_ERR_INVALID_ARG, "decode_attn_merge_lse: too many rows");
+    hipLaunchKernelGGL(merge_lse_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream), rows, d,
+                       shards, outs, lses, out, lse);
+    return launch_status("merge_lse_kernel");
 }
 
 int da_stream_read(const void *buf, size_t bytes, float *sink, void *stream) {

@@ -261,6 +261,42 @@ int decode_attn_run_static(const da_desc *desc, const void *q, const void *k_cac
                            const float *kv_scales, float *out, int32_t *dev_err, void *stream);
 
 /*
+ * decode_attn_run over one shard of the rows, for a context split over several devices: each
+ * device holds a contiguous part of every sequence's rows as a cache of its own (lens[b] rows
+ * of it, 0 allowed) and emits, per query row, the attention over its part together with that
+ * part's log-sum-exp; decode_attn_merge_lse then merges the parts into attention over all the
+ * rows (page "MoA-Structured Decode Attention", §2 eq. (2): the softmax normalisation over a
+ * union of row sets is the log-sum-exp-weighted combination of the normalisations over each
+ * set). Arguments as decode_attn_run, plus
+ *   lse  [batch, h_q] fp32 ([batch, T, h_q] for T = n_queries > 1), 4-byte aligned:
+ *        ln sum_l exp(scale * q . K[l]) over the rows the query attends to (natural log).
+ * A sequence with lens[b] = 0 holds no rows of this shard: its out rows are 0 and its lse
+ * -inf, with no device error; other lengths outside [max(1, T), max_len] raise
+ * DA_DEV_ERR_LEN_RANGE as in decode_attn_run (out 0, lse -inf). Always two kernels (the split
+ * kernel with every segment's partial kept, then the combine, which writes out and lse); the
+ * workspace is decode_attn_run's (da_workspace_size). With T > 1 the causal bound of query t
+ * counts this shard's rows only (row lens[b] - T + t of this cache is the query's own).
+ */
+int decode_attn_run_lse(const da_desc *desc, const void *q, const void *k_cache,
+                        const void *v_cache, const int32_t *lens, int32_t max_len,
+                        const float *kv_scales, float *out, float *lse, void *workspace,
+                        size_t ws_bytes, void *stream);
+
+/*
+ * Log-sum-exp merge of `shards` results over disjoint row sets, e.g. the decode_attn_run_lse
+ * outputs of the devices that split a context, gathered on one device (same passage as
+ * decode_attn_run_lse): with M = max_p lses[p][r] and w_p = exp(lses[p][r] - M),
+ *   out[r] = sum_p w_p * outs[p][r] / sum_p w_p,   lse[r] = M + ln sum_p w_p.
+ *   outs [shards, rows, d] fp32 (16-byte aligned), lses [shards, rows] fp32,
+ *   out  [rows, d] fp32 (16-byte aligned), lse [rows] fp32 or NULL (not wanted).
+ * rows >= 0 (any number of query rows, e.g. batch * h_q), d a positive multiple of 4 up to
+ * 4096, 1 <= shards <= 4096. A row that no shard holds (every lse -inf) gets out 0 and
+ * lse -inf. One kernel on the stream; out and lse must not overlap the inputs.
+ */
+int decode_attn_merge_lse(int64_t rows, int32_t d, int32_t shards, const float *outs,
+                          const float *lses, float *out, float *lse, void *stream);
+
+/*
  * Measurement helper, not part of the attention path: a plain streaming read of `bytes` bytes
  * at buf (16-byte aligned, bytes a positive multiple of 16) by 512 workgroups, each reading a
  * contiguous chunk with 16-byte non-temporal loads. sink is a device buffer of at least 512

@@ -295,3 +295,25 @@ def test_single_pass_choice(lib):
     assert lib.da_plan(ctypes.byref(gqa), 4096, None, None, None, ctypes.byref(pa)) == 0 and pa.value == 1
     # the workspace does not depend on the path
     assert _ws_size(lib, _desc(path=0), 100) == _ws_size(lib, _desc(path=1), 100)
+
+
+def test_shard_entry_points_validate_on_the_host(lib):
+    """decode_attn_run_lse needs out and a 4-byte aligned lse and takes decode_attn_run's
+    workspace; decode_attn_merge_lse checks its sizes and pointers before launching, and
+    merges zero rows without launching anything."""
+    d = _desc()
+    rc, n = _ws_size(lib, d, 1000)
+    assert rc == 0
+    args = (ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1000, None)
+    assert lib.decode_attn_run_lse(*args, None, FAKE, FAKE, n, None) == -1
+    assert lib.decode_attn_run_lse(*args, FAKE, None, FAKE, n, None) == -1
+    assert lib.decode_attn_run_lse(*args, FAKE, ctypes.c_void_p(0x10002), FAKE, n, None) == -1
+    assert lib.decode_attn_run_lse(*args, FAKE, FAKE, FAKE, n - 1, None) == -3
+    merge = lib.decode_attn_merge_lse
+    assert merge(0, 128, 4, None, None, None, None, None) == 0  # nothing to merge
+    for rows, dd, shards in [(-1, 128, 2), (10, 6, 2), (10, 0, 2), (10, 8192, 2), (10, 128, 0), (10, 128, 5000)]:
+        assert merge(rows, dd, shards, FAKE, FAKE, FAKE, None, None) == -1, (rows, dd, shards)
+    assert merge(10, 128, 2, None, FAKE, FAKE, None, None) == -1
+    assert merge(10, 128, 2, ctypes.c_void_p(0x10004), FAKE, FAKE, None, None) == -1  # outs misaligned
+    assert merge(10, 128, 2, FAKE, ctypes.c_void_p(0x10002), FAKE, None, None) == -1  # lses misaligned
+    assert merge(10, 128, 2, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10001), None) == -1  # lse misaligned
