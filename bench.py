@@ -34,6 +34,10 @@ Prints ONE JSON line:
   cpu_baseline= the fp64 CPU oracle on the same inputs, full step, host cores
   one_call_form = split path only: the same number of steps again, every one in the one-call
                 form (no events inside a step), bracketed by two events
+  --lse-parts P = one device's share of a context split P ways (workloads without an append):
+                the one-call step is decode_attn_run_lse over this workload's rows (the share,
+                e.g. --workload mqa_bf16 --const-len 16384 for 8 parts of 131072 rows), then the
+                decode_attn_merge_lse of P part results that follows the all-gather
   stream_ceiling = the read rate of a plain streaming read (da_stream_read over 2 GiB), and
                 value and roofline.achieved as percentages of it; measured before the warm-up
                 steps, after some 60 ms of untimed streaming that brings the part to steady
@@ -80,6 +84,10 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ceiling", action="store_true", help="skip the measured streaming-read ceiling")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle timing budget")
+    p.add_argument("--lse-parts", type=int, default=0,
+                   help="one device's share of a context split P ways: the one-call step is "
+                        "decode_attn_run_lse on this workload (one part's rows, e.g. --const-len L / P), "
+                        "then decode_attn_merge_lse of P part results (workloads without an append)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device copy (FETCH_SIZE / WRITE_SIZE scale factor)")
     return p.parse_args()
@@ -202,6 +210,9 @@ def main() -> int:
         if w.h_q % w.h_kv:
             print(f"bench.py: h_q {w.h_q} is not a multiple of h_kv {w.h_kv}", file=sys.stderr)
             return 2
+    if args.lse_parts and w.steps:
+        print("bench.py: --lse-parts takes a workload without an append", file=sys.stderr)
+        return 2
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     c = workloads.generate(w, poison=False)
@@ -233,7 +244,7 @@ def main() -> int:
                    workloads.TORCH_DTYPE[w.kv_dtype], w.scale, args.block_rows, w.nq, flavour, path)
     plan = da.da_plan(desc, max_len)
     # the single pass is one kernel per step; the split path two (split kernel, combine kernel)
-    one_kernel = plan["path"] == da.PATH_SINGLE
+    one_kernel = plan["path"] == da.PATH_SINGLE and not args.lse_parts  # the lse form: the split path
     step_kernel = "decode_step_single_kernel" if one_kernel else split_kernel_name(w, args.flavour)
     q = c["q"].to(dev)
     scales = c["kv_scales"].to(dev) if c["kv_scales"] is not None else None
@@ -250,6 +261,14 @@ def main() -> int:
     ws = da.Workspace(desc, max_len, device=dev)
     out = torch.empty(desc.rows_shape(), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if args.lse_parts:
+        # the share's result with its log-sum-exp, and the P part results the merge takes after an
+        # all-gather (here P copies of the share's own, which the merge reads like any others)
+        lse = torch.empty(desc.rows_shape()[:-1], dtype=torch.float32, device=dev)
+        parts_out = torch.zeros((args.lse_parts, *desc.rows_shape()), dtype=torch.float32, device=dev)
+        parts_lse = torch.zeros((args.lse_parts, *desc.rows_shape()[:-1]), dtype=torch.float32, device=dev)
+        merged = torch.empty_like(out)
+        merged_lse = torch.empty_like(lse)
 
     def step(i, ev=None):
         """One step, as the product calls it (one call). With events ev = (a, b) they bracket the
@@ -257,6 +276,10 @@ def main() -> int:
         path the step runs in its two-stage form, the split kernel between a and b, then the
         combine."""
         kc, vc, lens = slots[i % R]
+        if args.lse_parts and ev is None:
+            da.decode_attn_run_lse(desc, q, kc, vc, lens, max_len, scales, out, lse, ws)
+            da.decode_attn_merge_lse(parts_out, parts_lse, merged, merged_lse)
+            return
         if ev is None or one_kernel:
             if ev is not None:
                 ev[0].record(stream)
@@ -277,6 +300,8 @@ def main() -> int:
             da.decode_attn_append_combine(desc, lens, max_len, out, ws)
         else:
             da.decode_attn_combine(desc, lens, max_len, out, ws)
+        if args.lse_parts:
+            da.decode_attn_merge_lse(parts_out, parts_lse, merged, merged_lse)
 
     # the streaming-read ceiling is measured first: its untimed reads also bring the part to
     # steady clocks before the warm-up steps
@@ -395,6 +420,9 @@ def main() -> int:
             "rotations": R, "cache_bytes_per_copy": cache_bytes, "flavour": args.flavour,
             **{k: v for k, v in plan.items() if k != "path"},
             "path": "single" if one_kernel else "split",
+            **({"lse_parts": args.lse_parts,
+                "step": "decode_attn_run_lse on this share, then decode_attn_merge_lse of the parts"}
+               if args.lse_parts else {}),
         },
         "roofline": {
             "kernel": step_kernel,

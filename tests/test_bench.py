@@ -88,3 +88,11 @@ def test_cpu_baseline_fills_its_budget_with_whole_passes():
     assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
     assert r["passes"] > 1 and f"{r['passes']} passes" in r["sample"]
     assert float(r["sample"].rsplit(", ", 1)[1].rstrip(" s")) >= 0.15
+
+
+def test_lse_parts_take_a_workload_without_an_append():
+    # the shard form (decode_attn_run_lse + the merge) has no fused append: refused before any device is touched
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--lse-parts", "8"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "without an append" in r.stderr
