@@ -10,7 +10,8 @@ synchronisation sit between the replays, as in a real loop. No call of the libra
 memset: the workspace is cleared by its own kernels.
 
 The second test replays a captured multi-query attend (no append) with new queries written
-between the replays.
+between the replays. The third replays one device's shares of a context split in two
+(decode_attn_run_lse on each) and their merge.
 """
 import numpy as np
 import pytest
@@ -157,3 +158,66 @@ def test_graph_replayed_multi_query_attend(kv, d, h_q, h_kv, T, lens, cap):
         ref = oracle.decode_multi_f64(q, oracle._np(kc), oracle._np(vc), lens_t, scale, kv_scales=scales)
         check_close(got, ref, kv, f"replay {i}")
     assert da.da_read_device_error(ws_g) == 0 and da.da_read_device_error(ws_e) == 0
+
+
+def test_graph_replayed_context_parts_and_merge():
+    """One device's shares of a context split in two, then the merge, captured once and replayed
+    with new queries: every replay equals the eager calls bit for bit, and out and lse equal the
+    oracle's attention over all the rows."""
+    from tests.test_gpu_shard import check_lse
+    log("case graph context parts + merge")
+    B, h_q, h_kv, d, cap = 3, 32, 1, 128, 900
+    gen = torch.Generator().manual_seed(700)
+    qs = [torch.randn(B, h_q, d, generator=gen).to(torch.bfloat16) for _ in range(3)]
+    kc, vc = draw("bf16", (B, h_kv, 2 * cap, d), gen), draw("bf16", (B, h_kv, 2 * cap, d), gen)
+    lens_all = torch.tensor([1700, 901, 40], dtype=torch.int32)
+    cut = torch.tensor([900, 450, 0], dtype=torch.int32)  # part 0: rows [0, cut), part 1: the rest
+    scale = workloads._inv_sqrt(d)
+    desc = da.Desc(B, h_q, h_kv, d, cap, torch.bfloat16, torch.bfloat16, scale)
+    dev = torch.device("cuda")
+    parts = []
+    for p in range(2):
+        kp = torch.zeros(B, h_kv, cap, d, dtype=torch.bfloat16)
+        vp = torch.zeros_like(kp)
+        lp = torch.zeros(B, dtype=torch.int32)
+        for b in range(B):
+            r0 = 0 if p == 0 else int(cut[b])
+            r1 = int(cut[b]) if p == 0 else int(lens_all[b])
+            kp[b, :, :r1 - r0] = kc[b, :, r0:r1]
+            vp[b, :, :r1 - r0] = vc[b, :, r0:r1]
+            lp[b] = r1 - r0
+        parts.append((kp.to(dev), vp.to(dev), lp.to(dev)))
+    qin = torch.empty(B, h_q, d, dtype=torch.bfloat16, device=dev)
+    pouts = torch.empty(2, B, h_q, d, device=dev)
+    plses = torch.empty(2, B, h_q, device=dev)
+    out_g, lse_g = torch.empty(B, h_q, d, device=dev), torch.empty(B, h_q, device=dev)
+    ws = [da.Workspace(desc, cap) for _ in range(2)]
+    ws_e = [da.Workspace(desc, cap) for _ in range(2)]
+
+    def step(q, po, pl, out, lse, wss):
+        for p, (kp, vp, lp) in enumerate(parts):
+            da.decode_attn_run_lse(desc, q, kp, vp, lp, cap, None, po[p], pl[p], wss[p])
+        da.decode_attn_merge_lse(po, pl, out, lse)
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(qin, pouts, plses, out_g, lse_g, ws)
+    torch.cuda.synchronize()
+    po_e, pl_e = torch.empty_like(pouts), torch.empty_like(plses)
+    out_e, lse_e = torch.empty_like(out_g), torch.empty_like(lse_g)
+    for i, q in enumerate(qs):
+        qin.copy_(q.to(dev))
+        graph.replay()
+        got, got_l = out_g.clone(), lse_g.clone()
+        step(q.to(dev), po_e, pl_e, out_e, lse_e, ws_e)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(got), bits(out_e)) and np.array_equal(bits(got_l), bits(lse_e)), f"replay {i}"
+        ref_o, ref_l = oracle.decode_lse_f64(q, kc, vc, lens_all, scale)
+        check_close(got, ref_o, "bf16", f"replay {i}")
+        check_lse(got_l, ref_l, f"replay {i} lse")
+    for w_ in ws + ws_e:
+        assert da.da_read_device_error(w_) == 0
