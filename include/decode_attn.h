@@ -275,7 +275,9 @@ int decode_attn_run_static(const da_desc *desc, const void *q, const void *k_cac
  * DA_DEV_ERR_LEN_RANGE as in decode_attn_run (out 0, lse -inf). Always two kernels (the split
  * kernel with every segment's partial kept, then the combine, which writes out and lse); the
  * workspace is decode_attn_run's (da_workspace_size). With T > 1 the causal bound of query t
- * counts this shard's rows only (row lens[b] - T + t of this cache is the query's own).
+ * counts this shard's rows only (row lens[b] - T + t of this cache is the query's own), which
+ * is right for the shard holding the sequence's last rows; the earlier shards of a multi-query
+ * step would need no mask, which this entry point does not provide.
  */
 int decode_attn_run_lse(const da_desc *desc, const void *q, const void *k_cache,
                         const void *v_cache, const int32_t *lens, int32_t max_len,
