@@ -4,7 +4,9 @@ log-sum-exp) and decode_attn_merge_lse (the log-sum-exp merge of parts), which t
 what one device runs when a context is split over several (each holds a contiguous part of
 every sequence's rows and, after an all-gather of the parts' results, merges them). Head
 sharding needs no new entry point: every device runs decode_attn_run on its KV heads, and the
-outputs concatenate on the head axis (checked here too).
+outputs concatenate on the head axis (checked here too). Twenty-four seeded random splits
+(cache type, head size, group, batch, lengths, parts and cut points, partition) close the
+file.
 
 Tolerances: out as the other parity tests (tests/gpu_case.py: the cache type's contract and
 the regression bound); lse (natural log, magnitude ln n + the largest score, at most about 20
@@ -275,3 +277,54 @@ def test_head_split_concat_equals_whole():
     ws = da.Workspace(dw, ml)
     da.decode_attn_run(dw, g["q"], g["k_cache"], g["v_cache"], g["lens_final"], ml, None, whole, ws)
     check_close(whole, ref, "bf16", "all heads")
+
+
+def draw_split_cases(n=24, seed=4242):
+    """Random context splits: cache type, head size, group, batch, lengths, the number of parts
+    and where each sequence is cut (empty parts included), and the partition (the library's
+    own or small shares)."""
+    import random
+    rng = random.Random(seed)
+    groups = [(1, 1), (4, 1), (8, 2), (32, 8), (32, 1), (6, 3), (12, 4), (64, 8)]
+    cases = []
+    for i in range(n):
+        kv = rng.choice(["f32", "bf16", "bf16", "fp8", "int8"])
+        d = rng.choice([64, 128])
+        h_q, h_kv = rng.choice(groups)
+        B = rng.randint(1, 5)
+        cap = rng.choice([64, 500, 3000])
+        P = rng.randint(2, 6)
+        block_rows = rng.choice([0, 0, 16, 200])
+        cases.append((i, kv, d, h_q, h_kv, B, cap, P, block_rows, rng.randint(0, 1 << 30)))
+    return cases
+
+
+SPLIT_CASES = draw_split_cases()
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"s{c[0]}" for c in SPLIT_CASES])
+def test_random_context_split(case):
+    i, kv, d, h_q, h_kv, B, cap, P, block_rows, cut_seed = case
+    w = workloads.Workload("split", B, h_q, h_kv, d, cap, "f32" if kv == "f32" else "bf16", kv,
+                           ("uniform", 1, cap), 0, 9000 + i, workloads._inv_sqrt(d))
+    c = workloads.generate(w)
+    rng = np.random.default_rng(cut_seed)
+    cuts = [[0] + sorted(int(x) for x in rng.integers(0, n + 1, P - 1)) + [n] for n in c["lens_final"].tolist()]
+    log(f"case random split s{i}: {kv} d={d} h_q={h_q} h_kv={h_kv} B={B} cap={cap} P={P} block_rows={block_rows} "
+        f"lens={c['lens_final'].tolist()}")
+    q = c["q"].to("cuda")
+    sc = None if c["kv_scales"] is None else c["kv_scales"].to("cuda")
+    outs, lses = [], []
+    for kp, vp, lp in split_rows(c, cuts, kv):
+        ml = max(1, int(lp.max()))
+        desc = dataclasses.replace(desc_of(w), cap=kp.shape[2], block_rows=block_rows)
+        o, l = run_lse(w, desc, q, kp.to("cuda"), vp.to("cuda"), lp.to("cuda"), ml, sc)
+        outs.append(o)
+        lses.append(l)
+    out = torch.empty(w.B, w.h_q, w.d, device="cuda")
+    lse = torch.empty(w.B, w.h_q, device="cuda")
+    da.decode_attn_merge_lse(torch.stack(outs), torch.stack(lses), out, lse)
+    ref_o, ref_l = oracle.decode_lse_f64(c["q"], c["k_cache"], c["v_cache"], c["lens_final"], w.scale,
+                                         kv_scales=c["kv_scales"])
+    check_close(out, ref_o, kv, f"s{i} merged out")
+    check_lse(lse, ref_l, f"s{i} merged lse")
