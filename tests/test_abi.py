@@ -317,3 +317,48 @@ def test_shard_entry_points_validate_on_the_host(lib):
     assert merge(10, 128, 2, ctypes.c_void_p(0x10004), FAKE, FAKE, None, None) == -1  # outs misaligned
     assert merge(10, 128, 2, FAKE, ctypes.c_void_p(0x10002), FAKE, None, None) == -1  # lses misaligned
     assert merge(10, 128, 2, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10001), None) == -1  # lse misaligned
+
+
+C_PROGRAM = r"""
+#include "decode_attn.h"
+#include <stdio.h>
+#include <string.h>
+
+int main(void) {
+    /* the grouped-query workload's descriptor, built from C */
+    da_desc d;
+    memset(&d, 0, sizeof d);
+    d.batch = 16; d.h_q = 32; d.h_kv = 8; d.d_k = 128; d.d_v = 128; d.cap = 32768;
+    d.q_dtype = DA_BF16; d.kv_dtype = DA_BF16; d.scale = 0.08838834764f; d.path = DA_PATH_SPLIT;
+    size_t bytes = 0;
+    int rc = da_workspace_size(&d, 32768, &bytes);
+    int32_t rows = 0, blocks = 0, heads = 0, path = 0;
+    int rc2 = da_plan(&d, 32768, &rows, &blocks, &heads, &path);
+    /* host-side refusals, nothing launched */
+    int rc3 = decode_attn_run(&d, NULL, NULL, NULL, NULL, 100, NULL, NULL, NULL, 0, NULL);
+    int rc4 = decode_attn_merge_lse(0, 128, 2, NULL, NULL, NULL, NULL, NULL);
+    printf("%d %zu %d %d %d %d %d %s\n", rc, bytes, rc2, heads, path, rc3, rc4, da_status_string(rc3));
+    return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(tmp_path, lib):
+    """include/decode_attn.h compiles as C99 and a C program links against the library and
+    calls its host-side entry points (plan, workspace size, argument refusal) with no GPU."""
+    import shutil
+    import subprocess
+    if not shutil.which("gcc"):
+        pytest.skip("gcc is not available")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(_lib.library_path())
+    inc = os.path.dirname(HEADER)
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", f"-I{inc}", str(src), "-o", str(exe),
+                           f"-L{libdir}", "-ldecode_attn", f"-Wl,-rpath,{libdir}"])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    rc, nbytes, rc2, heads, path, rc3, rc4, status = out.stdout.split(maxsplit=7)
+    assert (int(rc), int(rc2), int(heads), int(path), int(rc3), int(rc4)) == (0, 0, 4, 1, -1, 0)
+    assert int(nbytes) > 0 and status.strip() == "invalid argument"
