@@ -490,11 +490,10 @@ def cpu_baseline(w, budget_s: float, kv_bytes_full: int) -> dict:
         k += 1
     elapsed = run(order[:k])
     passes = 1
-    if k == w.B:  # the whole batch is under the budget: the same step again, up to about the budget
-        more = max(0, int(budget_s / max(elapsed, 1e-3)) - 1)
-        for _ in range(more):
+    if k == w.B:  # the whole batch is under the budget: the same step again, until it is reached
+        while elapsed < budget_s and passes < 10000:
             elapsed += run(order[:k])
-        passes += more
+            passes += 1
     rows = int(lens[:k].sum())
     sample_bytes = rows * w.h_kv * 2 * w.d * esz * passes
     gbs = sample_bytes / elapsed / 1e9

@@ -87,7 +87,8 @@ def test_cpu_baseline_fills_its_budget_with_whole_passes():
     r = bench.cpu_baseline(w, 0.3, kv_bytes)
     assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
     assert r["passes"] > 1 and f"{r['passes']} passes" in r["sample"]
-    assert float(r["sample"].rsplit(", ", 1)[1].rstrip(" s")) >= 0.15
+    # whole passes until the budget is reached (the last pass may run past it)
+    assert float(r["sample"].rsplit(", ", 1)[1].rstrip(" s")) >= 0.3 * 0.9
 
 
 def test_lse_parts_take_a_workload_without_an_append():
