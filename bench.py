@@ -263,7 +263,8 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     if args.lse_parts:
         # the share's result with its log-sum-exp, and the P part results the merge takes after an
-        # all-gather (here P copies of the share's own, which the merge reads like any others)
+        # all-gather (zero-filled here: the merge reads and weighs them all the same, whatever the
+        # values)
         lse = torch.empty(desc.rows_shape()[:-1], dtype=torch.float32, device=dev)
         parts_out = torch.zeros((args.lse_parts, *desc.rows_shape()), dtype=torch.float32, device=dev)
         parts_lse = torch.zeros((args.lse_parts, *desc.rows_shape()[:-1]), dtype=torch.float32, device=dev)
