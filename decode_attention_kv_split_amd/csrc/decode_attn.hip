@@ -25,6 +25,8 @@
 //     scale, v_exp_f32 for 2^x); the waves of a workgroup merge through LDS at a segment's end.
 //   * For latency-bound problems a single-pass kernel does it in one launch: the splits of a
 //     unit count their arrivals and the last one merges them.
+//   * For a context split over devices, the combine also writes each query row's log-sum-exp
+//     (decode_attn_run_lse), and a small kernel merges the parts' results (decode_attn_merge_lse).
 //   * No atomics touch the outputs, so results are deterministic run to run.
 #include <hip/hip_runtime.h>
 
